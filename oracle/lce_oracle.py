@@ -1,0 +1,215 @@
+"""fp64 CPU oracle for fused linear + cross-entropy with ignored tokens.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg use it.  It shares no code with the HIP
+path.
+
+What it computes is the plain definition of the result.  The pages describe
+the method as reaching exactly this result with no approximation: the
+projection and the loss are chunked into streaming steps that skip padding
+tokens ("OjasX 0.6.1", section 核心技术 / "Core Technology": zero-byte
+vocabulary logits table), the streaming max / normaliser recurrence gives
+the same result as a full softmax (same page, paragraph on Online Softmax),
+and the backward pass recomputes the logits chunk by chunk instead of saving
+them ("6GB显卡预训练11亿参数模型", sections 内存实际花在哪里 and 关键参数说明,
+--chunked-loss 512).  None of the pages writes the loss formula; the oracle
+takes the textbook softmax cross-entropy that those passages name:
+
+    z[n, v]   = sum_k H[n, k] * W[v, k]                 (output projection)
+    lse[n]    = log sum_v exp(z[n, v])
+    loss[n]   = lse[n] - z[n, y[n]]       for valid n, 0 for ignored n
+    mean      = sum_n loss[n] / N_valid
+
+and its exact gradient
+
+    G[n, v]   = (exp(z[n, v] - lse[n]) - [v == y[n]]) * w,
+                w = grad / N_valid ("mean") or grad ("sum"), 0 for ignored n
+    dH        = G @ W,    dW = G^T @ H.
+
+A row is valid when its label differs from ignore_index (the pages' "skip
+padding tokens"; the valid-mask of the MaximusLLM page, section 2.3).  A
+valid label outside [0, V) is an error (the out-of-range index failure in
+"6GB显卡预训练11亿参数模型", section 可证伪测试抓到的8个静默bug, #155).
+
+Everything is computed in float64 from the given (already rounded) inputs.
+numpy's matrix product serves as the plain matrix product.  Each row block
+materialises its full [rows, V] logits: that is the point of an oracle.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+DEFAULT_ROW_BLOCK = 256
+
+
+# --------------------------------------------------------------------------
+# named steps (kept small so that each can be checked and mutated alone)
+# --------------------------------------------------------------------------
+
+def valid_mask(labels: np.ndarray, ignore_index: int) -> np.ndarray:
+    """Rows that take part in the loss: label != ignore_index."""
+    return np.asarray(labels) != ignore_index
+
+
+def logits(Hb: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """z = Hb W^T in float64 (the output projection)."""
+    return np.asarray(Hb, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+def logsumexp_rows(Z: np.ndarray) -> np.ndarray:
+    """log sum_v exp(Z[:, v]), shifted by the row max for range safety."""
+    m = Z.max(axis=1)
+    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+
+
+def target_logits(Z: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """z[n, y[n]] for each row of the block."""
+    return Z[np.arange(Z.shape[0]), y]
+
+
+def dlogits(Z: np.ndarray, lse: np.ndarray, y: np.ndarray, w: float) -> np.ndarray:
+    """G = (softmax(Z) - onehot(y)) * w for a block of valid rows."""
+    P = np.exp(Z - lse[:, None])
+    P[np.arange(Z.shape[0]), y] -= 1.0
+    return P * w
+
+
+# --------------------------------------------------------------------------
+# compaction
+# --------------------------------------------------------------------------
+
+def compact_valid(labels: np.ndarray, ignore_index: int, V: int):
+    """Ascending index of valid rows.
+
+    Returns (valid_idx int32[N_valid], N_valid, bad_rows).  ``bad_rows`` lists
+    rows whose label is neither ignore_index nor inside [0, V); they are not
+    in valid_idx.
+    """
+    labels = np.asarray(labels, dtype=np.int64)
+    keep = valid_mask(labels, ignore_index)
+    in_range = (labels >= 0) & (labels < V)
+    bad = np.flatnonzero(keep & ~in_range)
+    idx = np.flatnonzero(keep & in_range).astype(np.int32)
+    return idx, int(idx.size), bad
+
+
+def _checked_index(labels, ignore_index, V, bad_labels):
+    idx, n_valid, bad = compact_valid(labels, ignore_index, V)
+    if bad.size and bad_labels == "raise":
+        raise ValueError(
+            f"{bad.size} label(s) outside [0, {V}) that are not ignore_index "
+            f"(first at row {int(bad[0])}: {int(np.asarray(labels)[bad[0]])})")
+    return idx, n_valid
+
+
+def _scale(reduction: str, grad: float, n_valid: int) -> float:
+    if reduction == "mean":
+        return grad / n_valid if n_valid else 0.0
+    if reduction == "sum":
+        return grad
+    raise ValueError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
+
+
+# --------------------------------------------------------------------------
+# forward / backward
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class ForwardResult:
+    loss: np.ndarray       # float64 [N], 0 on ignored rows
+    lse: np.ndarray        # float64 [N], 0 on ignored rows
+    valid_idx: np.ndarray  # int32 [N_valid], ascending
+    valid_count: int
+    loss_sum: float
+    loss_mean: float       # NaN when no row is valid (PyTorch's convention)
+
+
+def forward(H, W, labels, ignore_index: int = -100, *, bad_labels: str = "raise",
+            row_block: int = DEFAULT_ROW_BLOCK) -> ForwardResult:
+    H = np.asarray(H)
+    W = np.asarray(W)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, V = H.shape[0], W.shape[0]
+    idx, n_valid = _checked_index(labels, ignore_index, V, bad_labels)
+    loss = np.zeros(N, dtype=np.float64)
+    lse = np.zeros(N, dtype=np.float64)
+    W64 = np.asarray(W, dtype=np.float64)
+    for s in range(0, n_valid, row_block):
+        rows = idx[s:s + row_block]
+        Z = logits(H[rows], W64)
+        l = logsumexp_rows(Z)
+        lse[rows] = l
+        loss[rows] = l - target_logits(Z, labels[rows])
+    loss_sum = float(loss[idx].sum()) if n_valid else 0.0
+    mean = loss_sum / n_valid if n_valid else float("nan")
+    return ForwardResult(loss, lse, idx, n_valid, loss_sum, mean)
+
+
+def backward(H, W, labels, ignore_index: int = -100, *, grad: float = 1.0,
+             reduction: str = "mean", bad_labels: str = "raise",
+             row_block: int = DEFAULT_ROW_BLOCK):
+    """(dH float64 [N, d], dW float64 [V, d]) of the reduced loss."""
+    H = np.asarray(H)
+    W = np.asarray(W)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, d = H.shape
+    V = W.shape[0]
+    idx, n_valid = _checked_index(labels, ignore_index, V, bad_labels)
+    w = _scale(reduction, grad, n_valid)
+    W64 = np.asarray(W, dtype=np.float64)
+    dH = np.zeros((N, d), dtype=np.float64)
+    dW = np.zeros((V, d), dtype=np.float64)
+    for s in range(0, n_valid, row_block):
+        rows = idx[s:s + row_block]
+        Hb = np.asarray(H[rows], dtype=np.float64)
+        Z = logits(Hb, W64)
+        G = dlogits(Z, logsumexp_rows(Z), labels[rows], w)
+        dH[rows] = G @ W64
+        dW += G.T @ Hb
+    return dH, dW
+
+
+# --------------------------------------------------------------------------
+# per-row evaluation (for sampled checks at full size)
+# --------------------------------------------------------------------------
+
+def rows_forward(H, W, labels, rows):
+    """(lse, loss, z_target) float64 for the given rows, assumed valid."""
+    rows = np.asarray(rows)
+    labels = np.asarray(labels, dtype=np.int64)
+    Z = logits(np.asarray(H)[rows], W)
+    l = logsumexp_rows(Z)
+    zt = target_logits(Z, labels[rows])
+    return l, l - zt, zt
+
+
+def rows_dH(H, W, labels, rows, w: float):
+    """dH rows for valid ``rows`` given the per-row scale w."""
+    rows = np.asarray(rows)
+    labels = np.asarray(labels, dtype=np.int64)
+    W64 = np.asarray(W, dtype=np.float64)
+    Z = logits(np.asarray(H)[rows], W64)
+    G = dlogits(Z, logsumexp_rows(Z), labels[rows], w)
+    return G @ W64
+
+
+def rows_dW(H, W, labels, valid_idx, lse_valid, vocab_rows, w: float,
+            row_block: int = 4096):
+    """dW[vocab_rows] given lse of every valid row (ordered as valid_idx)."""
+    vocab_rows = np.asarray(vocab_rows)
+    labels = np.asarray(labels, dtype=np.int64)
+    Wv = np.asarray(W, dtype=np.float64)[vocab_rows]
+    out = np.zeros((vocab_rows.size, np.asarray(H).shape[1]), dtype=np.float64)
+    for s in range(0, len(valid_idx), row_block):
+        rows = valid_idx[s:s + row_block]
+        Hb = np.asarray(np.asarray(H)[rows], dtype=np.float64)
+        Z = Hb @ Wv.T                        # [rows, |vocab_rows|]
+        P = np.exp(Z - np.asarray(lse_valid[s:s + row_block])[:, None])
+        onehot = labels[rows][:, None] == vocab_rows[None, :]
+        G = (P - onehot) * w
+        out += G.T @ Hb
+    return out

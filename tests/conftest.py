@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line(
+        "markers", "slow: full-size cases that take tens of seconds")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The loaded C-ABI library; fails loudly when it is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU")
+    from vocab_cross_entropy_valid_amd import _lib
+    return _lib.load()

@@ -1,0 +1,321 @@
+"""Pins that tie the fp64 oracle to facts outside itself.
+
+Each pin checks the oracle against something the mathematics fixes: closed
+forms (W = 0, H = 0, V = 1, V = 2), invariants (rows of softmax - onehot sum
+to zero, shift invariance, permutation equivariance, independence from
+ignored rows), central finite differences of the loss, a 50-digit evaluation
+of -log softmax from the exact rational logits, and PyTorch's CPU float64
+cross_entropy (a library routine the oracle does not use).  ``run_pins`` is
+reused by the mutation tests, which plant one plausible mistake at a time in
+the oracle and require at least one pin to fail.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+IGN = -100
+
+
+def _case(seed, N=9, d=6, V=11, n_ign=2, scale=1.0):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((N, d)) * scale
+    W = rng.standard_normal((V, d)) * scale
+    y = rng.integers(0, V, N).astype(np.int64)
+    y[rng.choice(N, n_ign, replace=False)] = IGN
+    return H, W, y
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_w_zero(o):
+    """W = 0: every valid loss is ln V, dH = 0 and
+    dW[v] = w (sum_valid H_n / V - sum_{valid, y_n = v} H_n)."""
+    H, _, y = _case(1)
+    V = 11
+    W = np.zeros((V, H.shape[1]))
+    f = o.forward(H, W, y, IGN)
+    dH, dW = o.backward(H, W, y, IGN)
+    valid = y != IGN
+    nv = int(valid.sum())
+    assert f.valid_count == nv
+    np.testing.assert_allclose(f.loss[valid], math.log(V), rtol=0, atol=4e-16)
+    assert np.all(f.loss[~valid] == 0)
+    assert np.all(dH == 0)
+    w = 1.0 / nv
+    exp = np.tile(H[valid].sum(0) / V, (V, 1))
+    for n in np.flatnonzero(valid):
+        exp[y[n]] -= H[n]
+    np.testing.assert_allclose(dW, w * exp, rtol=1e-13, atol=1e-15)
+    assert abs(f.loss_mean - math.log(V)) < 1e-15
+
+
+def pin_h_zero(o):
+    """H = 0: every valid loss is ln V, dW = 0 and
+    dH[n] = w (sum_v W_v / V - W[y_n]) on valid rows, 0 on ignored rows."""
+    _, W, y = _case(2)
+    H = np.zeros((y.size, W.shape[1]))
+    V = W.shape[0]
+    f = o.forward(H, W, y, IGN)
+    dH, dW = o.backward(H, W, y, IGN, reduction="sum", grad=0.5)
+    valid = y != IGN
+    np.testing.assert_allclose(f.loss[valid], math.log(V), rtol=0, atol=4e-16)
+    assert np.all(dW == 0)
+    for n in range(y.size):
+        if valid[n]:
+            np.testing.assert_allclose(dH[n], 0.5 * (W.mean(0) - W[y[n]]),
+                                       rtol=1e-13, atol=1e-15)
+        else:
+            assert np.all(dH[n] == 0)
+
+
+def pin_v_one(o):
+    """V = 1: the only class has probability 1, so loss and gradients vanish."""
+    H, W, y = _case(3, V=1)
+    y[y != IGN] = 0
+    f = o.forward(H, W, y, IGN)
+    dH, dW = o.backward(H, W, y, IGN)
+    assert np.all(np.abs(f.loss) <= 1e-15)
+    assert np.abs(dH).max() <= 1e-15 and np.abs(dW).max() <= 1e-15
+
+
+def pin_two_class(o):
+    """V = 2 is logistic regression: loss = log(1 + exp(z_o - z_y)) and
+    dloss/dH_n = sigma(z_o - z_y) (W_o - W_y) (sum reduction, grad 1)."""
+    H, W, y = _case(4, V=2, n_ign=1)
+    f = o.forward(H, W, y, IGN)
+    dH, _ = o.backward(H, W, y, IGN, reduction="sum")
+    for n in range(y.size):
+        if y[n] == IGN:
+            continue
+        other = 1 - y[n]
+        t = float(H[n] @ W[other] - H[n] @ W[y[n]])
+        exp_loss = math.log1p(math.exp(t)) if t < 30 else t + math.log1p(math.exp(-t))
+        assert abs(f.loss[n] - exp_loss) <= 1e-13 * max(1.0, exp_loss)
+        sig = 1.0 / (1.0 + math.exp(-t))
+        np.testing.assert_allclose(dH[n], sig * (W[other] - W[y[n]]), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_dw_colsum(o):
+    """Rows of softmax - onehot sum to 0, hence sum_v dW[v, :] = 0."""
+    H, W, y = _case(5, N=13, d=7, V=17)
+    _, dW = o.backward(H, W, y, IGN)
+    assert np.abs(dW.sum(0)).max() <= 1e-14 * max(1.0, np.abs(dW).max())
+    assert np.abs(dW).max() > 1e-3  # non-trivial
+
+
+def pin_shift_invariance(o):
+    """Adding c to every row of W adds H_n.c to every logit of row n, which
+    leaves loss and dH unchanged; a huge common logit offset must stay finite."""
+    H, W, y = _case(6)
+    c = np.random.default_rng(60).standard_normal(W.shape[1])
+    f0 = o.forward(H, W, y, IGN)
+    f1 = o.forward(H, W + c, y, IGN)
+    np.testing.assert_allclose(f1.loss, f0.loss, rtol=1e-10, atol=1e-12)
+    dH0, _ = o.backward(H, W, y, IGN)
+    dH1, _ = o.backward(H, W + c, y, IGN)
+    np.testing.assert_allclose(dH1, dH0, rtol=1e-9, atol=1e-12)
+    # large offset: append a feature of 1s to H and a column 1000 to W
+    Hb = np.concatenate([H, np.ones((H.shape[0], 1))], 1)
+    Wb = np.concatenate([W, np.full((W.shape[0], 1), 1000.0)], 1)
+    f2 = o.forward(Hb, Wb, y, IGN)
+    assert np.all(np.isfinite(f2.loss))
+    np.testing.assert_allclose(f2.loss, f0.loss, rtol=1e-9, atol=1e-9)
+
+
+def pin_permutation(o):
+    """Permuting W's rows and relabelling permutes dW's rows the same way."""
+    H, W, y = _case(7)
+    V = W.shape[0]
+    perm = np.random.default_rng(70).permutation(V)
+    inv = np.argsort(perm)
+    y2 = y.copy()
+    y2[y != IGN] = inv[y[y != IGN]]          # new row inv[v] holds old row v
+    W2 = W[perm]
+    f0, f1 = o.forward(H, W, y, IGN), o.forward(H, W2, y2, IGN)
+    np.testing.assert_allclose(f1.loss, f0.loss, rtol=1e-12, atol=1e-14)
+    _, dW0 = o.backward(H, W, y, IGN)
+    _, dW1 = o.backward(H, W2, y2, IGN)
+    np.testing.assert_allclose(dW1, dW0[perm], rtol=1e-11, atol=1e-14)
+
+
+def pin_ignored_rows(o):
+    """Ignored rows contribute nothing: giving their H rows huge values changes
+    no output, their loss and dH rows are 0, and the count excludes them."""
+    H, W, y = _case(8, n_ign=3)
+    ign = y == IGN
+    H2 = H.copy()
+    H2[ign] = 1e3
+    f0, f1 = o.forward(H, W, y, IGN), o.forward(H2, W, y, IGN)
+    assert f0.valid_count == int((~ign).sum()) == f1.valid_count
+    np.testing.assert_array_equal(f0.loss, f1.loss)
+    assert np.all(f0.loss[ign] == 0)
+    dH0, dW0 = o.backward(H, W, y, IGN)
+    dH1, dW1 = o.backward(H2, W, y, IGN)
+    np.testing.assert_array_equal(dW0, dW1)
+    assert np.all(dH1[ign] == 0)
+    np.testing.assert_array_equal(dH0, dH1)
+    assert np.all(f0.loss[~ign] > 0)
+
+
+def pin_ignore_inside_range(o):
+    """ignore_index may be a real class id: those rows are skipped."""
+    H, W, y = _case(9, n_ign=0)
+    y[[0, 3]] = 4
+    f = o.forward(H, W, y, 4)
+    keep = y != 4
+    assert f.valid_count == int(keep.sum())
+    assert np.all(f.loss[~keep] == 0)
+    g = o.forward(H[keep], W, y[keep], IGN)
+    np.testing.assert_allclose(f.loss[keep], g.loss, rtol=1e-14, atol=0)
+
+
+def pin_bad_label(o):
+    """A valid label outside [0, V) is an error, not an out-of-bounds read."""
+    H, W, y = _case(10)
+    y[np.flatnonzero(y != IGN)[0]] = W.shape[0]
+    try:
+        o.forward(H, W, y, IGN)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("label == V was accepted")
+    y[np.flatnonzero(y != IGN)[0]] = -5
+    try:
+        o.backward(H, W, y, IGN)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("label -5 was accepted")
+
+
+# ------------------------------------------------------------ finite differences
+
+def pin_finite_differences(o):
+    """Central differences of the mean loss match dH and dW entry by entry."""
+    H, W, y = _case(11, N=5, d=4, V=7, n_ign=1)
+    dH, dW = o.backward(H, W, y, IGN)
+
+    def mean_loss(Hx, Wx):
+        return o.forward(Hx, Wx, y, IGN).loss_mean
+
+    for arr, grad, which in ((H, dH, 0), (W, dW, 1)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            h = 1e-6 * max(1.0, abs(arr[idx]))
+            a, b = arr.copy(), arr.copy()
+            a[idx] += h
+            b[idx] -= h
+            fa = mean_loss(a, W) if which == 0 else mean_loss(H, a)
+            fb = mean_loss(b, W) if which == 0 else mean_loss(H, b)
+            num[idx] = (fa - fb) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-9)
+    assert np.all(dH[y == IGN] == 0)
+
+
+# ---------------------------------------------------- high precision brute force
+
+def pin_mpmath(o):
+    """loss_n = -log(exp(z_y) / sum_v exp(z_v)) with z the exact rational dot
+    product of the float inputs, evaluated with 50 significant digits."""
+    import mpmath
+    mpmath.mp.dps = 50
+    H, W, y = _case(12, N=6, d=5, V=9, n_ign=1, scale=3.0)
+    f = o.forward(H, W, y, IGN)
+    total = mpmath.mpf(0)
+    nv = 0
+    for n in range(y.size):
+        if y[n] == IGN:
+            assert f.loss[n] == 0
+            continue
+        z = [sum(Fraction(float(H[n, k])) * Fraction(float(W[v, k]))
+                 for k in range(H.shape[1])) for v in range(W.shape[0])]
+        zs = [mpmath.mpf(q.numerator) / q.denominator for q in z]
+        p = mpmath.exp(zs[y[n]]) / mpmath.fsum(mpmath.exp(t) for t in zs)
+        ref = -mpmath.log(p)
+        assert abs(f.loss[n] - float(ref)) <= 1e-13 * max(1.0, abs(float(ref)))
+        total += ref
+        nv += 1
+    assert abs(f.loss_mean - float(total / nv)) <= 1e-13
+
+
+# -------------------------------------------------------------- library routine
+
+def pin_torch_cross_entropy(o):
+    """PyTorch CPU float64 cross_entropy with ignore_index and autograd."""
+    import torch
+    import torch.nn.functional as F
+    for seed, red in ((13, "mean"), (14, "sum")):
+        H, W, y = _case(seed, N=23, d=8, V=19, n_ign=4)
+        Ht = torch.tensor(H, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        loss = F.cross_entropy(Ht @ Wt.T, torch.tensor(y), ignore_index=IGN, reduction=red)
+        loss.backward()
+        f = o.forward(H, W, y, IGN)
+        dH, dW = o.backward(H, W, y, IGN, reduction=red)
+        ref = f.loss_mean if red == "mean" else f.loss_sum
+        assert abs(ref - loss.item()) <= 1e-13 * max(1.0, abs(loss.item()))
+        per = F.cross_entropy(Ht.detach() @ Wt.detach().T, torch.tensor(y),
+                              ignore_index=IGN, reduction="none").numpy()
+        np.testing.assert_allclose(f.loss, per, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(dH, Ht.grad.numpy(), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------- row-sampled entry points
+
+def pin_row_functions(o):
+    """The per-row helpers used for sampled checks agree with the full pass
+    (the full pass itself is pinned above)."""
+    H, W, y = _case(15, N=17, d=5, V=13, n_ign=3)
+    f = o.forward(H, W, y, IGN)
+    dH, dW = o.backward(H, W, y, IGN)
+    rows = f.valid_idx[::2]
+    l, loss, _ = o.rows_forward(H, W, y, rows)
+    np.testing.assert_allclose(l, f.lse[rows], rtol=1e-14)
+    np.testing.assert_allclose(loss, f.loss[rows], rtol=1e-14)
+    w = 1.0 / f.valid_count
+    np.testing.assert_allclose(o.rows_dH(H, W, y, rows, w), dH[rows], rtol=1e-12, atol=1e-16)
+    vr = np.array([0, 3, 12])
+    got = o.rows_dW(H, W, y, f.valid_idx, f.lse[f.valid_idx], vr, w, row_block=4)
+    np.testing.assert_allclose(got, dW[vr], rtol=1e-12, atol=1e-16)
+
+
+def pin_compaction(o):
+    """valid_idx is the ascending list of rows whose label is kept, found by a
+    plain loop; out-of-range labels are reported, not kept."""
+    rng = np.random.default_rng(16)
+    y = rng.integers(-3, 40, 200).astype(np.int64)
+    y[rng.choice(200, 50, replace=False)] = IGN
+    idx, n, bad = o.compact_valid(y, IGN, 37)
+    exp_idx, exp_bad = [], []
+    for r in range(200):
+        if y[r] == IGN:
+            continue
+        (exp_idx if 0 <= y[r] < 37 else exp_bad).append(r)
+    assert n == len(exp_idx)
+    assert idx.tolist() == exp_idx and idx.dtype == np.int32
+    assert bad.tolist() == exp_bad
+
+
+PINS = [
+    pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
+    pin_shift_invariance, pin_permutation, pin_ignored_rows,
+    pin_ignore_inside_range, pin_bad_label, pin_finite_differences,
+    pin_mpmath, pin_torch_cross_entropy, pin_row_functions, pin_compaction,
+]
+
+
+def run_pins(o, pins=PINS):
+    """Names of the pins that fail for oracle module ``o``."""
+    failed = []
+    for p in pins:
+        try:
+            p(o)
+        except Exception:  # noqa: BLE001 -- any error counts as a failed pin
+            failed.append(p.__name__)
+    return failed

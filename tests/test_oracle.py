@@ -1,0 +1,108 @@
+"""The fp64 oracle against its pins, plus planted-mistake (mutation) checks.
+
+A pin that still passes when a plausible mistake is planted in the oracle
+tests nothing (the lesson of bug #138 on "6GB显卡预训练11亿参数模型", section
+可证伪测试抓到的8个静默bug: a comparison that passes at zero difference).  Every
+mutation below must make at least one pin fail.  Mistakes are planted in the
+oracle, on the CPU.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.lce_oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(O)
+
+
+def _no_onehot(Z, lse, y, w):
+    return np.exp(Z - lse[:, None]) * w
+
+
+def _wrong_sign(Z, lse, y, w):
+    P_ = np.exp(Z - lse[:, None])
+    P_[np.arange(Z.shape[0]), y] -= 1.0
+    return -P_ * w
+
+
+def _unscaled(Z, lse, y, w):
+    P_ = np.exp(Z - lse[:, None])
+    P_[np.arange(Z.shape[0]), y] -= 1.0
+    return P_
+
+
+def _label_off_by_one(Z, y):
+    return Z[np.arange(Z.shape[0]), (y + 1) % Z.shape[1]]
+
+
+def _dropped_feature(Hb, W):
+    Hb = np.asarray(Hb, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return Hb[:, :-1] @ W[:, :-1].T
+
+
+def _unshifted_lse(Z):
+    with np.errstate(over="ignore"):
+        return np.log(np.exp(Z).sum(axis=1))
+
+
+def _max_only_lse(Z):
+    return Z.max(axis=1)
+
+
+def _keep_everything(labels, ignore_index):
+    return np.ones(np.asarray(labels).shape, dtype=bool)
+
+
+def _mean_over_all(reduction, grad, n_valid):
+    return grad / (n_valid + 2)
+
+
+def _softmax_wrong_axis(Z, lse, y, w):
+    # normalise over the wrong axis (columns instead of rows)
+    m = Z.max(axis=0)
+    l0 = m + np.log(np.exp(Z - m[None, :]).sum(axis=0))
+    P_ = np.exp(Z - l0[None, :])
+    P_[np.arange(Z.shape[0]), y] -= 1.0
+    return P_ * w
+
+
+MUTATIONS = {
+    "dlogits_without_onehot": ("dlogits", _no_onehot),
+    "dlogits_wrong_sign": ("dlogits", _wrong_sign),
+    "dlogits_missing_scale": ("dlogits", _unscaled),
+    "dlogits_softmax_over_wrong_axis": ("dlogits", _softmax_wrong_axis),
+    "target_label_off_by_one": ("target_logits", _label_off_by_one),
+    "logits_dropped_feature": ("logits", _dropped_feature),
+    "lse_without_max_shift": ("logsumexp_rows", _unshifted_lse),
+    "lse_max_only": ("logsumexp_rows", _max_only_lse),
+    "ignore_index_not_skipped": ("valid_mask", _keep_everything),
+    "mean_over_wrong_count": ("_scale", _mean_over_all),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = P.run_pins(O)
+    assert failed, f"mutation {name} passed every pin"
+
+
+def test_statistical_band_tiny_fp32():
+    """Gaussian inputs: mean loss ~ ln V + sigma^2/2 with
+    sigma^2 = d Var(H) Var(W) (sanity check of generator + oracle)."""
+    from workloads import generate, CONFIGS
+    wl = CONFIGS[1]
+    H, W, y = generate(1)
+    f = O.forward(H, W, y, -100)
+    assert f.valid_count == 58
+    s2 = wl.d * wl.h_std ** 2 * wl.w_std ** 2
+    exp = math.log(wl.V) + s2 / 2
+    sd = math.sqrt(s2) / math.sqrt(f.valid_count) + 1e-6
+    assert abs(f.loss_mean - exp) < 5 * sd
