@@ -1,0 +1,216 @@
+"""Benchmark of the fused linear + cross-entropy path (forward + backward).
+
+One step = lce_forward + lce_backward over one batch of seeded synthetic
+input already resident in HBM: valid-token compaction, fused projection +
+online logsumexp, chunk merge, loss reduction, dH zeroing of ignored rows,
+operand layout for backward, logit recompute + G, dH += G W, dW += G^T H.
+
+Default workload: the Llama-3-8B-shaped head (N = 4 x 2048 tokens, d = 4096,
+V = 128256, per-sequence valid lengths uniform in [512, 2048], Zipf labels).
+Prints one JSON line with valid tokens/s, TFLOP/s (8 N_valid d V per step),
+the roofline entry of the dominant kernel (device time from HIP events on
+the launch stream), and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "valid tokens/sec and % bf16 MFMA peak, fused linear-CE fwd+bwd, d=4096 V=128256"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+# FLOPs per step of each kernel class, as a multiple of N_valid * d * V
+CLASS_FLOPS = {"fwd": 2, "bwd_g": 2, "dh": 2, "dw": 2}
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(H, W, y, target_s: float):
+    """The fp64 oracle on a sample of valid rows (full V and d), timed."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()
+                      if p.get("user_api") == "blas") or None
+    except Exception:  # noqa: BLE001
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    valid = np.flatnonzero(y != -100)
+
+    def run(nrows):
+        rows = valid[:nrows]
+        t0 = time.perf_counter()
+        oracle.forward(H[rows], W, y[rows], -100)
+        oracle.backward(H[rows], W, y[rows], -100)
+        return time.perf_counter() - t0
+
+    n = 16
+    t = run(n)
+    # per-row cost plus a fixed part (float64 copies of W); aim at target_s total
+    n2 = int(min(len(valid), max(n, n * target_s / max(t, 1e-3))))
+    if n2 > n:
+        t = run(n2)
+        n = n2
+    return {"value": n / t, "unit": "valid tokens/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"{n} valid rows of the same workload (full V and d), fp64 forward + "
+                      f"backward, {t:.1f} s; host cores available: {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the bare-GEMM reference rate")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no communication in forward; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from vocab_cross_entropy_valid_amd import _lib, torch_api
+
+    wl = workloads.CONFIGS[args.config]
+    _log(f"[bench] generating {wl.name}: N={wl.N} d={wl.d} V={wl.V} {wl.dtype}")
+    H, W, y = workloads.generate(args.config)
+    n_valid = int(np.count_nonzero(y != -100))
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Ht = torch.from_numpy(H).to(dev, dt)
+    Wt = torch.from_numpy(W).to(dev, dt)
+    yt = torch.from_numpy(y).to(dev)
+    ws = torch_api.alloc_workspace(wl.N, wl.d, wl.V, dt, dev)
+    dH = torch.empty(wl.N, wl.d, dtype=torch.float32, device=dev)
+    dW = torch.empty(wl.V, wl.d, dtype=torch.float32, device=dev)
+    g = torch.ones(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        fwd = torch_api.forward(Ht, Wt, yt, workspace=ws, check=False)
+        torch_api.backward(Ht, Wt, yt, fwd, grad_out=g, dH=dH, dW=dW, workspace=ws)
+        return fwd
+
+    _log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        fwd = step()
+    torch.cuda.synchronize()
+    _lib.lce_check_error(fwd.err_flag.data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    _lib.lce_timing_reset()
+    _lib.lce_timing_enable(True)
+    _log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.lce_timing_enable(False)
+    kernels = {}
+    for k, name in enumerate(_lib.KERNEL_CLASSES):
+        ms, n = _lib.lce_timing_query(k)
+        if n:
+            kernels[name] = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                             "avg_launch_us": 1e3 * ms / n}
+    _lib.lce_timing_reset()
+    assert int(fwd.valid_count.item()) == n_valid
+    loss_mean = float(fwd.loss_mean.item())
+    _log(f"[bench] done: {1e3 * elapsed / args.steps:.3f} ms/step, mean loss {loss_mean:.5f}")
+
+    ms_step = 1e3 * elapsed / args.steps
+    flops = 8.0 * n_valid * wl.d * wl.V
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # roofline entry of the dominant kernel class (largest device time per step)
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    if dom in CLASS_FLOPS:
+        per_step = CLASS_FLOPS[dom] * n_valid * wl.d * wl.V
+        ach = per_step / (kernels[dom]["ms_per_step"] * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "flops_per_launch": per_step / kernels[dom]["launches_per_step"],
+                    "avg_launch_us": round(kernels[dom]["avg_launch_us"], 2)}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": None, "traffic": None}
+
+    gemm = None
+    if not args.no_gemm and wl.dtype == "bf16":
+        # bare GEMM of the same engine at the forward's shape (N_valid x V x d)
+        A = Ht[:n_valid].contiguous()
+        C = torch.empty(n_valid, wl.V, dtype=torch.float32, device=dev)
+        s = torch.cuda.current_stream().cuda_stream
+        for _ in range(2):
+            _lib.lce_gemm_nt(A.data_ptr(), Wt.data_ptr(), C.data_ptr(), n_valid, wl.V, wl.d,
+                             _lib.LCE_BF16, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 5
+        for _ in range(reps):
+            _lib.lce_gemm_nt(A.data_ptr(), Wt.data_ptr(), C.data_ptr(), n_valid, wl.V, wl.d,
+                             _lib.LCE_BF16, s)
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / reps
+        gemm = {"shape": [n_valid, wl.V, wl.d], "ms": round(gms, 3),
+                "tflops": round(2.0 * n_valid * wl.V * wl.d / (gms * 1e-3) / 1e12, 1)}
+        del C
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        _log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(H, W, y, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(n_valid / (ms_step * 1e-3), 1),
+        "unit": "valid tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded Gaussian H, W and Zipf labels with padding (no dataset)",
+        "config": {"workload": f"{wl.name} (config {wl.cid})", "N": wl.N, "d": wl.d, "V": wl.V,
+                   "N_valid": n_valid, "ignore_index": -100, "seed": wl.seed},
+        "tflops": round(tflops, 2),
+        "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "mean_loss": loss_mean,
+        "workspace_bytes": int(ws.numel()),
+        "logits_table_bytes_avoided": wl.N * wl.V * 4,
+        "roofline": roofline,
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
+        "gemm_engine_reference": gemm,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * lce.h -- fused linear + cross-entropy over a large vocabulary, forward and
+ * backward, for AMD Instinct MI355X (gfx950).  C ABI, no C++ or torch types.
+ *
+ * The operation (for every row n of H that is not ignored):
+ *
+ *     z[n, v]  = sum_k H[n, k] W[v, k]
+ *     lse[n]   = log sum_v exp(z[n, v])
+ *     loss[n]  = lse[n] - z[n, labels[n]]
+ *
+ * and its gradient with respect to H and W for the mean (or sum) of loss over
+ * the valid rows.  The projection and the loss are computed in streaming
+ * tiles and never stored as an [N, V] logits table ("OjasX 0.6.1", section
+ * 核心技术 / Core Technology: zero-byte vocabulary logits table, chunked
+ * streaming projection + loss that skips padding tokens); the running max and
+ * normaliser are merged tile by tile (same page, Online Softmax paragraph);
+ * the backward pass recomputes the logits per chunk instead of saving them
+ * ("6GB显卡预训练11亿参数模型", sections 内存实际花在哪里 and 关键参数说明,
+ * --chunked-loss 512); rows are selected by a device-side valid-token index
+ * built without a host round trip (MaximusLLM page, section 2.3).
+ *
+ * Conventions shared by every entry point
+ *   - H is [N, d], W is [V, d], both row-major and contiguous, same dtype:
+ *     LCE_BF16 (bfloat16, fp32 accumulation) or LCE_F32.  W is the layout of
+ *     nn.Linear(d, V).weight and of nn.Embedding(V, d).weight, so a tied
+ *     embedding table is passed as is.
+ *   - labels is int64 [N].  A row is valid when labels[n] != ignore_index.  A
+ *     valid label must lie in [0, V); one that does not is reported through
+ *     err_flag (see lce_forward) and its row is treated as ignored.
+ *   - Every pointer argument is DEVICE memory owned by the caller, except
+ *     where noted.  The library allocates no device memory: scratch space is
+ *     the caller's `workspace` of at least lce_workspace_bytes(...) bytes,
+ *     256-byte aligned.  Its size does not depend on N beyond O(N) per-token
+ *     vectors and never on N * V.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every kernel is
+ *     launched on it and the calls return without synchronising (except
+ *     lce_check_error and lce_timing_query).
+ *   - Requirements: N >= 0, d > 0 with d % 64 == 0, V > 0, N, V and d below
+ *     2^31.  Outputs must not alias inputs.
+ *   - No state is kept between calls (besides the optional timing registry);
+ *     calls on different streams may run concurrently if they use different
+ *     workspaces and outputs.
+ *   - Errors are returned as lce_status; a host-checkable problem returns
+ *     before anything is launched.  lce_last_error() gives a message.
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCE_OK = 0,
+  LCE_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad enum value   */
+  LCE_ERR_UNSUPPORTED = 2,  /* shape outside the supported range (d % 64)     */
+  LCE_ERR_WORKSPACE = 3,    /* workspace smaller than lce_workspace_bytes     */
+  LCE_ERR_LABEL_RANGE = 4,  /* a valid label was outside [0, V) (from flag)   */
+  LCE_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed      */
+} lce_status;
+
+typedef enum { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype;
+typedef enum { LCE_MEAN = 0, LCE_SUM = 1 } lce_reduction;
+
+/* Bytes of device workspace that lce_forward and lce_backward need for these
+ * sizes (the larger of the two; the calls may share one buffer).  Returns 0
+ * for invalid sizes. */
+size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype);
+
+/* Forward pass.
+ *
+ *  H, W, labels   inputs as above.
+ *  ignore_index   label value of rows that take no part (PyTorch default -100;
+ *                 it may also be a class id inside [0, V)).
+ *  loss  [N] f32  per-row loss; 0 on ignored rows.
+ *  lse   [N] f32  per-row logsumexp; 0 on ignored rows.  Needed by backward.
+ *  valid_idx [N] int32   ascending original row numbers of the valid rows;
+ *                 the first *valid_count entries are meaningful.
+ *  valid_count [1] int32 number of valid rows.
+ *  loss_sum [1] f64      sum of loss over valid rows, summed in a fixed order
+ *                 (bitwise reproducible).
+ *  loss_mean [1] f32     loss_sum / valid_count, NaN when valid_count == 0;
+ *                 may be NULL.
+ *  err_flag [1] int32    set to 1 when a valid label lies outside [0, V),
+ *                 else 0; the call never reads W out of bounds.  Turn it into
+ *                 a status with lce_check_error.
+ */
+lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                       int64_t N, int64_t d, int64_t V, int dtype, float* loss, float* lse,
+                       int32_t* valid_idx, int32_t* valid_count, double* loss_sum,
+                       float* loss_mean, int32_t* err_flag, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Backward pass: dH = dL/dH [N, d] f32 and dW = dL/dW [V, d] f32 for
+ * L = mean (reduction LCE_MEAN) or sum (LCE_SUM) of loss over valid rows,
+ * scaled by the upstream gradient *grad_out (a device f32 scalar).
+ *
+ *  lse, valid_idx, valid_count  exactly as produced by lce_forward for the
+ *                 same H, W, labels and ignore_index.
+ *  dH             fully written: rows of ignored tokens are 0.
+ *  dW             overwritten when accumulate_dW == 0, added to otherwise
+ *                 (for a weight that also receives other gradients).
+ * The logits are recomputed chunk by chunk; nothing of size N * V is stored.
+ * No floating-point atomics are used: results are bitwise reproducible.
+ */
+lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                        const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                        int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
+                        int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream` and returns LCE_ERR_LABEL_RANGE when *err_flag is set
+ * (a valid label outside [0, V) -- the out-of-range index failure described
+ * in "6GB显卡预训练11亿参数模型", section 可证伪测试抓到的8个静默bug, #155),
+ * LCE_OK otherwise.  err_flag is device memory. */
+lce_status lce_check_error(const int32_t* err_flag, void* stream);
+
+/* Static description of a status code. */
+const char* lce_status_string(lce_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* lce_last_error(void);
+
+/* ---------------------------------------------------------- measurement */
+
+/* C[M, N] = A[M, K] B[N, K]^T with the same MFMA tile engine as the path
+ * (f32 output, row-major; K % 64 == 0).  Used to measure the engine's bare
+ * GEMM rate at the path's shapes and to check its layout in isolation. */
+lce_status lce_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                       int dtype, void* stream);
+
+/* Kernel classes for the optional timing registry. */
+typedef enum {
+  LCE_K_COMPACT = 0,   /* valid-token compaction                         */
+  LCE_K_FWD = 1,       /* fused projection + online logsumexp            */
+  LCE_K_MERGE = 2,     /* merge of vocabulary-chunk partials             */
+  LCE_K_REDUCE = 3,    /* loss reduction                                 */
+  LCE_K_ZERO = 4,      /* zeroing dH rows of ignored tokens              */
+  LCE_K_TRANSPOSE = 5, /* W / H^T operand layout for backward            */
+  LCE_K_BWD_G = 6,     /* logit recompute + G tile                       */
+  LCE_K_DH = 7,        /* dH += G W                                      */
+  LCE_K_DW = 8,        /* dW += G^T H                                    */
+  LCE_K_GEMM = 9,      /* lce_gemm_nt                                    */
+  LCE_K_COUNT = 10
+} lce_kernel_class;
+
+/* When enabled, every launch is bracketed by HIP events recorded on the
+ * launch stream (host-side registry, process-wide). */
+lce_status lce_timing_enable(int on);
+/* Clears the registry. */
+lce_status lce_timing_reset(void);
+/* Synchronises on the recorded events and returns, for one kernel class, the
+ * summed device time in milliseconds and the number of launches (both host
+ * pointers). */
+lce_status lce_timing_query(int kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lce.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocab_cross_entropy_valid_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lce.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lce_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("lce_forward", "lce_backward", "lce_workspace_bytes", "lce_status_string",
+              "lce_check_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    assert _lib.lce_status_string(0) == "ok"
+    assert "label" in _lib.lce_status_string(_lib.LCE_ERR_LABEL_RANGE)
+    assert _lib.lce_status_string(99) == "unknown status"
+
+
+def test_workspace_bounded_independent_of_n_times_v():
+    bf = _lib.LCE_BF16
+    # configs 3 and 5 differ only in N: the backward block dominates, same bytes
+    w3 = _lib.lce_workspace_bytes(8192, 4096, 128256, bf)
+    w5 = _lib.lce_workspace_bytes(65536, 4096, 128256, bf)
+    assert w3 == w5
+    # far below the [N, V] fp32 logits table it replaces
+    assert w5 < 65536 * 128256 * 4 / 50
+    # growing V past the vocabulary block does not grow the workspace
+    assert _lib.lce_workspace_bytes(8192, 4096, 260000, bf) == w3
+    # growing N only adds O(N) per-token vectors
+    big = _lib.lce_workspace_bytes(1 << 22, 4096, 128256, bf)
+    assert big - w5 < (1 << 22) * 64 * 3 * 4 + (1 << 22) * 4 + (1 << 20)
+    assert _lib.lce_workspace_bytes(64, 128, 1024, _lib.LCE_F32) > 0
+
+
+@pytest.mark.parametrize("N,d,V,dt,status", [
+    (-1, 64, 10, 1, _lib.LCE_ERR_INVALID_ARG),
+    (10, 0, 10, 1, _lib.LCE_ERR_INVALID_ARG),
+    (10, 64, 0, 1, _lib.LCE_ERR_INVALID_ARG),
+    (10, 64, 10, 7, _lib.LCE_ERR_INVALID_ARG),
+    (10, 100, 10, 1, _lib.LCE_ERR_UNSUPPORTED),
+    (10, 64, 1 << 31, 1, _lib.LCE_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_bad_sizes_before_launch(N, d, V, dt, status):
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    r = lib.lce_forward(fake, fake, fake, -100, N, d, V, dt, fake, fake, fake, fake, fake,
+                        None, fake, fake, 1 << 40, None)
+    assert r == status
+    assert _lib.lce_last_error() != ""
+    assert _lib.lce_workspace_bytes(N, d, V, dt) == 0
+
+
+def test_forward_rejects_null_and_small_workspace():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    r = lib.lce_forward(None, fake, fake, -100, 10, 64, 10, 1, fake, fake, fake, fake, fake,
+                        None, fake, fake, 1 << 40, None)
+    assert r == _lib.LCE_ERR_INVALID_ARG
+    need = _lib.lce_workspace_bytes(10, 64, 10, 1)
+    r = lib.lce_forward(fake, fake, fake, -100, 10, 64, 10, 1, fake, fake, fake, fake, fake,
+                        None, fake, fake, need - 1, None)
+    assert r == _lib.LCE_ERR_WORKSPACE
+    r = lib.lce_forward(fake, fake, fake, -100, 10, 64, 10, 1, fake, fake, fake, fake, fake,
+                        None, fake, ctypes.c_void_p(0x1010), need, None)
+    assert r == _lib.LCE_ERR_INVALID_ARG  # misaligned workspace
+
+
+def test_backward_rejects_bad_reduction_and_nulls():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, fake, fake, -100, fake, fake, fake, 10, 64, 10, 1, fake, 5, fake, fake, 0,
+            fake, 1 << 40, None]
+    assert lib.lce_backward(*args) == _lib.LCE_ERR_INVALID_ARG
+    args[12] = 0
+    args[11] = None  # grad_out
+    assert lib.lce_backward(*args) == _lib.LCE_ERR_INVALID_ARG
+    args[11] = fake
+    args[16] = fake
+    args[17] = 16
+    assert lib.lce_backward(*args) == _lib.LCE_ERR_WORKSPACE
+
+
+def test_gemm_and_timing_argument_checks():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.lce_gemm_nt(fake, fake, fake, 10, 10, 100, 1, None) == _lib.LCE_ERR_UNSUPPORTED
+    assert lib.lce_gemm_nt(fake, fake, fake, 0, 10, 64, 1, None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_check_error(None, None) == _lib.LCE_ERR_INVALID_ARG
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    assert lib.lce_timing_query(99, ctypes.byref(ms), ctypes.byref(n)) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_timing_reset() == 0
+    assert lib.lce_timing_query(0, ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        _lib.load(str(tmp_path / "nope.so"))

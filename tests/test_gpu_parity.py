@@ -1,0 +1,222 @@
+"""GPU path (HIP kernels via the C ABI) against the fp64 CPU oracle.
+
+Tolerances: valid_count / valid_idx bit-exact; fp32 inputs: mean loss within
+1e-5 relative, dH and dW within 1e-4 relative L2; bf16 inputs (fp32 accumulation): mean loss within 2e-3
+absolute and dH, dW within 1e-2 relative L2.  Per-token loss is also held to
+1e-4 absolute: the logits are fp32 sums of exactly the oracle's bf16 inputs,
+so the only per-token error is fp32 rounding of the sums (~1e-6 relative
+over d <= 4096 terms) and of the hardware exp2/log2 (a few ulp), far below
+1e-4 for losses around 10.  Sizes span several 256-wide tiles in every
+dimension and end in ragged tails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_helpers import announce, rel_l2, run_path, to_dev
+
+pytestmark = pytest.mark.gpu
+
+IGN = -100
+
+
+def _check(out, H, W, y, dtype, ignore_index=IGN, reduction="mean", grad=1.0,
+           bad_labels="raise"):
+    ref = oracle.forward(H, W, y, ignore_index, bad_labels=bad_labels)
+    idx, n_valid, _ = oracle.compact_valid(y, ignore_index, W.shape[0])
+    assert out["valid_count"] == n_valid
+    np.testing.assert_array_equal(out["valid_idx"][:n_valid], idx)
+    if n_valid:
+        if dtype == "f32":
+            assert abs(out["loss_mean"] - ref.loss_mean) <= 1e-5 * abs(ref.loss_mean)
+            np.testing.assert_allclose(out["loss"], ref.loss, rtol=1e-5, atol=1e-6)
+        else:
+            assert abs(out["loss_mean"] - ref.loss_mean) <= 2e-3
+            np.testing.assert_allclose(out["loss"], ref.loss, rtol=0, atol=1e-4)
+        np.testing.assert_allclose(out["lse"][idx], ref.lse[idx], rtol=0, atol=1e-4)
+        assert abs(out["loss_sum"] - ref.loss_sum) <= 1e-5 * max(1.0, abs(ref.loss_sum))
+    else:
+        assert np.isnan(out["loss_mean"]) and out["loss_sum"] == 0.0
+    ign = np.ones(y.shape[0], dtype=bool)
+    ign[idx] = False
+    assert np.all(out["loss"][ign] == 0)
+    if "dH" in out:
+        rdH, rdW = oracle.backward(H, W, y, ignore_index, grad=grad, reduction=reduction,
+                                   bad_labels=bad_labels)
+        assert np.all(out["dH"][ign] == 0)
+        if n_valid:
+            # fp32: the grads carry the lse rounding (~1e-6 relative of lse ~ 7
+            # moves every p = exp(z - lse) by ~7e-6 relative); 1e-4 is well above it
+            tol = 1e-4 if dtype == "f32" else 1e-2
+            assert rel_l2(out["dH"], rdH) <= tol, rel_l2(out["dH"], rdH)
+            assert rel_l2(out["dW"], rdW) <= tol, rel_l2(out["dW"], rdW)
+        else:
+            assert np.all(out["dH"] == 0) and np.all(out["dW"] == 0)
+    return ref
+
+
+# --------------------------------------------------------------- tile engine
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gemm_engine_layout(dtype):
+    """The bare MFMA tile engine against a float64 matrix product."""
+    import torch
+    from vocab_cross_entropy_valid_amd import _lib
+    announce(f"gemm_nt {dtype} 300x520x192")
+    rng = np.random.default_rng(3)
+    A = workloads.bf16_round(rng.standard_normal((300, 192)).astype(np.float32))
+    B = workloads.bf16_round(rng.standard_normal((520, 192)).astype(np.float32))
+    At, Bt, _ = to_dev(A, B, np.zeros(1, np.int64), dtype)
+    C = torch.empty(300, 520, dtype=torch.float32, device=At.device)
+    _lib.lce_gemm_nt(At.data_ptr(), Bt.data_ptr(), C.data_ptr(), 300, 520, 192,
+                     _lib.LCE_BF16 if dtype == "bf16" else _lib.LCE_F32,
+                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    np.testing.assert_allclose(C.cpu().numpy(), ref, rtol=0, atol=1e-4)
+
+
+# ------------------------------------------------------------------ configs
+
+def test_config1_tiny_fp32():
+    announce("config 1 tiny fp32 N=64 d=128 V=1024")
+    H, W, y = workloads.generate(1)
+    _check(run_path(H, W, y, "f32"), H, W, y, "f32")
+
+
+@pytest.mark.parametrize("N,d,V,dtype,ign,seed", [
+    (600, 256, 3000, "bf16", 0.1, 11),     # ragged N, V (V % 64 != 0)
+    (1100, 128, 9000, "bf16", 0.3, 12),    # many vocabulary chunks
+    (300, 64, 20000, "bf16", 0.1, 13),     # several backward vocabulary blocks
+    (333, 64, 1500, "f32", 0.2, 14),       # fp32, ragged everywhere
+    (257, 192, 257, "bf16", 0.0, 15),      # one past a tile in N and V
+    (9000, 64, 700, "bf16", 0.05, 16),     # several backward token chunks
+])
+def test_parity_small(N, d, V, dtype, ign, seed):
+    announce(f"parity N={N} d={d} V={V} {dtype} ignore={ign} seed={seed}")
+    H, W, y = workloads.custom(N, d, V, dtype=dtype, seed=seed, ignore_frac=ign)
+    _check(run_path(H, W, y, dtype), H, W, y, dtype)
+
+
+def test_reduction_sum_and_grad_scale():
+    announce("reduction=sum grad=2.5")
+    H, W, y = workloads.custom(400, 128, 2100, seed=21)
+    out = run_path(H, W, y, "bf16", reduction="sum", grad=2.5)
+    _check(out, H, W, y, "bf16", reduction="sum", grad=2.5)
+
+
+def test_large_logits_stay_finite():
+    announce("large logits")
+    H, W, y = workloads.custom(300, 128, 1000, seed=22, w_std=0.5, h_std=2.0)
+    out = run_path(H, W, y, "bf16")
+    assert np.all(np.isfinite(out["loss"])) and np.all(np.isfinite(out["dW"]))
+    _check(out, H, W, y, "bf16")
+
+
+# -------------------------------------------------------------- edge cases
+
+def test_all_rows_ignored():
+    announce("all ignored")
+    H, W, y = workloads.custom(130, 64, 500, seed=31)
+    y[:] = IGN
+    out = run_path(H, W, y, "bf16")
+    _check(out, H, W, y, "bf16")
+
+
+def test_single_row():
+    announce("N=1")
+    H, W, y = workloads.custom(1, 64, 777, seed=32, ignore_frac=0.0)
+    _check(run_path(H, W, y, "bf16"), H, W, y, "bf16")
+
+
+@pytest.mark.parametrize("N", [63, 64, 65, 1023, 1024, 1025, 2049])
+def test_compaction_boundaries(N):
+    announce(f"compaction N={N}")
+    H, W, y = workloads.custom(N, 64, 300, seed=N, ignore_frac=0.37)
+    out = run_path(H, W, y, "bf16", backward=False)
+    idx, n, _ = oracle.compact_valid(y, IGN, 300)
+    assert out["valid_count"] == n
+    np.testing.assert_array_equal(out["valid_idx"][:n], idx)
+
+
+def test_ignore_index_inside_vocabulary():
+    announce("ignore_index=5")
+    H, W, y = workloads.custom(500, 64, 300, seed=33, ignore_frac=0.0, zipf_s=1.1)
+    assert np.count_nonzero(y == 5) > 0
+    _check(run_path(H, W, y, "bf16", ignore_index=5), H, W, y, "bf16", ignore_index=5)
+
+
+def test_out_of_range_label_is_reported_not_read():
+    """A valid label outside [0, V) sets the error flag (no out-of-bounds read);
+    the row is treated as ignored and every other row is still exact."""
+    announce("bad labels")
+    H, W, y = workloads.custom(300, 64, 400, seed=34)
+    y[7] = 400
+    y[100] = -3
+    out = run_path(H, W, y, "bf16", check=False)
+    assert out["err_flag"] == 1
+    _check(out, H, W, y, "bf16", bad_labels="ignore")
+    with pytest.raises(ValueError, match="outside"):
+        run_path(H, W, y, "bf16", backward=False, check=True)
+
+
+def test_accumulate_dw():
+    import torch
+    from vocab_cross_entropy_valid_amd import torch_api
+    announce("accumulate dW")
+    H, W, y = workloads.custom(300, 128, 900, seed=35)
+    Ht, Wt, yt = to_dev(H, W, y, "bf16")
+    base = torch.from_numpy(np.random.default_rng(1).standard_normal((900, 128)).astype(np.float32)).cuda()
+    dW = base.clone()
+    fwd = torch_api.forward(Ht, Wt, yt)
+    torch_api.backward(Ht, Wt, yt, fwd, dW=dW, accumulate_dW=True)
+    torch.cuda.synchronize()
+    _, rdW = oracle.backward(H, W, y, IGN)
+    assert rel_l2(dW.cpu().numpy() - base.cpu().numpy(), rdW) <= 1e-2
+
+
+def test_deterministic_bitwise():
+    announce("determinism")
+    H, W, y = workloads.custom(700, 128, 5000, seed=36)
+    a = run_path(H, W, y, "bf16")
+    b = run_path(H, W, y, "bf16")
+    for k in ("loss", "lse", "dH", "dW"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert a["loss_sum"] == b["loss_sum"]
+
+
+def test_mutated_input_fails_parity():
+    """A comparison that cannot fail tests nothing: change one label on the
+    GPU side only and the per-token check must catch it."""
+    announce("mutation")
+    H, W, y = workloads.custom(300, 128, 1000, seed=37)
+    y2 = y.copy()
+    n = int(np.flatnonzero(y != IGN)[0])
+    y2[n] = (y[n] + 1) % 1000
+    out = run_path(H, W, y2, "bf16")
+    with pytest.raises(AssertionError):
+        _check(out, H, W, y, "bf16")
+
+
+def test_workspace_is_the_only_scratch():
+    """Peak device memory of forward + backward beyond inputs and outputs is
+    exactly the workspace the library asks for (it allocates nothing)."""
+    import torch
+    from vocab_cross_entropy_valid_amd import torch_api
+    announce("workspace accounting")
+    H, W, y = workloads.custom(2000, 256, 9000, seed=38)
+    Ht, Wt, yt = to_dev(H, W, y, "bf16")
+    torch.cuda.synchronize()
+    ws = torch_api.alloc_workspace(2000, 256, 9000, torch.bfloat16, Ht.device)
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    fwd = torch_api.forward(Ht, Wt, yt, workspace=ws)
+    dH, dW = torch_api.backward(Ht, Wt, yt, fwd, workspace=ws)
+    torch.cuda.synchronize()
+    outputs = sum(t.numel() * t.element_size() for t in
+                  (fwd.loss, fwd.lse, fwd.valid_idx, fwd.valid_count, fwd.loss_sum,
+                   fwd.loss_mean, fwd.err_flag, dH, dW))
+    extra = torch.cuda.max_memory_allocated() - before - outputs
+    # only allocator rounding and the 4-byte grad_out scalar remain
+    assert extra <= 64 * 1024, extra

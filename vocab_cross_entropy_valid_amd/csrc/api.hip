@@ -1,0 +1,421 @@
+// C-ABI of liblce: argument checks, workspace plan, launch sequence and the
+// optional event-timing registry.  Every kernel runs on the caller's stream;
+// nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "lce.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lce_status fail(lce_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+lce_status hip_fail(hipError_t e, const char* what) {
+  return fail(LCE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Token chunk C (rows of the compact index) and vocabulary block Vs of the
+// backward pass.  G and G^T hold C * Vs elements each; with C = Vs = 8192 the
+// backward workspace is fixed once N and V exceed the block sizes.
+constexpr int64_t kChunkMax = 8192;
+constexpr int64_t kVocabBlockMax = 8192;
+constexpr int64_t kTargetChunks = 64;  // vocabulary chunks of the forward
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+  int64_t N, d, V;
+  int dtype;
+  size_t esz;
+  // forward
+  int n_vtiles, tpc, J;
+  int64_t Nb;
+  size_t off_pm, off_ps, off_pz, off_lossc, fwd_bytes;
+  // backward
+  int64_t C, Vs;
+  size_t off_G, off_GT, off_HT, off_WT, bwd_bytes;
+  size_t total;
+};
+
+Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype) {
+  Plan p{};
+  p.N = N;
+  p.d = d;
+  p.V = V;
+  p.dtype = dtype;
+  p.esz = dtype == LCE_BF16 ? 2 : 4;
+  p.n_vtiles = (int)((V + 255) / 256);
+  p.tpc = (int)std::max<int64_t>(1, (p.n_vtiles + kTargetChunks - 1) / kTargetChunks);
+  p.J = (p.n_vtiles + p.tpc - 1) / p.tpc;
+  p.Nb = round_up(std::max<int64_t>(N, 1), 256);
+  size_t o = 0;
+  const size_t part = align_up((size_t)p.J * (size_t)p.Nb * sizeof(float));
+  p.off_pm = o; o += part;
+  p.off_ps = o; o += part;
+  p.off_pz = o; o += part;
+  p.off_lossc = o; o += align_up((size_t)p.Nb * sizeof(float));
+  p.fwd_bytes = o;
+  p.C = std::min<int64_t>(kChunkMax, round_up(std::max<int64_t>(N, 1), 256));
+  p.Vs = std::min<int64_t>(kVocabBlockMax, round_up(V, 256));
+  o = 0;
+  p.off_G = o; o += align_up((size_t)p.C * (size_t)p.Vs * p.esz);
+  p.off_GT = o; o += align_up((size_t)p.C * (size_t)p.Vs * p.esz);
+  p.off_HT = o; o += align_up((size_t)d * (size_t)p.C * p.esz);
+  p.off_WT = o; o += align_up((size_t)d * (size_t)p.Vs * p.esz);
+  p.bwd_bytes = o;
+  p.total = std::max(p.fwd_bytes, p.bwd_bytes);
+  return p;
+}
+
+lce_status check_sizes(int64_t N, int64_t d, int64_t V, int dtype) {
+  if (dtype != LCE_F32 && dtype != LCE_BF16)
+    return fail(LCE_ERR_INVALID_ARG, "dtype must be LCE_F32 (0) or LCE_BF16 (1)");
+  if (N < 0) return fail(LCE_ERR_INVALID_ARG, "N must be >= 0");
+  if (d <= 0) return fail(LCE_ERR_INVALID_ARG, "d must be > 0");
+  if (V <= 0) return fail(LCE_ERR_INVALID_ARG, "V must be > 0");
+  const int64_t lim = (int64_t)1 << 31;
+  if (N >= lim || d >= lim || V >= lim)
+    return fail(LCE_ERR_UNSUPPORTED, "N, d and V must be below 2^31");
+  if (d % 64 != 0) return fail(LCE_ERR_UNSUPPORTED, "d must be a multiple of 64");
+  return LCE_OK;
+}
+
+lce_status check_workspace(const Plan& p, const void* ws, size_t bytes) {
+  if (bytes < p.total)
+    return fail(LCE_ERR_WORKSPACE, "workspace of " + std::to_string(bytes) +
+                                       " bytes is smaller than the required " +
+                                       std::to_string(p.total));
+  if (p.total && !ws) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return LCE_OK;
+}
+
+int grid_persistent() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::mutex mu;
+  static std::vector<int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (!cache[dev]) {
+    int cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    cache[dev] = std::max(8, cus / 8 * 8);
+  }
+  return cache[dev];
+}
+
+// ------------------------------------------------------------ timing registry
+struct Timing {
+  std::atomic<bool> on{false};
+  std::mutex mu;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[LCE_K_COUNT];
+  std::vector<hipEvent_t> pool;
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event() {
+  Timing& t = timing();
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.pool.empty()) {
+      hipEvent_t e = t.pool.back();
+      t.pool.pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t run(int kid, hipStream_t s, F&& launch) {
+  Timing& t = timing();
+  if (!t.on.load(std::memory_order_relaxed)) return launch();
+  hipEvent_t a = take_event(), b = take_event();
+  const bool ok_a = a && hipEventRecord(a, s) == hipSuccess;
+  const hipError_t e = launch();
+  const bool ok_b = b && hipEventRecord(b, s) == hipSuccess;
+  if (ok_a && ok_b) {
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.ev[kid].emplace_back(a, b);
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype) {
+  if (check_sizes(N, d, V, dtype) != LCE_OK) return 0;
+  return make_plan(N, d, V, dtype).total;
+}
+
+lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                       int64_t N, int64_t d, int64_t V, int dtype, float* loss, float* lse,
+                       int32_t* valid_idx, int32_t* valid_count, double* loss_sum,
+                       float* loss_mean, int32_t* err_flag, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (!W || !valid_count || !loss_sum || !err_flag)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, loss_sum and err_flag must not be NULL");
+  if (N > 0 && (!H || !labels || !loss || !lse || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, loss, lse and valid_idx must not be NULL");
+  const Plan p = make_plan(N, d, V, dtype);
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != LCE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  hipError_t e = run(LCE_K_COMPACT, s, [&] {
+    return lce::launch_compact(labels, N, ignore_index, V, valid_idx, valid_count, err_flag, loss,
+                               lse, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "compaction launch");
+
+  lce::FwdArgs fa{};
+  fa.H = H;
+  fa.W = W;
+  fa.labels = labels;
+  fa.valid_idx = valid_idx;
+  fa.valid_count = valid_count;
+  fa.d = d;
+  fa.V = V;
+  fa.n_vtiles = p.n_vtiles;
+  fa.tpc = p.tpc;
+  fa.J = p.J;
+  fa.Nb = p.Nb;
+  fa.pm = (float*)(ws + p.off_pm);
+  fa.ps = (float*)(ws + p.off_ps);
+  fa.pz = (float*)(ws + p.off_pz);
+  float* loss_c = (float*)(ws + p.off_lossc);
+  if (N > 0) {
+    e = run(LCE_K_FWD, s, [&] { return lce::launch_fwd(fa, dtype, grid_persistent(), s); });
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    e = run(LCE_K_MERGE, s, [&] { return lce::launch_fwd_merge(fa, loss, lse, loss_c, N, s); });
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  e = run(LCE_K_REDUCE, s,
+          [&] { return lce::launch_loss_reduce(loss_c, valid_count, loss_sum, loss_mean, s); });
+  if (e != hipSuccess) return hip_fail(e, "reduction launch");
+  return LCE_OK;
+}
+
+lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                        const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                        int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
+                        int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (reduction != LCE_MEAN && reduction != LCE_SUM)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
+  if (!W || !valid_count || !grad_out || !dW)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and dW must not be NULL");
+  if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
+  const Plan p = make_plan(N, d, V, dtype);
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != LCE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* G = ws + p.off_G;
+  void* GT = ws + p.off_GT;
+  void* HT = ws + p.off_HT;
+  void* WT = ws + p.off_WT;
+
+  hipError_t e = run(LCE_K_ZERO, s, [&] {
+    return lce::launch_zero_ignored(labels, N, ignore_index, V, dH, d, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "zero-rows launch");
+
+  // At least one chunk, so that dW is written even when N == 0.
+  for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
+    lce::TransposeArgs th{};
+    th.src = H;
+    th.ld_src = d;
+    th.gather = valid_idx;
+    th.row0 = c0;
+    th.count = valid_count;
+    th.dst = HT;
+    th.ncols = p.C;
+    th.K = d;
+    th.active_count = c0 > 0 ? valid_count : nullptr;
+    th.active_c0 = c0;
+    e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(th, dtype, s); });
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
+      lce::TransposeArgs tw{};
+      tw.src = W;
+      tw.ld_src = d;
+      tw.gather = nullptr;
+      tw.row0 = v0;
+      tw.count = nullptr;
+      tw.nrows_static = V;
+      tw.dst = WT;
+      tw.ncols = p.Vs;
+      tw.K = d;
+      tw.active_count = c0 > 0 ? valid_count : nullptr;
+      tw.active_c0 = c0;
+      e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+
+      lce::BwdGArgs ga{};
+      ga.H = H;
+      ga.W = W;
+      ga.labels = labels;
+      ga.lse = lse;
+      ga.valid_idx = valid_idx;
+      ga.valid_count = valid_count;
+      ga.grad_out = grad_out;
+      ga.reduction = reduction;
+      ga.d = d;
+      ga.V = V;
+      ga.c0 = c0;
+      ga.C = p.C;
+      ga.v0 = v0;
+      ga.Vs = p.Vs;
+      ga.G = G;
+      ga.GT = GT;
+      e = run(LCE_K_BWD_G, s, [&] { return lce::launch_bwd_g(ga, dtype, s); });
+      if (e != hipSuccess) return hip_fail(e, "recompute launch");
+
+      lce::DhArgs ha{};
+      ha.G = G;
+      ha.WT = WT;
+      ha.C = p.C;
+      ha.Vs = p.Vs;
+      ha.d = d;
+      ha.valid_idx = valid_idx;
+      ha.valid_count = valid_count;
+      ha.c0 = c0;
+      ha.v0 = v0;
+      ha.V = V;
+      ha.dH = dH;
+      ha.beta = v0 > 0 ? 1 : 0;
+      e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
+      if (e != hipSuccess) return hip_fail(e, "dH launch");
+
+      lce::DwArgs wa{};
+      wa.GT = GT;
+      wa.HT = HT;
+      wa.C = p.C;
+      wa.Vs = p.Vs;
+      wa.d = d;
+      wa.valid_count = valid_count;
+      wa.c0 = c0;
+      wa.v0 = v0;
+      wa.V = V;
+      wa.dW = dW;
+      wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
+      e = run(LCE_K_DW, s, [&] { return lce::launch_dw(wa, dtype, s); });
+      if (e != hipSuccess) return hip_fail(e, "dW launch");
+    }
+  }
+  return LCE_OK;
+}
+
+lce_status lce_check_error(const int32_t* err_flag, void* stream) {
+  g_err.clear();
+  if (!err_flag) return fail(LCE_ERR_INVALID_ARG, "err_flag is NULL");
+  int32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, err_flag, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reading err_flag");
+  if (h) return fail(LCE_ERR_LABEL_RANGE, "a label that is not ignore_index lies outside [0, V)");
+  return LCE_OK;
+}
+
+const char* lce_status_string(lce_status s) {
+  switch (s) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_INVALID_ARG: return "invalid argument";
+    case LCE_ERR_UNSUPPORTED: return "unsupported shape";
+    case LCE_ERR_WORKSPACE: return "workspace too small";
+    case LCE_ERR_LABEL_RANGE: return "label outside [0, V)";
+    case LCE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* lce_last_error(void) { return g_err.c_str(); }
+
+lce_status lce_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                       int dtype, void* stream) {
+  g_err.clear();
+  if (dtype != LCE_F32 && dtype != LCE_BF16) return fail(LCE_ERR_INVALID_ARG, "bad dtype");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(LCE_ERR_INVALID_ARG, "M, N, K must be > 0");
+  if (K % 64 != 0) return fail(LCE_ERR_UNSUPPORTED, "K must be a multiple of 64");
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "M and N must be below 2^31");
+  if (!A || !B || !C) return fail(LCE_ERR_INVALID_ARG, "NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = run(LCE_K_GEMM, s, [&] { return lce::launch_gemm_nt(A, B, C, M, N, K, dtype, s); });
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return LCE_OK;
+}
+
+lce_status lce_timing_enable(int on) {
+  timing().on.store(on != 0);
+  return LCE_OK;
+}
+
+lce_status lce_timing_reset(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& v : t.ev) {
+    for (auto& pr : v) {
+      t.pool.push_back(pr.first);
+      t.pool.push_back(pr.second);
+    }
+    v.clear();
+  }
+  return LCE_OK;
+}
+
+lce_status lce_timing_query(int kernel_class, double* total_ms, int64_t* launches) {
+  g_err.clear();
+  if (kernel_class < 0 || kernel_class >= LCE_K_COUNT || !total_ms || !launches)
+    return fail(LCE_ERR_INVALID_ARG, "bad kernel class or NULL output");
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double sum = 0.0;
+  for (auto& pr : t.ev[kernel_class]) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return hip_fail(e, "event synchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_fail(e, "event elapsed time");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)t.ev[kernel_class].size();
+  return LCE_OK;
+}
+
+}  // extern "C"

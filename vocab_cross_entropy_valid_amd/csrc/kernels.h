@@ -1,0 +1,93 @@
+// Host-side launchers of the HIP kernels (internal to liblce).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+struct FwdArgs {
+  const void* H;
+  const void* W;
+  const int64_t* labels;
+  const int32_t* valid_idx;
+  const int32_t* valid_count;
+  int64_t d, V;
+  int n_vtiles;  // ceil(V / 256)
+  int tpc;       // vocabulary tiles per chunk
+  int J;         // chunks: ceil(n_vtiles / tpc)
+  int64_t Nb;    // row stride of the partial arrays (multiple of 256, >= N)
+  float* pm;     // [J][Nb] running max, log2 units
+  float* ps;     // [J][Nb] running sum of 2^(u - m)
+  float* pz;     // [J][Nb] target logit if it lies in the chunk, else -inf
+};
+
+struct BwdGArgs {
+  const void* H;
+  const void* W;
+  const int64_t* labels;
+  const float* lse;
+  const int32_t* valid_idx;
+  const int32_t* valid_count;
+  const float* grad_out;
+  int reduction;  // 0 mean, 1 sum
+  int64_t d, V;
+  int64_t c0, C;   // token chunk of the compact index
+  int64_t v0, Vs;  // vocabulary block
+  void* G;         // [C][Vs]
+  void* GT;        // [Vs][C]
+};
+
+struct DhArgs {
+  const void* G;   // [C][Vs]
+  const void* WT;  // [d][Vs]
+  int64_t C, Vs, d;
+  const int32_t* valid_idx;
+  const int32_t* valid_count;
+  int64_t c0, v0, V;
+  float* dH;
+  int beta;
+};
+
+struct DwArgs {
+  const void* GT;  // [Vs][C]
+  const void* HT;  // [d][C]
+  int64_t C, Vs, d;
+  const int32_t* valid_count;
+  int64_t c0, v0, V;
+  float* dW;
+  int accumulate;
+};
+
+struct TransposeArgs {
+  const void* src;
+  int64_t ld_src;          // elements
+  const int32_t* gather;   // nullable: physical row = gather[row0 + i]
+  int64_t row0;
+  const int32_t* count;    // nullable: rows available = *count - row0 (clamped)
+  int64_t nrows_static;    // used when count is null: rows available = nrows_static - row0
+  void* dst;               // [K][ncols]
+  int64_t ncols;           // columns of dst (multiple of 64)
+  int64_t K;               // rows of dst = columns read from src (multiple of 64)
+  const int32_t* active_count;  // nullable: skip the whole launch when *active_count <= active_c0
+  int64_t active_c0;
+};
+
+hipError_t launch_compact(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
+                          int32_t* valid_idx, int32_t* valid_count, int32_t* err_flag, float* loss,
+                          float* lse, hipStream_t s);
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int grid, hipStream_t s);
+hipError_t launch_fwd_merge(const FwdArgs& a, float* loss, float* lse, float* loss_c,
+                            int64_t N, hipStream_t s);
+hipError_t launch_loss_reduce(const float* loss_c, const int32_t* valid_count, double* loss_sum,
+                              float* loss_mean, hipStream_t s);
+hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
+                               float* dH, int64_t d, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s);
+hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
+hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s);
+hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                          int dtype, hipStream_t s);
+
+}  // namespace lce

@@ -1,0 +1,425 @@
+// Backward kernels: recompute each logit tile and form
+// G = (softmax - onehot) * w in registers, then the two contractions
+// dH += G W and dW += G^T H over a bounded [C x Vs] block of G, plus the
+// helpers that lay operands out K-contiguous for the tile engine.
+//
+// Recomputing the logits chunk by chunk in the backward pass instead of
+// saving them is what "6GB显卡预训练11亿参数模型" describes for its chunked loss
+// (sections 内存实际花在哪里 and 关键参数说明: --chunked-loss 512 recomputes the
+// logits in backward).  Here the chunk is a C-row slice of the compact token
+// index times a Vs-entry slice of the vocabulary, so the workspace is
+// O((C + d) * (Vs + C)) and independent of N and V.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lce {
+
+// ------------------------------------------------ zero rows of ignored tokens
+//
+// Padding / ignored tokens take no part in the loss (OjasX page, core
+// technology: padding tokens are skipped), so their dH rows are exactly 0.
+__global__ __launch_bounds__(256) void zero_ignored_kernel(const int64_t* __restrict__ labels,
+                                                           int64_t ignore_index, int64_t V,
+                                                           float* __restrict__ dH, int64_t d) {
+  const int64_t row = blockIdx.x;
+  const int64_t y = labels[row];
+  if (y != ignore_index && y >= 0 && y < V) return;
+  f32x4* p = (f32x4*)(dH + row * d);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k = threadIdx.x; k < d / 4; k += 256) p[k] = z;
+}
+
+hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
+                               float* dH, int64_t d, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ignored_kernel, dim3((unsigned)N), dim3(256), 0, s, labels, ignore_index,
+                     V, dH, d);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- transpose
+//
+// dst[k][i] = src[row(row0 + i)][k] for i < rows available, 0 for the rest of
+// the ncols columns.  64 x 64 element tiles through LDS; HBM-bound.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+  __shared__ T tile[64][65];
+  const int tid = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int64_t k0 = (int64_t)blockIdx.y * 64;
+  if (a.active_count && (int64_t)(*a.active_count) <= a.active_c0) return;
+  int64_t avail = a.count ? (int64_t)(*a.count) - a.row0 : a.nrows_static - a.row0;
+  if (avail < 0) avail = 0;
+  if (avail > a.ncols) avail = a.ncols;
+  // read: thread -> (row ii, 16 consecutive k)
+  {
+    const int ii = tid >> 2;
+    const int kk = (tid & 3) * 16;
+    const int64_t i = i0 + ii;
+    if (i < avail) {
+      const int64_t r = a.row0 + i;
+      const int64_t phys = a.gather ? (int64_t)a.gather[r] : r;
+      const T* src = (const T*)a.src + phys * a.ld_src + k0 + kk;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tile[ii][kk + e] = src[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tile[ii][kk + e] = (T)0;
+    }
+  }
+  __syncthreads();
+  // write: thread -> (dst row k, 16 consecutive i)
+  {
+    const int kk = tid >> 2;
+    const int ii = (tid & 3) * 16;
+    T* dst = (T*)a.dst + (k0 + kk) * a.ncols + i0 + ii;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dst[e] = tile[ii + e][kk];
+  }
+}
+
+hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
+  const dim3 grid((unsigned)(a.ncols / 64), (unsigned)(a.K / 64));
+  if (dtype == 1)
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------- recompute + G tile
+//
+// Same MFMA tile as the forward (A = W rows, B = gathered H rows, so each lane
+// holds 4 consecutive tokens).  Epilogue: p = exp(z - lse), subtract 1 at the
+// label, scale by w = grad / N_valid (mean) or grad (sum); entries past V or
+// past the valid tokens are 0.  G is written row-major [token][vocab] for the
+// dH contraction and transposed [vocab][token] for the dW contraction; both
+// stores are 4-element vectors.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 1;
+  const int wb = wave >> 1;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+
+  const int TM = (int)(a.Vs / kTile);
+  const int TN = (int)(a.C / kTile);
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, TM, TN, 8, 4, tm, tn)) return;
+  const int count = *a.valid_count;
+  const int64_t n_act = (int64_t)count - a.c0;
+  if ((int64_t)tn * kTile >= n_act) return;
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  if ((int64_t)tm * kTile >= nv) return;
+
+  const int64_t ld = a.d * Elem<T>::kSize;
+  RowSource as{(const char*)a.W, ld, nullptr, a.v0 + (int64_t)tm * kTile, a.V};
+  RowSource bs{(const char*)a.H, ld, a.valid_idx, a.c0 + (int64_t)tn * kTile, count};
+  const RowPtrs pa = make_row_ptrs<false>(as, tid);
+  const RowPtrs pb = make_row_ptrs<true>(bs, tid);
+
+  // per-token data (4 consecutive tokens per lane)
+  float lse_t[4], w_t[4];
+  int y[4];
+  const float g = *a.grad_out;
+  const float w = a.reduction == 0 ? g / (float)count : g;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t i = a.c0 + (int64_t)tn * kTile + wb * kHalf + 4 * j + nt;
+    if (i < count) {
+      const int r = a.valid_idx[i];
+      y[nt] = (int)a.labels[r];
+      lse_t[nt] = a.lse[r];
+      w_t[nt] = w;
+    } else {
+      y[nt] = -1;
+      lse_t[nt] = 0.f;
+      w_t[nt] = 0.f;
+    }
+  }
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T>(acc, lds, pa, pb, (int)(a.d / Elem<T>::kPerStage), tid);
+
+  const int64_t vl0 = (int64_t)tm * kTile + wa * kHalf;  // first local vocab entry of this wave
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+      const int64_t v = a.v0 + vl;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float p = fast_exp2((acc[mt][nt][i] - lse_t[nt]) * kLog2e);
+        float gv = (p - (v == (int64_t)y[nt] ? 1.f : 0.f)) * w_t[nt];
+        if (vl >= nv) gv = 0.f;
+        acc[mt][nt][i] = gv;
+      }
+    }
+
+  // G[token][vocab]: 4 consecutive vocabulary entries per store
+  const int64_t il0 = (int64_t)tn * kTile + wb * kHalf + 4 * j;  // local token of nt = 0
+  char* G = (char*)a.G;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t vl = vl0 + 32 * mt + 8 * g4 + 4 * h;
+        Store4<T>::run(G + ((il0 + nt) * a.Vs + vl) * Elem<T>::kSize, acc[mt][nt][4 * g4],
+                       acc[mt][nt][4 * g4 + 1], acc[mt][nt][4 * g4 + 2], acc[mt][nt][4 * g4 + 3]);
+      }
+  // G^T[vocab][token]: the lane's 4 consecutive tokens per store
+  char* GT = (char*)a.GT;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+      Store4<T>::run(GT + (vl * a.C + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i],
+                     acc[mt][2][i], acc[mt][3][i]);
+    }
+}
+
+hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s) {
+  const int TM = (int)(a.Vs / kTile), TN = (int)(a.C / kTile);
+  const int nsb = ((TM + 7) / 8) * ((TN + 3) / 4);
+  const int grid = 256 * ((nsb + 7) / 8);
+  if (dtype == 1)
+    hipLaunchKernelGGL(bwd_g_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_g_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- dH += G W
+//
+// C tile rows = tokens of the chunk (A = G rows), columns = hidden units
+// (B = W^T rows); K runs over the vocabulary block.  Rows are scattered to the
+// tokens' original positions through valid_idx.  beta = 0 on the first
+// vocabulary block, 1 afterwards.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  __shared__ int rows[kTile];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 1;
+  const int wb = wave >> 1;
+  const int h = lane >> 5;
+
+  const int TM = (int)(a.C / kTile);
+  const int TN = (int)((a.d + kTile - 1) / kTile);
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
+  const int count = *a.valid_count;
+  int64_t n_act = (int64_t)count - a.c0;
+  if (n_act > a.C) n_act = a.C;
+  if ((int64_t)tm * kTile >= n_act) return;
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
+
+  {
+    const int64_t m = (int64_t)tm * kTile + tid;
+    rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
+  }
+  __syncthreads();
+  const int64_t ld = a.Vs * Elem<T>::kSize;
+  RowSource as{(const char*)a.G, ld, nullptr, (int64_t)tm * kTile, a.C};
+  RowSource bs{(const char*)a.WT, ld, nullptr, (int64_t)tn * kTile, a.d};
+  const RowPtrs pa = make_row_ptrs<false>(as, tid);
+  const RowPtrs pb = make_row_ptrs<false>(bs, tid);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: rows[] visible
+
+  const int n_base = tn * kTile + wb * kHalf + (lane & 31);
+  if (a.beta) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
+        if (r < 0) continue;
+        float* out = a.dH + (int64_t)r * a.d;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = n_base + 32 * nt;
+          if (n < a.d) out[n] += acc[mt][nt][i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
+        if (r < 0) continue;
+        float* out = a.dH + (int64_t)r * a.d;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = n_base + 32 * nt;
+          if (n < a.d) out[n] = acc[mt][nt][i];
+        }
+      }
+  }
+}
+
+hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
+  const int TM = (int)(a.C / kTile), TN = (int)((a.d + kTile - 1) / kTile);
+  const int nsb = ((TM + 3) / 4) * ((TN + 7) / 8);
+  const int grid = 256 * ((nsb + 7) / 8);
+  if (dtype == 1)
+    hipLaunchKernelGGL(dh_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- dW += G^T H
+//
+// C tile rows = vocabulary entries of the block (A = G^T rows), columns =
+// hidden units (B = H^T rows); K runs over the chunk's valid tokens only
+// (the count is read on the device).  Each workgroup owns its dW tile, so
+// no atomics are needed and the result is deterministic.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 1;
+  const int wb = wave >> 1;
+  const int h = lane >> 5;
+
+  const int TM = (int)(a.Vs / kTile);
+  const int TN = (int)((a.d + kTile - 1) / kTile);
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  if ((int64_t)tm * kTile >= nv) return;
+  const int count = *a.valid_count;
+  int64_t kact = (int64_t)count - a.c0;
+  if (kact < 0) kact = 0;
+  if (kact > a.C) kact = a.C;
+  const int nstages = (int)((kact + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
+  if (nstages == 0 && a.accumulate) return;
+
+  const int64_t ld = a.C * Elem<T>::kSize;
+  RowSource as{(const char*)a.GT, ld, nullptr, (int64_t)tm * kTile, a.Vs};
+  RowSource bs{(const char*)a.HT, ld, nullptr, (int64_t)tn * kTile, a.d};
+  const RowPtrs pa = make_row_ptrs<false>(as, tid);
+  const RowPtrs pb = make_row_ptrs<false>(bs, tid);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
+
+  const int n_base = tn * kTile + wb * kHalf + (lane & 31);
+  const int m_base = tm * kTile + wa * kHalf + 4 * h;
+  float* out0 = a.dW + a.v0 * a.d;
+  if (a.accumulate) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+        if (ml >= nv) continue;
+        float* out = out0 + (int64_t)ml * a.d;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = n_base + 32 * nt;
+          if (n < a.d) out[n] += acc[mt][nt][i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+        if (ml >= nv) continue;
+        float* out = out0 + (int64_t)ml * a.d;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = n_base + 32 * nt;
+          if (n < a.d) out[n] = acc[mt][nt][i];
+        }
+      }
+  }
+}
+
+hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s) {
+  const int TM = (int)(a.Vs / kTile), TN = (int)((a.d + kTile - 1) / kTile);
+  const int nsb = ((TM + 3) / 4) * ((TN + 7) / 8);
+  const int grid = 256 * ((nsb + 7) / 8);
+  if (dtype == 1)
+    hipLaunchKernelGGL(dw_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dw_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- plain NT GEMM
+//
+// C[M][N] = A[M][K] B[N][K]^T in fp32: the same tile engine with a plain
+// store, used to measure what this MFMA engine reaches on a bare GEMM of the
+// path's shapes and to check the engine's layout in isolation.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(const void* A, const void* B, float* C,
+                                                              int64_t M, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 1;
+  const int wb = wave >> 1;
+  const int h = lane >> 5;
+  const int TM = (int)((M + kTile - 1) / kTile);
+  const int TN = (int)((N + kTile - 1) / kTile);
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
+  const int64_t ld = K * Elem<T>::kSize;
+  RowSource as{(const char*)A, ld, nullptr, (int64_t)tm * kTile, M};
+  RowSource bs{(const char*)B, ld, nullptr, (int64_t)tn * kTile, N};
+  const RowPtrs pa = make_row_ptrs<false>(as, tid);
+  const RowPtrs pb = make_row_ptrs<false>(bs, tid);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T>(acc, lds, pa, pb, (int)(K / Elem<T>::kPerStage), tid);
+  const int64_t n_base = (int64_t)tn * kTile + wb * kHalf + (lane & 31);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = (int64_t)tm * kTile + wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int64_t n = n_base + 32 * nt;
+        if (n < N) C[m * N + n] = acc[mt][nt][i];
+      }
+    }
+}
+
+hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                          int dtype, hipStream_t s) {
+  const int TM = (int)((M + kTile - 1) / kTile), TN = (int)((N + kTile - 1) / kTile);
+  const int nsb = ((TM + 3) / 4) * ((TN + 7) / 8);
+  const int grid = 256 * ((nsb + 7) / 8);
+  if (dtype == 1)
+    hipLaunchKernelGGL(gemm_nt_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, A, B, C, M, N, K);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<float>, dim3(grid), dim3(kThreads), 0, s, A, B, C, M, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace lce

@@ -1,0 +1,314 @@
+// Forward kernels: valid-token compaction, fused projection + online
+// logsumexp over vocabulary tiles, merge of vocabulary chunks, and the
+// deterministic loss reduction.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lce {
+
+// ------------------------------------------------------------ compaction
+//
+// Builds the ascending index of rows whose label is kept (label !=
+// ignore_index) in one workgroup, with no host round trip: the MaximusLLM
+// page (section 2.3, padding-aware sparse index engine) builds its valid mask
+// and uses it inside the same kernel to avoid a host-device sync; the OjasX
+// page (core technology) packs per-lane predicates into hardware ballot masks.
+// Here each wave64 takes a 64-bit ballot of the predicate, a lane's slot is
+// the popcount of the ballot bits below it (mbcnt), and the 16 wave totals
+// are scanned in LDS.  A kept label outside [0, V) raises err_flag and the
+// row is treated as ignored, so no later kernel indexes W with it.
+// Ignored rows get loss = lse = 0 here.
+__global__ __launch_bounds__(1024) void compact_kernel(const int64_t* __restrict__ labels, int64_t N,
+                                                       int64_t ignore_index, int64_t V,
+                                                       int32_t* __restrict__ valid_idx,
+                                                       int32_t* __restrict__ valid_count,
+                                                       int32_t* __restrict__ err_flag,
+                                                       float* __restrict__ loss,
+                                                       float* __restrict__ lse) {
+  __shared__ int wave_tot[16];
+  __shared__ int wave_base[17];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  int base = 0;
+  int err = 0;
+  for (int64_t n0 = 0; n0 < N; n0 += 1024) {
+    const int64_t n = n0 + tid;
+    const bool in = n < N;
+    const int64_t y = in ? labels[n] : ignore_index;
+    const bool keep = in && (y != ignore_index);
+    const bool in_range = (y >= 0) && (y < V);
+    err |= (keep && !in_range) ? 1 : 0;
+    const bool valid = keep && in_range;
+    if (in && !valid) {
+      loss[n] = 0.f;
+      lse[n] = 0.f;
+    }
+    const uint64_t m = __ballot(valid);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (lane == 0) wave_tot[wv] = __popcll(m);
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int w = 0; w < 16; ++w) {
+        wave_base[w] = acc;
+        acc += wave_tot[w];
+      }
+      wave_base[16] = acc;
+    }
+    __syncthreads();
+    if (valid) valid_idx[base + wave_base[wv] + rank] = (int32_t)n;
+    base += wave_base[16];
+    __syncthreads();
+  }
+  const int any_err = __syncthreads_or(err);
+  if (tid == 0) {
+    *valid_count = base;
+    *err_flag = any_err ? 1 : 0;
+  }
+}
+
+hipError_t launch_compact(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
+                          int32_t* valid_idx, int32_t* valid_count, int32_t* err_flag, float* loss,
+                          float* lse, hipStream_t s) {
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, labels, N, ignore_index, V,
+                     valid_idx, valid_count, err_flag, loss, lse);
+  return hipGetLastError();
+}
+
+// -------------------------------------------- fused projection + logsumexp
+//
+// The output projection and the loss are computed tile by tile and never
+// stored as a [N, V] table (OjasX page, core technology: zero-byte
+// vocabulary logits table).  Per token the running (max, sum of
+// exponentials) pair is updated tile after tile, which is the online
+// softmax recurrence of the same page: after each tile the stored maximum is
+// corrected and the sum rescaled, which gives exactly the full logsumexp.
+//
+// Work decomposition: vocabulary tiles of 256 entries are grouped into J
+// chunks of tpc tiles; an item is (token tile of 256 compact rows, chunk).
+// The kernel is persistent: each workgroup walks items in rounds.  Within a
+// round the 32 workgroups on one XCD take a 4 x 8 block of (token tile,
+// chunk) items, so that four H tiles and eight W streams are shared through
+// that XCD's L2.  A item leaves per-token partials (m, s, z_target) for its
+// chunk; fwd_merge_kernel combines the J chunks.
+//
+// MFMA operand order: A = W rows (vocabulary), B = H rows (tokens, gathered
+// through valid_idx).  Each lane then holds 4 consecutive tokens x 64
+// vocabulary entries per tile, so the max / sum reductions run inside the
+// lane, and only once per item across the lane pair (l, l ^ 32) and across
+// the two waves that split the tile's vocabulary.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 2 * kHalf * 3 * sizeof(float)];
+  float* mg = (float*)(lds + kMainLds);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 1;
+  const int wb = wave >> 1;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+
+  const int count = *a.valid_count;
+  const int R = (count + kTile - 1) / kTile;
+  if (R == 0) return;
+  const int GA = 4, GB = 8;
+  const int nsb = ((R + GA - 1) / GA) * ((a.J + GB - 1) / GB);
+  const int nstages = (int)(a.d / Elem<T>::kPerStage);
+  const int64_t ldb = a.d * Elem<T>::kSize;
+
+  for (int64_t ls = blockIdx.x;; ls += gridDim.x) {
+    const int k = (int)(ls >> 3);
+    const int sb = ((k >> 5) << 3) + (int)(ls & 7);
+    if (sb >= nsb) break;
+    int tt, ch;
+    if (!xcd_tile((int)ls, R, a.J, GA, GB, tt, ch)) continue;
+
+    RowSource bs{(const char*)a.H, ldb, a.valid_idx, (int64_t)tt * kTile, count};
+    const RowPtrs pb = make_row_ptrs<true>(bs, tid);
+
+    int y[4];
+    float m[4], s[4], zy[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int i = tt * kTile + wb * kHalf + 4 * j + nt;
+      y[nt] = (i < count) ? (int)a.labels[a.valid_idx[i]] : -1;
+      m[nt] = -INFINITY;
+      s[nt] = 0.f;
+      zy[nt] = -INFINITY;
+    }
+
+    const int vt0 = ch * a.tpc;
+    const int vt1 = min(vt0 + a.tpc, a.n_vtiles);
+    for (int vt = vt0; vt < vt1; ++vt) {
+      RowSource as{(const char*)a.W, ldb, nullptr, (int64_t)vt * kVocabTile, a.V};
+      const RowPtrs pa = make_row_ptrs<false>(as, tid);
+      f32x16 acc[4][4];
+      zero_acc(acc);
+      tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
+
+      const int vw0 = vt * kVocabTile + wa * kHalf;  // first vocabulary entry of this wave
+      // entries of this lane at or beyond V (only in the last tile): vr >= vlim
+      const int vlim = (int)min<int64_t>(a.V - vw0, (int64_t)kHalf);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float z[64];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int vr = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+            // entries at or beyond V (last tile only) drop out as -inf
+            z[16 * mt + i] = vr < vlim ? acc[mt][nt][i] : -INFINITY;
+          }
+        // target logit, taken from the same fp32 accumulator as the sum
+        const int rel = y[nt] - vw0;
+        if ((unsigned)rel < (unsigned)kHalf) {
+#pragma unroll
+          for (int q = 0; q < 64; ++q) {
+            const int vr = 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * h + (q & 3);
+            if (vr == rel) zy[nt] = z[q];
+          }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 64; ++q) tmax = fmaxf(tmax, z[q]);
+        if (tmax != -INFINITY) {  // else every entry of this lane is past V
+          tmax *= kLog2e;
+          if (tmax > m[nt]) {
+            s[nt] *= fast_exp2(m[nt] - tmax);
+            m[nt] = tmax;
+          }
+          const float mn = m[nt];
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < 64; ++q) sum += fast_exp2(fmaf(z[q], kLog2e, -mn));
+          s[nt] += sum;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // merge the lane pair (l, l ^ 32): same tokens, other vocabulary rows
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const float mo = __shfl_xor(m[nt], 32);
+      const float so = __shfl_xor(s[nt], 32);
+      const float zo = __shfl_xor(zy[nt], 32);
+      const float M = fmaxf(m[nt], mo);
+      s[nt] = (M == -INFINITY) ? 0.f : s[nt] * fast_exp2(m[nt] - M) + so * fast_exp2(mo - M);
+      m[nt] = M;
+      zy[nt] = fmaxf(zy[nt], zo);
+    }
+    // merge the two waves (wa = 0, 1) that split the tile's vocabulary
+    if (wa == 1 && h == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float* q = mg + (wb * kHalf + 4 * j + nt) * 3;
+        q[0] = m[nt];
+        q[1] = s[nt];
+        q[2] = zy[nt];
+      }
+    }
+    __syncthreads();
+    if (wa == 0 && h == 0) {
+      f32x4 om, os, oz;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float* q = mg + (wb * kHalf + 4 * j + nt) * 3;
+        const float M = fmaxf(m[nt], q[0]);
+        om[nt] = M;
+        os[nt] = (M == -INFINITY) ? 0.f : s[nt] * fast_exp2(m[nt] - M) + q[1] * fast_exp2(q[0] - M);
+        oz[nt] = fmaxf(zy[nt], q[2]);
+      }
+      const int64_t off = (int64_t)ch * a.Nb + (int64_t)tt * kTile + wb * kHalf + 4 * j;
+      *(f32x4*)(a.pm + off) = om;
+      *(f32x4*)(a.ps + off) = os;
+      *(f32x4*)(a.pz + off) = oz;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int grid, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(fwd_lse_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(fwd_lse_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- merge
+//
+// Combines the J chunk partials of each compact row with the same
+// max-and-rescale step, then lse = (M + log2 S) ln 2 and
+// loss = lse - z_target, written at the row's original position.
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __restrict__ loss,
+                                                        float* __restrict__ lse,
+                                                        float* __restrict__ loss_c) {
+  const int count = *a.valid_count;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float M = -INFINITY;
+  for (int c = 0; c < a.J; ++c) M = fmaxf(M, a.pm[(int64_t)c * a.Nb + i]);
+  float S = 0.f;
+  for (int c = 0; c < a.J; ++c) {
+    const int64_t o = (int64_t)c * a.Nb + i;
+    S += a.ps[o] * fast_exp2(a.pm[o] - M);
+  }
+  const int r = a.valid_idx[i];
+  const int64_t yv = a.labels[r];
+  const int cy = (int)(yv / kVocabTile) / a.tpc;
+  const float zt = a.pz[(int64_t)cy * a.Nb + i];
+  const float l = (M + fast_log2(S)) * kLn2;
+  const float lv = l - zt;
+  lse[r] = l;
+  loss[r] = lv;
+  loss_c[i] = lv;
+}
+
+hipError_t launch_fwd_merge(const FwdArgs& a, float* loss, float* lse, float* loss_c, int64_t N,
+                            hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int grid = (int)((N + 255) / 256);
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3(grid), dim3(256), 0, s, a, loss, lse, loss_c);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- loss reduction
+//
+// Sum of per-token losses over valid rows in a fixed order (strided fp64
+// per-thread sums, then a fixed binary tree in LDS), so the result is
+// bitwise reproducible.  Writes the sum and the mean over valid rows (NaN
+// when no row is valid, as PyTorch's mean cross-entropy does).
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ loss_c,
+                                                           const int32_t* __restrict__ valid_count,
+                                                           double* __restrict__ loss_sum,
+                                                           float* __restrict__ loss_mean) {
+  __shared__ double part[1024];
+  const int tid = threadIdx.x;
+  const int count = *valid_count;
+  double acc = 0.0;
+  for (int i = tid; i < count; i += 1024) acc += (double)loss_c[i];
+  part[tid] = acc;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    *loss_sum = part[0];
+    if (loss_mean) *loss_mean = count > 0 ? (float)(part[0] / (double)count) : __builtin_nanf("");
+  }
+}
+
+hipError_t launch_loss_reduce(const float* loss_c, const int32_t* valid_count, double* loss_sum,
+                              float* loss_mean, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, loss_c, valid_count, loss_sum,
+                     loss_mean);
+  return hipGetLastError();
+}
+
+}  // namespace lce

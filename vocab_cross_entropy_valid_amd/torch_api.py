@@ -1,0 +1,175 @@
+"""PyTorch-facing wrapper over the C ABI.
+
+PyTorch supplies device memory and the current stream; every step of the
+computation runs in liblce's HIP kernels.  ``linear_cross_entropy`` has the
+semantics of ``F.cross_entropy(H @ W.T, labels, ignore_index=..., reduction=...)``
+without materialising ``H @ W.T``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.LCE_BF16, torch.float32: _lib.LCE_F32}
+_RED = {"mean": _lib.LCE_MEAN, "sum": _lib.LCE_SUM}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_inputs(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor):
+    if H.dim() != 2 or W.dim() != 2 or labels.dim() != 1:
+        raise ValueError("H must be [N, d], W [V, d] and labels [N]")
+    if H.shape[1] != W.shape[1] or H.shape[0] != labels.shape[0]:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)}, W {tuple(W.shape)}, "
+                         f"labels {tuple(labels.shape)}")
+    if H.dtype != W.dtype or H.dtype not in _DTYPES:
+        raise ValueError("H and W must both be bfloat16 or both float32")
+    if labels.dtype != torch.int64:
+        raise ValueError("labels must be int64")
+    for t in (H, W, labels):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if not (H.device == W.device == labels.device):
+        raise ValueError("all tensors must be on the same device")
+
+
+def workspace_bytes(N: int, d: int, V: int, dtype: torch.dtype) -> int:
+    return _lib.lce_workspace_bytes(N, d, V, _DTYPES[dtype])
+
+
+def alloc_workspace(N: int, d: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
+    n = workspace_bytes(N, d, V, dtype)
+    if n == 0:
+        raise ValueError(f"unsupported sizes N={N} d={d} V={V}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+@dataclasses.dataclass
+class ForwardOut:
+    loss: torch.Tensor         # f32 [N], 0 on ignored rows
+    lse: torch.Tensor          # f32 [N], 0 on ignored rows
+    valid_idx: torch.Tensor    # int32 [N]; first valid_count entries meaningful
+    valid_count: torch.Tensor  # int32 [1]
+    loss_sum: torch.Tensor     # f64 [1]
+    loss_mean: torch.Tensor    # f32 [1]
+    err_flag: torch.Tensor     # int32 [1]
+
+
+def forward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+            workspace: Optional[torch.Tensor] = None, check: bool = True) -> ForwardOut:
+    """lce_forward on the current stream.  With check=True the error flag is
+    read back (one synchronisation) and a bad label raises ValueError."""
+    _check_inputs(H, W, labels)
+    N, d = H.shape
+    V = W.shape[0]
+    dev = H.device
+    dt = _DTYPES[H.dtype]
+    if workspace is None:
+        workspace = alloc_workspace(N, d, V, H.dtype, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = ForwardOut(
+        loss=torch.empty(N, **f32), lse=torch.empty(N, **f32),
+        valid_idx=torch.empty(N, dtype=torch.int32, device=dev),
+        valid_count=torch.empty(1, dtype=torch.int32, device=dev),
+        loss_sum=torch.empty(1, dtype=torch.float64, device=dev),
+        loss_mean=torch.empty(1, **f32),
+        err_flag=torch.empty(1, dtype=torch.int32, device=dev))
+    s = _stream(dev)
+    _lib.lce_forward(_ptr(H), _ptr(W), _ptr(labels), int(ignore_index), N, d, V, dt,
+                     _ptr(out.loss), _ptr(out.lse), _ptr(out.valid_idx), _ptr(out.valid_count),
+                     _ptr(out.loss_sum), _ptr(out.loss_mean), _ptr(out.err_flag),
+                     _ptr(workspace), workspace.numel(), s)
+    if check:
+        try:
+            _lib.lce_check_error(_ptr(out.err_flag), s)
+        except _lib.LceError as e:
+            if e.status == _lib.LCE_ERR_LABEL_RANGE:
+                raise ValueError(str(e)) from e
+            raise
+    return out
+
+
+def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, fwd: ForwardOut,
+             grad_out: Optional[torch.Tensor] = None, reduction: str = "mean",
+             ignore_index: int = -100, dH: Optional[torch.Tensor] = None,
+             dW: Optional[torch.Tensor] = None, accumulate_dW: bool = False,
+             workspace: Optional[torch.Tensor] = None):
+    """lce_backward on the current stream; returns (dH, dW) in float32."""
+    _check_inputs(H, W, labels)
+    N, d = H.shape
+    V = W.shape[0]
+    dev = H.device
+    if reduction not in _RED:
+        raise ValueError("reduction must be 'mean' or 'sum'")
+    if grad_out is None:
+        grad_out = torch.ones(1, dtype=torch.float32, device=dev)
+    grad_out = grad_out.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    if workspace is None:
+        workspace = alloc_workspace(N, d, V, H.dtype, dev)
+    if dH is None:
+        dH = torch.empty(N, d, dtype=torch.float32, device=dev)
+    if dW is None:
+        if accumulate_dW:
+            raise ValueError("accumulate_dW needs dW")
+        dW = torch.empty(V, d, dtype=torch.float32, device=dev)
+    for t, shp in ((dH, (N, d)), (dW, (V, d))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError("dH and dW must be contiguous float32 of shapes [N, d] and [V, d]")
+    _lib.lce_backward(_ptr(H), _ptr(W), _ptr(labels), int(ignore_index), _ptr(fwd.lse),
+                      _ptr(fwd.valid_idx), _ptr(fwd.valid_count), N, d, V, _DTYPES[H.dtype],
+                      _ptr(grad_out), _RED[reduction], _ptr(dH), _ptr(dW),
+                      1 if accumulate_dW else 0, _ptr(workspace), workspace.numel(),
+                      _stream(dev))
+    return dH, dW
+
+
+class _LinearCrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, W, labels, ignore_index, reduction, check):
+        fwd = forward(H, W, labels, ignore_index, check=check)
+        ctx.save_for_backward(H, W, labels, fwd.lse, fwd.valid_idx, fwd.valid_count)
+        ctx.ignore_index = ignore_index
+        ctx.reduction = reduction
+        ctx.mark_non_differentiable(fwd.loss, fwd.lse, fwd.valid_count)
+        out = fwd.loss_mean if reduction == "mean" else fwd.loss_sum.to(torch.float32)
+        return out.reshape(()), fwd.loss, fwd.lse, fwd.valid_count
+
+    @staticmethod
+    def backward(ctx, g, *unused):
+        H, W, labels, lse, valid_idx, valid_count = ctx.saved_tensors
+        fwd = ForwardOut(None, lse, valid_idx, valid_count, None, None, None)
+        dH, dW = backward(H, W, labels, fwd, grad_out=g, reduction=ctx.reduction,
+                          ignore_index=ctx.ignore_index)
+        gH = dH.to(H.dtype) if ctx.needs_input_grad[0] else None
+        gW = dW.to(W.dtype) if ctx.needs_input_grad[1] else None
+        return gH, gW, None, None, None, None
+
+
+def linear_cross_entropy(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                         ignore_index: int = -100, reduction: str = "mean",
+                         return_aux: bool = False, check: bool = True):
+    """Cross-entropy of the projection H @ W^T against labels, streamed.
+
+    Returns the reduced loss (a 0-d float32 tensor; NaN for "mean" when every
+    label is ignored).  With return_aux=True also (per-token loss, lse,
+    valid_count).  Gradients flow to H and W (cast to their dtype).
+    """
+    if reduction not in _RED:
+        raise ValueError("reduction must be 'mean' or 'sum'")
+    loss, per_tok, lse, cnt = _LinearCrossEntropy.apply(H, W, labels, ignore_index, reduction,
+                                                        check)
+    if return_aux:
+        return loss, (per_tok, lse, cnt)
+    return loss
