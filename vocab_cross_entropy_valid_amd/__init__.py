@@ -4,6 +4,8 @@ The compute path is liblce.so (hand-written HIP kernels behind a C ABI,
 include/lce.h); ``_lib`` binds it with ctypes under the same names, and
 ``torch_api`` offers ``linear_cross_entropy`` as an autograd function.
 """
+import importlib
+
 from . import _lib  # noqa: F401
 
 __all__ = ["_lib", "torch_api", "linear_cross_entropy"]
@@ -11,6 +13,6 @@ __all__ = ["_lib", "torch_api", "linear_cross_entropy"]
 
 def __getattr__(name):
     if name in ("torch_api", "linear_cross_entropy"):
-        from . import torch_api
-        return torch_api if name == "torch_api" else torch_api.linear_cross_entropy
+        mod = importlib.import_module(__name__ + ".torch_api")
+        return mod if name == "torch_api" else mod.linear_cross_entropy
     raise AttributeError(name)
