@@ -57,13 +57,13 @@ def cpu_baseline(H, W, y, target_s: float):
         oracle.backward(H[rows], W, y[rows], -100)
         return time.perf_counter() - t0
 
-    n = 16
-    t = run(n)
-    # per-row cost plus a fixed part (float64 copies of W); aim at target_s total
-    n2 = int(min(len(valid), max(n, n * target_s / max(t, 1e-3))))
-    if n2 > n:
-        t = run(n2)
-        n = n2
+    # t(n) = fixed (float64 copies of W) + n * per_row; fit from two sizes
+    n1, n2 = 8, 32
+    t1, t2 = run(n1), run(n2)
+    per_row = max((t2 - t1) / (n2 - n1), 1e-6)
+    fixed = max(t1 - n1 * per_row, 0.0)
+    n = int(min(len(valid), max(n2, (target_s - fixed) / per_row)))
+    t = run(n) if n > n2 else t2
     return {"value": n / t, "unit": "valid tokens/s", "cores": threads or cores,
             "kind": "oracle",
             "sample": f"{n} valid rows of the same workload (full V and d), fp64 forward + "
