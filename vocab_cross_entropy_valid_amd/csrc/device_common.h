@@ -10,15 +10,22 @@
 //    [128 wa, 128 wa + 128) and B rows [128 wb, 128 wb + 128) of the tile,
 //    held as 4 x 4 accumulators of the 32x32 MFMA (16 fp32 per lane each,
 //    256 accumulator registers per lane).
-//  * K advances 128 bytes per pipeline stage (64 bf16 or 32 fp32).  In LDS
-//    one operand stage is split by K into four sub-buffers of 256 rows x 32 B
-//    (one per MFMA step); a lane's 16-byte fragment of row r sits at
-//    r * 32 + 16 * (h ^ g(r)) with g(r) = bit 2 ^ bit 3 of r, so that any 8 or
-//    16 consecutive lanes read distinct banks, and the sub-buffers are 32 B
-//    apart modulo 256 so that the loader's 16-byte writes do not collide.
-//    With this layout every LDS address of the main loop is one per-lane
-//    register plus a compile-time offset.  Two operands, double buffered,
-//    take 2 x 2 x 32.1 KB of the 160 KB per CU.
+//  * K advances 128 bytes per pipeline stage (64 bf16 or 32 fp32).  An
+//    operand stage is 256 rows x 128 B = 32 KB of LDS; two operands, double
+//    buffered, use 128 KB of the 160 KB per CU.  The eight 16-byte chunks of
+//    row r are XOR-swizzled (chunk c sits at position c ^ swz(r), swz(r) =
+//    (r ^ (r >> 3)) & 7) so that the fragment reads of 8 or 16 consecutive
+//    rows hit distinct banks.
+//  * Global -> LDS moves use the gfx950 direct-to-LDS 16-byte load
+//    (global_load_lds_dwordx4): each wave instruction fills 1 KB of LDS (8
+//    swizzled rows), each lane fetching the chunk that lands at its slot, so
+//    the 8 lanes of a row read its 128 contiguous bytes.  No staging
+//    registers; the loads of stage k + 1 are in flight while stage k feeds
+//    the MFMAs, and one vmcnt wait + barrier closes each stage.
+//  * Fragment reads are double buffered in registers: the 8 fragments of
+//    MFMA step s + 1 are requested before the 16 MFMAs of step s issue.  A
+//    lane's fragment address is one base register XOR a compile-time
+//    constant plus an immediate offset.
 //  * bf16 uses v_mfma_f32_32x32x16_bf16 (one per 16-byte fragment pair);
 //    fp32 uses four v_mfma_f32_32x32x2_f32, one per float of the fragment.
 //    Lanes 0-31 and 32-63 hold the two halves of a 32-byte K slice.  A and B
@@ -47,10 +54,9 @@ constexpr int kThreads = 256;
 constexpr int kTile = 256;                     // rows of A and of B per tile
 constexpr int kHalf = 128;                     // rows per wave along A or B
 constexpr int kRowBytes = 128;                 // K bytes per row per stage
-constexpr int kSubBytes = kTile * 32 + 32;     // one K sub-buffer (+32 B bank shift)
-constexpr int kOpBytes = 4 * kSubBytes;        // one operand, one stage
+constexpr int kOpBytes = kTile * kRowBytes;    // 32 KB: one operand, one stage
 constexpr int kStageBytes = 2 * kOpBytes;      // A + B
-constexpr int kMainLds = 2 * kStageBytes;      // double buffered
+constexpr int kMainLds = 2 * kStageBytes;      // double buffered: 128 KB
 constexpr int kVocabTile = kTile;              // vocabulary entries per tile
 
 template <typename T> struct Elem;
@@ -65,27 +71,7 @@ template <> struct Elem<float> {
 
 // ---------------------------------------------------------------- LDS layout
 
-__device__ __forceinline__ int lds_g(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
-
-// Row of the loader: thread t moves 16-byte chunk t % 8 of tile rows
-// row_base(t) + 32 i, i = 0..7.  Inside a wave the eight row groups are
-// ordered 0,4,1,5,2,6,3,7 so that lanes t and t + 8 write rows 4 apart
-// (different banks for 16-lane write groups).
-__device__ __forceinline__ int loader_row_base(int tid) {
-  const int q = (tid >> 3) & 7;
-  return ((tid >> 6) << 3) + (((q & 1) << 2) | (q >> 1));
-}
-__device__ __forceinline__ int loader_lds_off(int tid) {
-  const int r = loader_row_base(tid);
-  const int kc = tid & 7;
-  return (kc >> 1) * kSubBytes + r * 32 + (((kc & 1) ^ lds_g(r)) << 4);
-}
-// Per-lane part of a fragment read: row lane % 32 of a 32-row block.
-__device__ __forceinline__ int frag_lds_off(int lane) {
-  const int r = lane & 31;
-  const int h = lane >> 5;
-  return r * 32 + ((h ^ lds_g(r)) << 4);
-}
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Token permutation used when B holds tokens: within each 128-row wave half,
 // MFMA column (nt, j) (nt = 0..3 the accumulator index, j = lane % 32) reads
@@ -118,8 +104,7 @@ template <> struct Mma<float> {
 // Where the 256 rows of one operand tile come from.  Logical row r of the
 // tile is row0 + r; rows at or beyond nrows are clamped to nrows - 1 (their
 // results are never stored); with a gather list the physical row is
-// gather[logical].  With perm_tokens, LDS row R holds logical row
-// tok_of_lds_row(R).
+// gather[logical].
 struct RowSource {
   const char* base;
   int64_t ld;              // row stride in bytes
@@ -128,6 +113,11 @@ struct RowSource {
   int64_t nrows;           // >= 1
 };
 
+// Per-lane global addresses of the 8 direct-to-LDS loads one wave issues per
+// operand and stage.  Load i of wave w fills LDS rows 8 b .. 8 b + 7 with
+// b = 4 i + w; lane L covers row 8 b + L / 8 at slot L % 8, which must hold
+// chunk (L % 8) ^ swz(row).  With kPerm (B holding tokens) LDS row R holds
+// logical row tok_of_lds_row(R).
 struct RowPtrs {
   const char* p[8];
 };
@@ -135,55 +125,109 @@ struct RowPtrs {
 template <bool kPerm>
 __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
   RowPtrs rp;
-  const int kc = tid & 7;
-  const int rb = loader_row_base(tid);
+  const int w = tid >> 6;
+  const int L = tid & 63;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int lr = kPerm ? tok_of_lds_row(rb + 32 * i) : rb + 32 * i;
+    const int row = 8 * (4 * i + w) + (L >> 3);
+    const int chunk = (L & 7) ^ lds_swz(row);
+    const int lr = kPerm ? tok_of_lds_row(row) : row;
     int64_t r = s.row0 + lr;
     if (r >= s.nrows) r = s.nrows - 1;
     const int64_t phys = s.gather ? (int64_t)s.gather[r] : r;
-    rp.p[i] = s.base + phys * s.ld + kc * 16;
+    rp.p[i] = s.base + phys * s.ld + chunk * 16;
   }
   return rp;
 }
 
-struct Staged {
-  u32x4 a[8];
-  u32x4 b[8];
-};
+#define LCE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ void load_stage(Staged& st, const RowPtrs& pa, const RowPtrs& pb,
-                                           int64_t kbyte) {
+// Issue the 16 direct-to-LDS loads (8 per operand) of one stage.
+__device__ __forceinline__ void load_stage(char* stage, const RowPtrs& pa, const RowPtrs& pb,
+                                           int64_t kbyte, int wave_u) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.a[i] = *(const u32x4*)(pa.p[i] + kbyte);
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(pa.p[i] + kbyte, LCE_LDS_PTR(stage + (4 * i + wave_u) * 1024),
+                                     16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.b[i] = *(const u32x4*)(pb.p[i] + kbyte);
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(pb.p[i] + kbyte,
+                                     LCE_LDS_PTR(stage + kOpBytes + (4 * i + wave_u) * 1024), 16,
+                                     0, 0);
 }
 
-// wr = lds stage base + loader_lds_off(tid)
-__device__ __forceinline__ void store_stage(char* wr, const Staged& st) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(u32x4*)(wr + i * 1024) = st.a[i];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(u32x4*)(wr + kOpBytes + i * 1024) = st.b[i];
+// wait for this wave's outstanding global loads (vmcnt = 0), leave others
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Fragment reads of MFMA step s (32 bytes of K).  base = per-lane offset of
+// row (wave half + lane % 32), slot bits holding h ^ (r & 7) ^ (r >> 3);
+// step s XORs 2 s into the slot, mt adds 32 rows (4 KB) and XORs 4 into the
+// slot for odd mt (slot bits are byte-offset bits 4..6, hence XOR, not add).
+__device__ __forceinline__ void load_frags(u32x4 (&f)[4], const char* op, int base, int s) {
+  const int e = base ^ (32 * s);
+  const int o = base ^ ((32 * s) ^ 64);
+  f[0] = *(const u32x4*)(op + e);
+  f[1] = *(const u32x4*)(op + o + 4096);
+  f[2] = *(const u32x4*)(op + e + 8192);
+  f[3] = *(const u32x4*)(op + o + 12288);
 }
 
-// rd_a / rd_b = lds stage base + operand offset + wave-half rows + frag_lds_off
 template <typename T>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* rd_a,
-                                              const char* rd_b) {
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const u32x4 (&fa)[4],
+                                         const u32x4 (&fb)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
+}
+
+#ifndef LCE_SCHED_GROUPS
+#define LCE_SCHED_GROUPS 0
+#endif
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x020;
+constexpr int kSchedDsRead = 0x100;
+
+// One pipeline stage: 4 MFMA steps of 16 MFMAs on the current LDS buffer,
+// with the fragment reads of step s + 1 and (kLoad) the 16 direct-to-LDS
+// loads of the next stage interleaved between the MFMAs of step s.  The
+// sched_group_barrier sequence pins that interleaving; without it the
+// scheduler serialises each fragment read with its MFMAs.
+template <typename T, bool kLoad>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage, int a_base,
+                                              int b_base, char* nxt, const RowPtrs& pa,
+                                              const RowPtrs& pb, int64_t kbyte, int wave_u) {
+  u32x4 fa[2][4], fb[2][4];
+  load_frags(fa[0], stage, a_base, 0);
+  load_frags(fb[0], stage + kOpBytes, b_base, 0);
+  if (kLoad) load_stage(nxt, pa, pb, kbyte, wave_u);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    u32x4 fa[4], fb[4];
+    if (s < 3) {
+      load_frags(fa[(s + 1) & 1], stage, a_base, s + 1);
+      load_frags(fb[(s + 1) & 1], stage + kOpBytes, b_base, s + 1);
+    }
+    mma_step<T>(acc, fa[s & 1], fb[s & 1]);
+  }
+  // schedule: 8 reads of step 0; then per step 16 MFMAs with the 8 reads of
+  // the next step after the first 8 MFMAs and 4 global loads after the rest
+  // (bf16 only: fp32 issues 4 MFMAs per fragment pair and is left alone)
+  if constexpr (sizeof(T) != 2 || !LCE_SCHED_GROUPS) return;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) fa[mt] = *(const u32x4*)(rd_a + s * kSubBytes + mt * 32 * 32);
+  for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) fb[nt] = *(const u32x4*)(rd_b + s * kSubBytes + nt * 32 * 32);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (kLoad) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
   }
 }
 
@@ -197,34 +241,34 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 }
 
 // acc += A_tile(256 x K) * B_tile(256 x K)^T over nstages stages of 128 bytes.
-// Double-buffered LDS with register staging: the global loads of stage k + 1
-// are in flight while stage k feeds the MFMAs.  Ends with a barrier, so the
-// caller may reuse LDS afterwards.
+// Ends with a barrier, so the caller may reuse LDS afterwards.
 template <typename T>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[4][4], char* lds, const RowPtrs& pa,
                                               const RowPtrs& pb, int nstages, int tid) {
   if (nstages <= 0) return;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wa = wave & 1;
   const int wb = wave >> 1;
-  const int wr_off = loader_lds_off(tid);
-  const int rd_off = frag_lds_off(lane);
-  const int rd_a = rd_off + wa * kHalf * 32;
-  const int rd_b = kOpBytes + rd_off + wb * kHalf * 32;
-  Staged st;
-  load_stage(st, pa, pb, 0);
-  store_stage(lds + wr_off, st);
+  const int r = lane & 31;
+  const int x = ((lane >> 5) ^ (r & 7) ^ (r >> 3)) << 4;
+  const int a_base = (wa * kHalf + r) * kRowBytes + x;
+  const int b_base = (wb * kHalf + r) * kRowBytes + x;
+  load_stage(lds, pa, pb, 0, wave_u);
+  wait_vmem();
   __syncthreads();
-  for (int k = 0; k < nstages; ++k) {
-    char* cur = lds + (k & 1) * kStageBytes;
+  for (int k = 0; k + 1 < nstages; ++k) {
+    const char* cur = lds + (k & 1) * kStageBytes;
     char* nxt = lds + ((k + 1) & 1) * kStageBytes;
-    const bool more = k + 1 < nstages;
-    if (more) load_stage(st, pa, pb, (int64_t)(k + 1) * kRowBytes);
-    compute_stage<T>(acc, cur + rd_a, cur + rd_b);
-    if (more) store_stage(nxt + wr_off, st);
+    compute_stage<T, true>(acc, cur, a_base, b_base, nxt, pa, pb, (int64_t)(k + 1) * kRowBytes,
+                           wave_u);
+    wait_vmem();
     __syncthreads();
   }
+  compute_stage<T, false>(acc, lds + ((nstages - 1) & 1) * kStageBytes, a_base, b_base, nullptr,
+                          pa, pb, 0, wave_u);
+  __syncthreads();
 }
 
 // ------------------------------------------------------- XCD-aware mapping
