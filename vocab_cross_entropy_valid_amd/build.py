@@ -29,6 +29,9 @@ FLAGS = [
     "-Wall",
     # keep the compiler from emitting packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # schedule for instruction-level parallelism (one wave per SIMD: the
+    # MFMA loop cannot hide LDS latency behind other waves)
+    "-mllvm", "-amdgpu-sched-strategy=max-ilp",
     f"-I{os.path.join(ROOT, 'include')}",
     f"-I{CSRC}",
 ]

@@ -92,6 +92,10 @@ lce_status check_sizes(int64_t N, int64_t d, int64_t V, int dtype) {
   if (N >= lim || d >= lim || V >= lim)
     return fail(LCE_ERR_UNSUPPORTED, "N, d and V must be below 2^31");
   if (d % 64 != 0) return fail(LCE_ERR_UNSUPPORTED, "d must be a multiple of 64");
+  // gathered token rows are addressed by 32-bit byte offsets from H
+  const int64_t esz = dtype == LCE_BF16 ? 2 : 4;
+  if (N * d * esz >= ((int64_t)1 << 32))
+    return fail(LCE_ERR_UNSUPPORTED, "N * d * element size must stay below 4 GiB");
   return LCE_OK;
 }
 
@@ -203,6 +207,7 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
   fa.labels = labels;
   fa.valid_idx = valid_idx;
   fa.valid_count = valid_count;
+  fa.N = N;
   fa.d = d;
   fa.V = V;
   fa.n_vtiles = p.n_vtiles;
@@ -294,6 +299,7 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       ga.valid_count = valid_count;
       ga.grad_out = grad_out;
       ga.reduction = reduction;
+      ga.N = N;
       ga.d = d;
       ga.V = V;
       ga.c0 = c0;

@@ -111,22 +111,41 @@ struct RowSource {
   const int32_t* gather;   // nullable
   int64_t row0;
   int64_t nrows;           // >= 1
+  int64_t phys_rows;       // rows of the source tensor (bounds of the gathered rows)
 };
 
-// Per-lane global addresses of the 8 direct-to-LDS loads one wave issues per
-// operand and stage.  Load i of wave w fills LDS rows 8 b .. 8 b + 7 with
-// b = 4 i + w; lane L covers row 8 b + L / 8 at slot L % 8, which must hold
-// chunk (L % 8) ^ swz(row).  With kPerm (B holding tokens) LDS row R holds
-// logical row tok_of_lds_row(R).
+// Sources of the 8 direct-to-LDS loads one wave issues per operand and
+// stage: a buffer resource (wave-uniform, in SGPRs) and 32-bit per-lane byte
+// offsets; the stage advance goes in the scalar soffset, so the loop carries
+// no per-lane address arithmetic (buffer_load_dwordx4 ... offen lds).  The
+// resource covers exactly the source tensor: an offset past its end reads
+// zeros instead of faulting.  Load i of wave w fills LDS rows 8 b .. 8 b + 7
+// with b = 4 i + w; lane L covers row 8 b + L / 8 at slot L % 8, which must
+// hold chunk (L % 8) ^ swz(row).  With kPerm (B holding tokens) LDS row R
+// holds logical row tok_of_lds_row(R).  Offsets stay below 4 GB (the host
+// checks the tensor sizes).
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
 struct RowPtrs {
-  const char* p[8];
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[8];
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
+  const int64_t lim = 0xFFFFFFFFll;
+  const uint32_t n = (uint32_t)(bytes < lim ? bytes : lim);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, kBufferFlags);
+}
 
 template <bool kPerm>
 __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
   RowPtrs rp;
   const int w = tid >> 6;
   const int L = tid & 63;
+  // direct rows: the resource starts at row0; gathered rows: at row 0
+  const int64_t first = s.gather ? 0 : s.row0;
+  const int64_t rows = s.gather ? s.phys_rows : s.nrows - s.row0;
+  rp.rsrc = make_rsrc(s.base + first * s.ld, rows * s.ld);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 8 * (4 * i + w) + (L >> 3);
@@ -134,8 +153,8 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
     const int lr = kPerm ? tok_of_lds_row(row) : row;
     int64_t r = s.row0 + lr;
     if (r >= s.nrows) r = s.nrows - 1;
-    const int64_t phys = s.gather ? (int64_t)s.gather[r] : r;
-    rp.p[i] = s.base + phys * s.ld + chunk * 16;
+    const int64_t rel = s.gather ? (int64_t)s.gather[r] : r - s.row0;
+    rp.off[i] = (uint32_t)(rel * s.ld) + chunk * 16;
   }
   return rp;
 }
@@ -144,16 +163,16 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
 
 // Issue the 16 direct-to-LDS loads (8 per operand) of one stage.
 __device__ __forceinline__ void load_stage(char* stage, const RowPtrs& pa, const RowPtrs& pb,
-                                           int64_t kbyte, int wave_u) {
+                                           uint32_t kbyte, int wave_u) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(pa.p[i] + kbyte, LCE_LDS_PTR(stage + (4 * i + wave_u) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pa.rsrc, LCE_LDS_PTR(stage + (4 * i + wave_u) * 1024),
+                                             16, pa.off[i], kbyte, 0, 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(pb.p[i] + kbyte,
-                                     LCE_LDS_PTR(stage + kOpBytes + (4 * i + wave_u) * 1024), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        pb.rsrc, LCE_LDS_PTR(stage + kOpBytes + (4 * i + wave_u) * 1024), 16, pb.off[i], kbyte, 0,
+        0);
 }
 
 // wait for this wave's outstanding global loads (vmcnt = 0), leave others
@@ -261,7 +280,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[4][4], char* lds, co
   for (int k = 0; k + 1 < nstages; ++k) {
     const char* cur = lds + (k & 1) * kStageBytes;
     char* nxt = lds + ((k + 1) & 1) * kStageBytes;
-    compute_stage<T, true>(acc, cur, a_base, b_base, nxt, pa, pb, (int64_t)(k + 1) * kRowBytes,
+    compute_stage<T, true>(acc, cur, a_base, b_base, nxt, pa, pb, (uint32_t)((k + 1) * kRowBytes),
                            wave_u);
     wait_vmem();
     __syncthreads();
@@ -294,6 +313,16 @@ __device__ __forceinline__ bool xcd_tile(int slot, int TM, int TN, int GA, int G
 }
 
 // ---------------------------------------------------------------- helpers
+
+// Read one accumulator element where it is used.  The accumulators live in
+// AGPRs during the main loop; plain C++ uses make the register allocator copy
+// all 256 of them to VGPRs at the loop exit, which spills.  Taking the value
+// as an AGPR operand of an explicit v_accvgpr_read keeps each copy local.
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -12,7 +12,7 @@ struct FwdArgs {
   const int64_t* labels;
   const int32_t* valid_idx;
   const int32_t* valid_count;
-  int64_t d, V;
+  int64_t N, d, V;
   int n_vtiles;  // ceil(V / 256)
   int tpc;       // vocabulary tiles per chunk
   int J;         // chunks: ceil(n_vtiles / tpc)
@@ -31,7 +31,7 @@ struct BwdGArgs {
   const int32_t* valid_count;
   const float* grad_out;
   int reduction;  // 0 mean, 1 sum
-  int64_t d, V;
+  int64_t N, d, V;
   int64_t c0, C;   // token chunk of the compact index
   int64_t v0, Vs;  // vocabulary block
   void* G;         // [C][Vs]

@@ -93,8 +93,7 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
 // holds 4 consecutive tokens).  Epilogue: p = exp(z - lse), subtract 1 at the
 // label, scale by w = grad / N_valid (mean) or grad (sum); entries past V or
 // past the valid tokens are 0.  G is written row-major [token][vocab] for the
-// dH contraction and transposed [vocab][token] for the dW contraction; both
-// stores are 4-element vectors.
+// dH contraction and transposed [vocab][token] for the dW contraction.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
@@ -106,19 +105,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   const int j = lane & 31;
   const int h = lane >> 5;
 
-  const int TM = (int)(a.Vs / kTile);
-  const int TN = (int)(a.C / kTile);
+  // tile grid of this block: vocabulary tiles x token tiles that hold valid
+  // tokens (the count is read on the device, so the active tiles are mapped
+  // first and spread over every XCD; surplus slots exit)
+  const int count = *a.valid_count;
+  const int64_t n_act = min((int64_t)count - a.c0, a.C);
+  if (n_act <= 0) return;
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  const int TM = (int)((nv + kTile - 1) / kTile);
+  const int TN = (int)((n_act + kTile - 1) / kTile);
   int tm, tn;
   if (!xcd_tile(blockIdx.x, TM, TN, 8, 4, tm, tn)) return;
-  const int count = *a.valid_count;
-  const int64_t n_act = (int64_t)count - a.c0;
-  if ((int64_t)tn * kTile >= n_act) return;
-  const int64_t nv = min(a.Vs, a.V - a.v0);
-  if ((int64_t)tm * kTile >= nv) return;
 
   const int64_t ld = a.d * Elem<T>::kSize;
-  RowSource as{(const char*)a.W, ld, nullptr, a.v0 + (int64_t)tm * kTile, a.V};
-  RowSource bs{(const char*)a.H, ld, a.valid_idx, a.c0 + (int64_t)tn * kTile, count};
+  RowSource as{(const char*)a.W, ld, nullptr, a.v0 + (int64_t)tm * kTile, a.V, 0};
+  RowSource bs{(const char*)a.H, ld, a.valid_idx, a.c0 + (int64_t)tn * kTile, count, a.N};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<true>(bs, tid);
 
@@ -146,36 +147,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   zero_acc(acc);
   tile_mainloop<T>(acc, lds, pa, pb, (int)(a.d / Elem<T>::kPerStage), tid);
 
-  const int64_t vl0 = (int64_t)tm * kTile + wa * kHalf;  // first local vocab entry of this wave
+  const int vl0 = tm * kTile + wa * kHalf;  // first local vocab entry of this wave
+  // entry (mt, i) sits at c + 4 h past vl0, c = 32 mt + 8 (i / 4) + i % 4 a
+  // compile-time constant; bounds are shifted instead of the positions
+  const int nv_h = (int)nv - vl0 - 4 * h;             // c < nv_h: inside V
+  int y_h[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) y_h[nt] = (int)(y[nt] - a.v0) - vl0 - 4 * h;  // label at c
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      const int64_t v = a.v0 + vl;
+      const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float p = fast_exp2((acc[mt][nt][i] - lse_t[nt]) * kLog2e);
-        float gv = (p - (v == (int64_t)y[nt] ? 1.f : 0.f)) * w_t[nt];
-        if (vl >= nv) gv = 0.f;
-        acc[mt][nt][i] = gv;
+        const float gv = (p - (c == y_h[nt] ? 1.f : 0.f)) * w_t[nt];
+        // selects (not products) so that a clamped row can never turn into NaN
+        acc[mt][nt][i] = (c < nv_h && w_t[nt] != 0.f) ? gv : 0.f;
       }
     }
 
-  // G[token][vocab]: 4 consecutive vocabulary entries per store
-  const int64_t il0 = (int64_t)tn * kTile + wb * kHalf + 4 * j;  // local token of nt = 0
-  char* G = (char*)a.G;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int64_t vl = vl0 + 32 * mt + 8 * g4 + 4 * h;
-        Store4<T>::run(G + ((il0 + nt) * a.Vs + vl) * Elem<T>::kSize, acc[mt][nt][4 * g4],
-                       acc[mt][nt][4 * g4 + 1], acc[mt][nt][4 * g4 + 2], acc[mt][nt][4 * g4 + 3]);
-      }
-  // G^T[vocab][token]: the lane's 4 consecutive tokens per store
+  // G^T[vocab][token]: the lane's 4 consecutive tokens per store; for a fixed
+  // accumulator register the 32 lanes of a half-wave cover 256 contiguous bytes
+  const int il0 = tn * kTile + wb * kHalf + 4 * j;  // local token of nt = 0
   char* GT = (char*)a.GT;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -185,6 +180,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
       Store4<T>::run(GT + (vl * a.C + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i],
                      acc[mt][2][i], acc[mt][3][i]);
     }
+
+  char* G = (char*)a.G;
+  if constexpr (sizeof(T) == 2) {
+    // G[token][vocab] goes through LDS: a lane holds 4 tokens x 64 vocabulary
+    // entries, so direct row-major stores would scatter.  The 256 x 256 bf16
+    // tile (128 KB) is written to LDS as rows of 32 sixteen-byte slots, slot q
+    // of row t at position q ^ ((t >> 2) & 31) (conflict-free for both the
+    // scattered writes and the row reads), then streamed out row by row.
+    // The main loop ended with a barrier, so its LDS buffers are free.
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int row = wb * kHalf + 4 * j + nt;
+      const int f = (row >> 2) & 31;
+      char* lrow = lds + row * 512;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q = wa * 16 + 4 * mt + g4;
+          Store4<T>::run(lrow + ((q ^ f) << 4) + 8 * h, acc[mt][nt][4 * g4],
+                         acc[mt][nt][4 * g4 + 1], acc[mt][nt][4 * g4 + 2], acc[mt][nt][4 * g4 + 3]);
+        }
+    }
+    __syncthreads();
+    const int64_t grow0 = (int64_t)tn * kTile;
+    const int64_t gcol0 = (int64_t)tm * kTile;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int idx = it * kThreads + tid;
+      const int row = idx >> 5;
+      const int q = idx & 31;
+      const u32x4 v = *(const u32x4*)(lds + row * 512 + ((q ^ ((row >> 2) & 31)) << 4));
+      *(u32x4*)(G + ((grow0 + row) * a.Vs + gcol0 + 8 * q) * 2) = v;
+    }
+  } else {
+    // fp32 (small shapes only): direct 16-byte stores
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t vl = vl0 + 32 * mt + 8 * g4 + 4 * h;
+          Store4<T>::run(G + ((int64_t)(il0 + nt) * a.Vs + vl) * Elem<T>::kSize,
+                         acc[mt][nt][4 * g4], acc[mt][nt][4 * g4 + 1], acc[mt][nt][4 * g4 + 2],
+                         acc[mt][nt][4 * g4 + 3]);
+        }
+  }
 }
 
 hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s) {
@@ -215,14 +258,14 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const int wb = wave >> 1;
   const int h = lane >> 5;
 
-  const int TM = (int)(a.C / kTile);
+  // token tiles holding valid tokens x hidden tiles; active tiles map first
+  const int count = *a.valid_count;
+  const int64_t n_act = min((int64_t)count - a.c0, a.C);
+  if (n_act <= 0) return;
+  const int TM = (int)((n_act + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
   int tm, tn;
   if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
-  const int count = *a.valid_count;
-  int64_t n_act = (int64_t)count - a.c0;
-  if (n_act > a.C) n_act = a.C;
-  if ((int64_t)tm * kTile >= n_act) return;
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
 
@@ -232,8 +275,8 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   }
   __syncthreads();
   const int64_t ld = a.Vs * Elem<T>::kSize;
-  RowSource as{(const char*)a.G, ld, nullptr, (int64_t)tm * kTile, a.C};
-  RowSource bs{(const char*)a.WT, ld, nullptr, (int64_t)tn * kTile, a.d};
+  RowSource as{(const char*)a.G, ld, nullptr, (int64_t)tm * kTile, a.C, 0};
+  RowSource bs{(const char*)a.WT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   f32x16 acc[4][4];
@@ -300,12 +343,11 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const int wb = wave >> 1;
   const int h = lane >> 5;
 
-  const int TM = (int)(a.Vs / kTile);
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  const int TM = (int)((nv + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
   int tm, tn;
   if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
-  const int64_t nv = min(a.Vs, a.V - a.v0);
-  if ((int64_t)tm * kTile >= nv) return;
   const int count = *a.valid_count;
   int64_t kact = (int64_t)count - a.c0;
   if (kact < 0) kact = 0;
@@ -314,8 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   if (nstages == 0 && a.accumulate) return;
 
   const int64_t ld = a.C * Elem<T>::kSize;
-  RowSource as{(const char*)a.GT, ld, nullptr, (int64_t)tm * kTile, a.Vs};
-  RowSource bs{(const char*)a.HT, ld, nullptr, (int64_t)tn * kTile, a.d};
+  RowSource as{(const char*)a.GT, ld, nullptr, (int64_t)tm * kTile, a.Vs, 0};
+  RowSource bs{(const char*)a.HT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   f32x16 acc[4][4];
@@ -388,8 +430,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(const void* A, con
   int tm, tn;
   if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
   const int64_t ld = K * Elem<T>::kSize;
-  RowSource as{(const char*)A, ld, nullptr, (int64_t)tm * kTile, M};
-  RowSource bs{(const char*)B, ld, nullptr, (int64_t)tn * kTile, N};
+  RowSource as{(const char*)A, ld, nullptr, (int64_t)tm * kTile, M, 0};
+  RowSource bs{(const char*)B, ld, nullptr, (int64_t)tn * kTile, N, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   f32x16 acc[4][4];

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     int tt, ch;
     if (!xcd_tile((int)ls, R, a.J, GA, GB, tt, ch)) continue;
 
-    RowSource bs{(const char*)a.H, ldb, a.valid_idx, (int64_t)tt * kTile, count};
+    RowSource bs{(const char*)a.H, ldb, a.valid_idx, (int64_t)tt * kTile, count, a.N};
     const RowPtrs pb = make_row_ptrs<true>(bs, tid);
 
     int y[4];
@@ -143,51 +143,50 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     const int vt0 = ch * a.tpc;
     const int vt1 = min(vt0 + a.tpc, a.n_vtiles);
     for (int vt = vt0; vt < vt1; ++vt) {
-      RowSource as{(const char*)a.W, ldb, nullptr, (int64_t)vt * kVocabTile, a.V};
+      RowSource as{(const char*)a.W, ldb, nullptr, (int64_t)vt * kVocabTile, a.V, 0};
       const RowPtrs pa = make_row_ptrs<false>(as, tid);
       f32x16 acc[4][4];
       zero_acc(acc);
       tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
 
       const int vw0 = vt * kVocabTile + wa * kHalf;  // first vocabulary entry of this wave
-      // entries of this lane at or beyond V (only in the last tile): vr >= vlim
-      const int vlim = (int)min<int64_t>(a.V - vw0, (int64_t)kHalf);
+      // Entry (mt, i) of this lane sits at c(mt, i) + 4 h past vw0, with the
+      // compile-time constant c = 32 mt + 8 (i / 4) + i % 4.  Comparing c with
+      // per-lane bounds keeps the 64 positions out of registers.
+      const int vlim_h = (int)min<int64_t>(a.V - vw0, (int64_t)kHalf) - 4 * h;  // c < vlim_h: < V
+      // per token: online (max, sum) update over each 32-entry slice (mt), so
+      // that only 16 accumulator values are live in VGPRs at a time
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        float z[64];
+        const int rel_h = y[nt] - vw0 - 4 * h;  // label at c == rel_h
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+          float z[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int vr = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+            const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
             // entries at or beyond V (last tile only) drop out as -inf
-            z[16 * mt + i] = vr < vlim ? acc[mt][nt][i] : -INFINITY;
+            z[i] = c < vlim_h ? acc_read(acc[mt][nt][i]) : -INFINITY;
+            // target logit, taken from the same fp32 accumulator as the sum
+            if (c == rel_h) zy[nt] = z[i];
           }
-        // target logit, taken from the same fp32 accumulator as the sum
-        const int rel = y[nt] - vw0;
-        if ((unsigned)rel < (unsigned)kHalf) {
+          float tmax = z[0];
 #pragma unroll
-          for (int q = 0; q < 64; ++q) {
-            const int vr = 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * h + (q & 3);
-            if (vr == rel) zy[nt] = z[q];
+          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[i]);
+          if (tmax != -INFINITY) {  // else every entry of this slice is past V
+            tmax *= kLog2e;
+            if (tmax > m[nt]) {
+              s[nt] *= fast_exp2(m[nt] - tmax);
+              m[nt] = tmax;
+            }
+            const float mn = m[nt];
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(z[i], kLog2e, -mn));
+            s[nt] += sum;
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 64; ++q) tmax = fmaxf(tmax, z[q]);
-        if (tmax != -INFINITY) {  // else every entry of this lane is past V
-          tmax *= kLog2e;
-          if (tmax > m[nt]) {
-            s[nt] *= fast_exp2(m[nt] - tmax);
-            m[nt] = tmax;
-          }
-          const float mn = m[nt];
-          float sum = 0.f;
-#pragma unroll
-          for (int q = 0; q < 64; ++q) sum += fast_exp2(fmaf(z[q], kLog2e, -mn));
-          s[nt] += sum;
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
