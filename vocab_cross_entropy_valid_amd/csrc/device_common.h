@@ -6,10 +6,11 @@
 // contiguously): that is how H [N, d] and W [V, d] are stored, and how the
 // backward pass lays out its bounded G / G^T / W^T / H^T buffers.
 //
-//  * 256 threads = 4 waves in a 2 x 2 arrangement; wave (wa, wb) owns A rows
-//    [128 wa, 128 wa + 128) and B rows [128 wb, 128 wb + 128) of the tile,
-//    held as 4 x 4 accumulators of the 32x32 MFMA (16 fp32 per lane each,
-//    256 accumulator registers per lane).
+//  * 512 threads = 8 waves, two per SIMD, in a 2 x 4 arrangement: wave
+//    (wa, wb) owns A rows [128 wa, 128 wa + 128) and B rows [64 wb, 64 wb +
+//    64) of the tile, held as 4 x 2 accumulators of the 32x32 MFMA (16 fp32
+//    per lane each, 128 accumulator registers per lane).  Two waves per SIMD
+//    let one wave's MFMAs run while the other waits on a barrier or on LDS.
 //  * K advances 128 bytes per pipeline stage (64 bf16 or 32 fp32).  An
 //    operand stage is 256 rows x 128 B = 32 KB of LDS; two operands, double
 //    buffered, use 128 KB of the 160 KB per CU.  The eight 16-byte chunks of
@@ -44,15 +45,18 @@ typedef uint16_t bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kTile = 256;                     // rows of A and of B per tile
-constexpr int kHalf = 128;                     // rows per wave along A or B
+constexpr int kHalf = 128;                     // rows per wave along A
+constexpr int kWaveN = 64;                     // rows per wave along B
+constexpr int kNT = 2;                         // 32-row MFMA blocks per wave along B
 constexpr int kRowBytes = 128;                 // K bytes per row per stage
 constexpr int kOpBytes = kTile * kRowBytes;    // 32 KB: one operand, one stage
 constexpr int kStageBytes = 2 * kOpBytes;      // A + B
@@ -73,12 +77,12 @@ template <> struct Elem<float> {
 
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Token permutation used when B holds tokens: within each 128-row wave half,
-// MFMA column (nt, j) (nt = 0..3 the accumulator index, j = lane % 32) reads
-// LDS row 32 nt + j, which is loaded with token 4 j + nt, so that one lane owns
-// four consecutive tokens.  tok_of_lds_row maps an LDS row to its token.
+// Token permutation used when B holds tokens: within each 64-row wave slice,
+// MFMA column (nt, j) (nt = 0..1 the accumulator index, j = lane % 32) reads
+// LDS row 32 nt + j, which is loaded with token 2 j + nt, so that one lane owns
+// two consecutive tokens.  tok_of_lds_row maps an LDS row to its token.
 __device__ __forceinline__ int tok_of_lds_row(int r) {
-  return (r & kHalf) | (((r & 31) << 2) + ((r & (kHalf - 1)) >> 5));
+  return (r & ~(kWaveN - 1)) | ((r & 31) << 1) | ((r >> 5) & 1);
 }
 
 // ------------------------------------------------------------------- MFMA
@@ -120,7 +124,7 @@ struct RowSource {
 // no per-lane address arithmetic (buffer_load_dwordx4 ... offen lds).  The
 // resource covers exactly the source tensor: an offset past its end reads
 // zeros instead of faulting.  Load i of wave w fills LDS rows 8 b .. 8 b + 7
-// with b = 4 i + w; lane L covers row 8 b + L / 8 at slot L % 8, which must
+// with b = 8 i + w; lane L covers row 8 b + L / 8 at slot L % 8, which must
 // hold chunk (L % 8) ^ swz(row).  With kPerm (B holding tokens) LDS row R
 // holds logical row tok_of_lds_row(R).  Offsets stay below 4 GB (the host
 // checks the tensor sizes).
@@ -128,7 +132,7 @@ constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer, gfx9 family
 
 struct RowPtrs {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[8];
+  uint32_t off[4];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
@@ -147,8 +151,8 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
   const int64_t rows = s.gather ? s.phys_rows : s.nrows - s.row0;
   rp.rsrc = make_rsrc(s.base + first * s.ld, rows * s.ld);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (4 * i + w) + (L >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (8 * i + w) + (L >> 3);
     const int chunk = (L & 7) ^ lds_swz(row);
     const int lr = kPerm ? tok_of_lds_row(row) : row;
     int64_t r = s.row0 + lr;
@@ -161,17 +165,17 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
 
 #define LCE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Issue the 16 direct-to-LDS loads (8 per operand) of one stage.
+// Issue the 8 direct-to-LDS loads (4 per operand) of one wave for one stage.
 __device__ __forceinline__ void load_stage(char* stage, const RowPtrs& pa, const RowPtrs& pb,
                                            uint32_t kbyte, int wave_u) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(pa.rsrc, LCE_LDS_PTR(stage + (4 * i + wave_u) * 1024),
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pa.rsrc, LCE_LDS_PTR(stage + (8 * i + wave_u) * 1024),
                                              16, pa.off[i], kbyte, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        pb.rsrc, LCE_LDS_PTR(stage + kOpBytes + (4 * i + wave_u) * 1024), 16, pb.off[i], kbyte, 0,
+        pb.rsrc, LCE_LDS_PTR(stage + kOpBytes + (8 * i + wave_u) * 1024), 16, pb.off[i], kbyte, 0,
         0);
 }
 
@@ -191,70 +195,50 @@ __device__ __forceinline__ void load_frags(u32x4 (&f)[4], const char* op, int ba
   f[3] = *(const u32x4*)(op + o + 12288);
 }
 
+// B fragments of a 64-row wave slice: two 32-row blocks
+__device__ __forceinline__ void load_frags_b(u32x4 (&f)[kNT], const char* op, int base, int s) {
+  const int e = base ^ (32 * s);
+  const int o = base ^ ((32 * s) ^ 64);
+  f[0] = *(const u32x4*)(op + e);
+  f[1] = *(const u32x4*)(op + o + 4096);
+}
+
+typedef f32x16 Acc[4][kNT];
+
 template <typename T>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const u32x4 (&fa)[4],
-                                         const u32x4 (&fb)[4]) {
+__device__ __forceinline__ void mma_step(Acc& acc, const u32x4 (&fa)[4], const u32x4 (&fb)[kNT]) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
+    for (int nt = 0; nt < kNT; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
 }
 
-#ifndef LCE_SCHED_GROUPS
-#define LCE_SCHED_GROUPS 0
-#endif
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmem = 0x020;
-constexpr int kSchedDsRead = 0x100;
-
-// One pipeline stage: 4 MFMA steps of 16 MFMAs on the current LDS buffer,
-// with the fragment reads of step s + 1 and (kLoad) the 16 direct-to-LDS
-// loads of the next stage interleaved between the MFMAs of step s.  The
-// sched_group_barrier sequence pins that interleaving; without it the
-// scheduler serialises each fragment read with its MFMAs.
+// One pipeline stage: 4 MFMA steps on the current LDS buffer; the fragment
+// reads of step s + 1 and (kLoad) the direct-to-LDS loads of the next stage
+// are issued before the MFMAs of step s.
 template <typename T, bool kLoad>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage, int a_base,
-                                              int b_base, char* nxt, const RowPtrs& pa,
-                                              const RowPtrs& pb, int64_t kbyte, int wave_u) {
-  u32x4 fa[2][4], fb[2][4];
+__device__ __forceinline__ void compute_stage(Acc& acc, const char* stage, int a_base, int b_base,
+                                              char* nxt, const RowPtrs& pa, const RowPtrs& pb,
+                                              uint32_t kbyte, int wave_u) {
+  u32x4 fa[2][4], fb[2][kNT];
   load_frags(fa[0], stage, a_base, 0);
-  load_frags(fb[0], stage + kOpBytes, b_base, 0);
+  load_frags_b(fb[0], stage + kOpBytes, b_base, 0);
   if (kLoad) load_stage(nxt, pa, pb, kbyte, wave_u);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < 3) {
       load_frags(fa[(s + 1) & 1], stage, a_base, s + 1);
-      load_frags(fb[(s + 1) & 1], stage + kOpBytes, b_base, s + 1);
+      load_frags_b(fb[(s + 1) & 1], stage + kOpBytes, b_base, s + 1);
     }
     mma_step<T>(acc, fa[s & 1], fb[s & 1]);
   }
-  // schedule: 8 reads of step 0; then per step 16 MFMAs with the 8 reads of
-  // the next step after the first 8 MFMAs and 4 global loads after the rest
-  // (bf16 only: fp32 issues 4 MFMAs per fragment pair and is left alone)
-  if constexpr (sizeof(T) != 2 || !LCE_SCHED_GROUPS) return;
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (kLoad) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    }
-  }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 }
@@ -262,7 +246,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 // acc += A_tile(256 x K) * B_tile(256 x K)^T over nstages stages of 128 bytes.
 // Ends with a barrier, so the caller may reuse LDS afterwards.
 template <typename T>
-__device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[4][4], char* lds, const RowPtrs& pa,
+__device__ __forceinline__ void tile_mainloop(Acc& acc, char* lds, const RowPtrs& pa,
                                               const RowPtrs& pb, int nstages, int tid) {
   if (nstages <= 0) return;
   const int lane = tid & 63;
@@ -273,7 +257,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[4][4], char* lds, co
   const int r = lane & 31;
   const int x = ((lane >> 5) ^ (r & 7) ^ (r >> 3)) << 4;
   const int a_base = (wa * kHalf + r) * kRowBytes + x;
-  const int b_base = (wb * kHalf + r) * kRowBytes + x;
+  const int b_base = (wb * kWaveN + r) * kRowBytes + x;
   load_stage(lds, pa, pb, 0, wave_u);
   wait_vmem();
   __syncthreads();
@@ -314,16 +298,6 @@ __device__ __forceinline__ bool xcd_tile(int slot, int TM, int TN, int GA, int G
 
 // ---------------------------------------------------------------- helpers
 
-// Read one accumulator element where it is used.  The accumulators live in
-// AGPRs during the main loop; plain C++ uses make the register allocator copy
-// all 256 of them to VGPRs at the loop exit, which spills.  Taking the value
-// as an AGPR operand of an explicit v_accvgpr_read keeps each copy local.
-__device__ __forceinline__ float acc_read(float x) {
-  float r;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
-  return r;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -333,6 +307,19 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+
+template <typename T> struct Store2;
+template <> struct Store2<bf16_t> {
+  __device__ __forceinline__ static void run(void* p, float a, float b) {
+    *(uint32_t*)p = bf16_bits(a) | (bf16_bits(b) << 16);
+  }
+};
+template <> struct Store2<float> {
+  __device__ __forceinline__ static void run(void* p, float a, float b) {
+    f32x2 v = {a, b};
+    *(f32x2*)p = v;
+  }
+};
 
 template <typename T> struct Store4;
 template <> struct Store4<bf16_t> {

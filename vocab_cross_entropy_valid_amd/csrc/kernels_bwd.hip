@@ -90,7 +90,7 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
 // --------------------------------------------------- recompute + G tile
 //
 // Same MFMA tile as the forward (A = W rows, B = gathered H rows, so each lane
-// holds 4 consecutive tokens).  Epilogue: p = exp(z - lse), subtract 1 at the
+// holds 2 consecutive tokens).  Epilogue: p = exp(z - lse), subtract 1 at the
 // label, scale by w = grad / N_valid (mean) or grad (sum); entries past V or
 // past the valid tokens are 0.  G is written row-major [token][vocab] for the
 // dH contraction and transposed [vocab][token] for the dW contraction.
@@ -123,14 +123,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<true>(bs, tid);
 
-  // per-token data (4 consecutive tokens per lane)
-  float lse_t[4], w_t[4];
-  int y[4];
+  // per-token data (2 consecutive tokens per lane)
+  float lse_t[kNT], w_t[kNT];
+  int y[kNT];
   const float g = *a.grad_out;
   const float w = a.reduction == 0 ? g / (float)count : g;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t i = a.c0 + (int64_t)tn * kTile + wb * kHalf + 4 * j + nt;
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int64_t i = a.c0 + (int64_t)tn * kTile + wb * kWaveN + 2 * j + nt;
     if (i < count) {
       const int r = a.valid_idx[i];
       y[nt] = (int)a.labels[r];
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
     }
   }
 
-  f32x16 acc[4][4];
+  Acc acc;
   zero_acc(acc);
   tile_mainloop<T>(acc, lds, pa, pb, (int)(a.d / Elem<T>::kPerStage), tid);
 
@@ -151,16 +151,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   // entry (mt, i) sits at c + 4 h past vl0, c = 32 mt + 8 (i / 4) + i % 4 a
   // compile-time constant; bounds are shifted instead of the positions
   const int nv_h = (int)nv - vl0 - 4 * h;             // c < nv_h: inside V
-  int y_h[4];
+  int y_h[kNT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) y_h[nt] = (int)(y[nt] - a.v0) - vl0 - 4 * h;  // label at c
+  for (int nt = 0; nt < kNT; ++nt) y_h[nt] = (int)(y[nt] - a.v0) - vl0 - 4 * h;  // label at c
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const float p = fast_exp2((acc[mt][nt][i] - lse_t[nt]) * kLog2e);
         const float gv = (p - (c == y_h[nt] ? 1.f : 0.f)) * w_t[nt];
         // selects (not products) so that a clamped row can never turn into NaN
@@ -168,31 +168,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
       }
     }
 
-  // G^T[vocab][token]: the lane's 4 consecutive tokens per store; for a fixed
-  // accumulator register the 32 lanes of a half-wave cover 256 contiguous bytes
-  const int il0 = tn * kTile + wb * kHalf + 4 * j;  // local token of nt = 0
+  // G^T[vocab][token]: the lane's 2 consecutive tokens per store; for a fixed
+  // accumulator register the 32 lanes of a half-wave cover 128 contiguous bytes
+  const int il0 = tn * kTile + wb * kWaveN + 2 * j;  // local token of nt = 0
   char* GT = (char*)a.GT;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      Store4<T>::run(GT + (vl * a.C + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i],
-                     acc[mt][2][i], acc[mt][3][i]);
+      Store2<T>::run(GT + (vl * a.C + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
     }
 
   char* G = (char*)a.G;
   if constexpr (sizeof(T) == 2) {
-    // G[token][vocab] goes through LDS: a lane holds 4 tokens x 64 vocabulary
+    // G[token][vocab] goes through LDS: a lane holds 2 tokens x 64 vocabulary
     // entries, so direct row-major stores would scatter.  The 256 x 256 bf16
     // tile (128 KB) is written to LDS as rows of 32 sixteen-byte slots, slot q
-    // of row t at position q ^ ((t >> 2) & 31) (conflict-free for both the
+    // of row t at position q ^ ((t >> 1) & 31) (conflict-free for both the
     // scattered writes and the row reads), then streamed out row by row.
     // The main loop ended with a barrier, so its LDS buffers are free.
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int row = wb * kHalf + 4 * j + nt;
-      const int f = (row >> 2) & 31;
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int row = wb * kWaveN + 2 * j + nt;
+      const int f = (row >> 1) & 31;
       char* lrow = lds + row * 512;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -207,17 +206,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
     const int64_t grow0 = (int64_t)tn * kTile;
     const int64_t gcol0 = (int64_t)tm * kTile;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
+    for (int it = 0; it < kTile * 32 / kThreads; ++it) {
       const int idx = it * kThreads + tid;
       const int row = idx >> 5;
       const int q = idx & 31;
-      const u32x4 v = *(const u32x4*)(lds + row * 512 + ((q ^ ((row >> 2) & 31)) << 4));
+      const u32x4 v = *(const u32x4*)(lds + row * 512 + ((q ^ ((row >> 1) & 31)) << 4));
       *(u32x4*)(G + ((grow0 + row) * a.Vs + gcol0 + 8 * q) * 2) = v;
     }
   } else {
     // fp32 (small shapes only): direct 16-byte stores
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -269,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
 
-  {
+  if (tid < kTile) {
     const int64_t m = (int64_t)tm * kTile + tid;
     rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
   }
@@ -279,11 +278,11 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   RowSource bs{(const char*)a.WT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
-  f32x16 acc[4][4];
+  Acc acc;
   zero_acc(acc);
   tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: rows[] visible
 
-  const int n_base = tn * kTile + wb * kHalf + (lane & 31);
+  const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   if (a.beta) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
         if (r < 0) continue;
         float* out = a.dH + (int64_t)r * a.d;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           const int n = n_base + 32 * nt;
           if (n < a.d) out[n] += acc[mt][nt][i];
         }
@@ -308,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
         if (r < 0) continue;
         float* out = a.dH + (int64_t)r * a.d;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           const int n = n_base + 32 * nt;
           if (n < a.d) out[n] = acc[mt][nt][i];
         }
@@ -360,11 +359,11 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   RowSource bs{(const char*)a.HT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
-  f32x16 acc[4][4];
+  Acc acc;
   zero_acc(acc);
   tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
 
-  const int n_base = tn * kTile + wb * kHalf + (lane & 31);
+  const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   const int m_base = tm * kTile + wa * kHalf + 4 * h;
   float* out0 = a.dW + a.v0 * a.d;
   if (a.accumulate) {
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
         if (ml >= nv) continue;
         float* out = out0 + (int64_t)ml * a.d;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           const int n = n_base + 32 * nt;
           if (n < a.d) out[n] += acc[mt][nt][i];
         }
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
         if (ml >= nv) continue;
         float* out = out0 + (int64_t)ml * a.d;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           const int n = n_base + 32 * nt;
           if (n < a.d) out[n] = acc[mt][nt][i];
         }
@@ -434,10 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(const void* A, con
   RowSource bs{(const char*)B, ld, nullptr, (int64_t)tn * kTile, N, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
-  f32x16 acc[4][4];
+  Acc acc;
   zero_acc(acc);
   tile_mainloop<T>(acc, lds, pa, pb, (int)(K / Elem<T>::kPerStage), tid);
-  const int64_t n_base = (int64_t)tn * kTile + wb * kHalf + (lane & 31);
+  const int64_t n_base = (int64_t)tn * kTile + wb * kWaveN + (lane & 31);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -445,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(const void* A, con
       const int64_t m = (int64_t)tm * kTile + wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
       if (m >= M) continue;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const int64_t n = n_base + 32 * nt;
         if (n < N) C[m * N + n] = acc[mt][nt][i];
       }

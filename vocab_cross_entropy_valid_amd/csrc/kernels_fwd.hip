@@ -95,13 +95,13 @@ hipError_t launch_compact(const int64_t* labels, int64_t N, int64_t ignore_index
 // chunk; fwd_merge_kernel combines the J chunks.
 //
 // MFMA operand order: A = W rows (vocabulary), B = H rows (tokens, gathered
-// through valid_idx).  Each lane then holds 4 consecutive tokens x 64
+// through valid_idx).  Each lane then holds 2 consecutive tokens x 64
 // vocabulary entries per tile, so the max / sum reductions run inside the
 // lane, and only once per item across the lane pair (l, l ^ 32) and across
 // the two waves that split the tile's vocabulary.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 2 * kHalf * 3 * sizeof(float)];
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds + kTile * 3 * sizeof(float)];
   float* mg = (float*)(lds + kMainLds);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,11 +129,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     RowSource bs{(const char*)a.H, ldb, a.valid_idx, (int64_t)tt * kTile, count, a.N};
     const RowPtrs pb = make_row_ptrs<true>(bs, tid);
 
-    int y[4];
-    float m[4], s[4], zy[4];
+    int y[kNT];
+    float m[kNT], s[kNT], zy[kNT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int i = tt * kTile + wb * kHalf + 4 * j + nt;
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int i = tt * kTile + wb * kWaveN + 2 * j + nt;
       y[nt] = (i < count) ? (int)a.labels[a.valid_idx[i]] : -1;
       m[nt] = -INFINITY;
       s[nt] = 0.f;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     for (int vt = vt0; vt < vt1; ++vt) {
       RowSource as{(const char*)a.W, ldb, nullptr, (int64_t)vt * kVocabTile, a.V, 0};
       const RowPtrs pa = make_row_ptrs<false>(as, tid);
-      f32x16 acc[4][4];
+      Acc acc;
       zero_acc(acc);
       tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
 
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       // per token: online (max, sum) update over each 32-entry slice (mt), so
       // that only 16 accumulator values are live in VGPRs at a time
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const int rel_h = y[nt] - vw0 - 4 * h;  // label at c == rel_h
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
           for (int i = 0; i < 16; ++i) {
             const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
             // entries at or beyond V (last tile only) drop out as -inf
-            z[i] = c < vlim_h ? acc_read(acc[mt][nt][i]) : -INFINITY;
+            z[i] = c < vlim_h ? acc[mt][nt][i] : -INFINITY;
             // target logit, taken from the same fp32 accumulator as the sum
             if (c == rel_h) zy[nt] = z[i];
           }
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
 
     // merge the lane pair (l, l ^ 32): same tokens, other vocabulary rows
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
       const float mo = __shfl_xor(m[nt], 32);
       const float so = __shfl_xor(s[nt], 32);
       const float zo = __shfl_xor(zy[nt], 32);
@@ -204,8 +204,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     // merge the two waves (wa = 0, 1) that split the tile's vocabulary
     if (wa == 1 && h == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float* q = mg + (wb * kHalf + 4 * j + nt) * 3;
+      for (int nt = 0; nt < kNT; ++nt) {
+        float* q = mg + (wb * kWaveN + 2 * j + nt) * 3;
         q[0] = m[nt];
         q[1] = s[nt];
         q[2] = zy[nt];
@@ -213,19 +213,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
     }
     __syncthreads();
     if (wa == 0 && h == 0) {
-      f32x4 om, os, oz;
+      f32x2 om, os, oz;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float* q = mg + (wb * kHalf + 4 * j + nt) * 3;
+      for (int nt = 0; nt < kNT; ++nt) {
+        const float* q = mg + (wb * kWaveN + 2 * j + nt) * 3;
         const float M = fmaxf(m[nt], q[0]);
         om[nt] = M;
         os[nt] = (M == -INFINITY) ? 0.f : s[nt] * fast_exp2(m[nt] - M) + q[1] * fast_exp2(q[0] - M);
         oz[nt] = fmaxf(zy[nt], q[2]);
       }
-      const int64_t off = (int64_t)ch * a.Nb + (int64_t)tt * kTile + wb * kHalf + 4 * j;
-      *(f32x4*)(a.pm + off) = om;
-      *(f32x4*)(a.ps + off) = os;
-      *(f32x4*)(a.pz + off) = oz;
+      const int64_t off = (int64_t)ch * a.Nb + (int64_t)tt * kTile + wb * kWaveN + 2 * j;
+      *(f32x2*)(a.pm + off) = om;
+      *(f32x2*)(a.ps + off) = os;
+      *(f32x2*)(a.pz + off) = oz;
     }
     __syncthreads();
   }
