@@ -33,6 +33,7 @@ lce_status hip_fail(hipError_t e, const char* what) {
 constexpr int64_t kChunkMax = 8192;
 constexpr int64_t kVocabBlockMax = 8192;
 constexpr int64_t kTargetChunks = 64;  // vocabulary chunks of the forward
+constexpr int64_t kStridePad = 64;     // elements added to workspace row strides
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -48,6 +49,7 @@ struct Plan {
   size_t off_pm, off_ps, off_pz, off_lossc, fwd_bytes;
   // backward
   int64_t C, Vs;
+  int64_t ldG, ldGT, ldHT, ldWT;  // padded row strides (elements)
   size_t off_G, off_GT, off_HT, off_WT, bwd_bytes;
   size_t total;
 };
@@ -72,11 +74,18 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype) {
   p.fwd_bytes = o;
   p.C = std::min<int64_t>(kChunkMax, round_up(std::max<int64_t>(N, 1), 256));
   p.Vs = std::min<int64_t>(kVocabBlockMax, round_up(V, 256));
+  // Row strides of the K-contiguous backward buffers are padded by 64
+  // elements: with power-of-two strides the 256 rows of a tile all start on
+  // the same memory channel at every K step.
+  p.ldG = p.Vs + kStridePad;
+  p.ldGT = p.C + kStridePad;
+  p.ldHT = p.C + kStridePad;
+  p.ldWT = p.Vs + kStridePad;
   o = 0;
-  p.off_G = o; o += align_up((size_t)p.C * (size_t)p.Vs * p.esz);
-  p.off_GT = o; o += align_up((size_t)p.C * (size_t)p.Vs * p.esz);
-  p.off_HT = o; o += align_up((size_t)d * (size_t)p.C * p.esz);
-  p.off_WT = o; o += align_up((size_t)d * (size_t)p.Vs * p.esz);
+  p.off_G = o; o += align_up((size_t)p.C * (size_t)p.ldG * p.esz);
+  p.off_GT = o; o += align_up((size_t)p.Vs * (size_t)p.ldGT * p.esz);
+  p.off_HT = o; o += align_up((size_t)d * (size_t)p.ldHT * p.esz);
+  p.off_WT = o; o += align_up((size_t)d * (size_t)p.ldWT * p.esz);
   p.bwd_bytes = o;
   p.total = std::max(p.fwd_bytes, p.bwd_bytes);
   return p;
@@ -269,6 +278,7 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
     th.count = valid_count;
     th.dst = HT;
     th.ncols = p.C;
+    th.ld_dst = p.ldHT;
     th.K = d;
     th.active_count = c0 > 0 ? valid_count : nullptr;
     th.active_c0 = c0;
@@ -284,6 +294,7 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       tw.nrows_static = V;
       tw.dst = WT;
       tw.ncols = p.Vs;
+      tw.ld_dst = p.ldWT;
       tw.K = d;
       tw.active_count = c0 > 0 ? valid_count : nullptr;
       tw.active_c0 = c0;
@@ -308,12 +319,16 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       ga.Vs = p.Vs;
       ga.G = G;
       ga.GT = GT;
+      ga.ldG = p.ldG;
+      ga.ldGT = p.ldGT;
       e = run(LCE_K_BWD_G, s, [&] { return lce::launch_bwd_g(ga, dtype, s); });
       if (e != hipSuccess) return hip_fail(e, "recompute launch");
 
       lce::DhArgs ha{};
       ha.G = G;
       ha.WT = WT;
+      ha.ldG = p.ldG;
+      ha.ldWT = p.ldWT;
       ha.C = p.C;
       ha.Vs = p.Vs;
       ha.d = d;
@@ -324,12 +339,11 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       ha.V = V;
       ha.dH = dH;
       ha.beta = v0 > 0 ? 1 : 0;
-      e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
-      if (e != hipSuccess) return hip_fail(e, "dH launch");
-
       lce::DwArgs wa{};
       wa.GT = GT;
       wa.HT = HT;
+      wa.ldGT = p.ldGT;
+      wa.ldHT = p.ldHT;
       wa.C = p.C;
       wa.Vs = p.Vs;
       wa.d = d;
@@ -341,6 +355,8 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
       e = run(LCE_K_DW, s, [&] { return lce::launch_dw(wa, dtype, s); });
       if (e != hipSuccess) return hip_fail(e, "dW launch");
+      e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
+      if (e != hipSuccess) return hip_fail(e, "dH launch");
     }
   }
   return LCE_OK;

@@ -34,14 +34,16 @@ struct BwdGArgs {
   int64_t N, d, V;
   int64_t c0, C;   // token chunk of the compact index
   int64_t v0, Vs;  // vocabulary block
-  void* G;         // [C][Vs]
-  void* GT;        // [Vs][C]
+  void* G;         // [C][ldG]
+  void* GT;        // [Vs][ldGT]
+  int64_t ldG, ldGT;  // row strides in elements (padded off powers of two)
 };
 
 struct DhArgs {
-  const void* G;   // [C][Vs]
-  const void* WT;  // [d][Vs]
+  const void* G;   // [C][ldG]
+  const void* WT;  // [d][ldWT]
   int64_t C, Vs, d;
+  int64_t ldG, ldWT;
   const int32_t* valid_idx;
   const int32_t* valid_count;
   int64_t c0, v0, V;
@@ -50,9 +52,10 @@ struct DhArgs {
 };
 
 struct DwArgs {
-  const void* GT;  // [Vs][C]
-  const void* HT;  // [d][C]
+  const void* GT;  // [Vs][ldGT]
+  const void* HT;  // [d][ldHT]
   int64_t C, Vs, d;
+  int64_t ldGT, ldHT;
   const int32_t* valid_count;
   int64_t c0, v0, V;
   float* dW;
@@ -66,8 +69,9 @@ struct TransposeArgs {
   int64_t row0;
   const int32_t* count;    // nullable: rows available = *count - row0 (clamped)
   int64_t nrows_static;    // used when count is null: rows available = nrows_static - row0
-  void* dst;               // [K][ncols]
-  int64_t ncols;           // columns of dst (multiple of 64)
+  void* dst;               // [K][ld_dst]
+  int64_t ncols;           // columns of dst written (multiple of 64)
+  int64_t ld_dst;          // row stride of dst in elements
   int64_t K;               // rows of dst = columns read from src (multiple of 64)
   const int32_t* active_count;  // nullable: skip the whole launch when *active_count <= active_c0
   int64_t active_c0;

@@ -40,10 +40,12 @@ hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_
 // ------------------------------------------------------------- transpose
 //
 // dst[k][i] = src[row(row0 + i)][k] for i < rows available, 0 for the rest of
-// the ncols columns.  64 x 64 element tiles through LDS; HBM-bound.
+// the ncols columns.  64 x 64 element tiles through LDS; HBM-bound.  Reads
+// and writes are 16-byte vectors (8 bf16 or 4 fp32 per access).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
-  __shared__ T tile[64][65];
+  constexpr int kV = 16 / sizeof(T);  // elements per 16-byte vector
+  __shared__ T tile[64][64 + kV];
   const int tid = threadIdx.x;
   const int64_t i0 = (int64_t)blockIdx.x * 64;
   const int64_t k0 = (int64_t)blockIdx.y * 64;
@@ -51,30 +53,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   int64_t avail = a.count ? (int64_t)(*a.count) - a.row0 : a.nrows_static - a.row0;
   if (avail < 0) avail = 0;
   if (avail > a.ncols) avail = a.ncols;
-  // read: thread -> (row ii, 16 consecutive k)
-  {
-    const int ii = tid >> 2;
-    const int kk = (tid & 3) * 16;
+  // read: 64 rows x 64 elements = 64 * 64 / kV vectors; thread -> (row, vector)
+  constexpr int kVecPerRow = 64 / kV;
+#pragma unroll
+  for (int it = 0; it < 64 * kVecPerRow / 256; ++it) {
+    const int idx = it * 256 + tid;
+    const int ii = idx / kVecPerRow;
+    const int kk = (idx % kVecPerRow) * kV;
     const int64_t i = i0 + ii;
+    u32x4 v = {0u, 0u, 0u, 0u};
     if (i < avail) {
       const int64_t r = a.row0 + i;
       const int64_t phys = a.gather ? (int64_t)a.gather[r] : r;
-      const T* src = (const T*)a.src + phys * a.ld_src + k0 + kk;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tile[ii][kk + e] = src[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tile[ii][kk + e] = (T)0;
+      v = *(const u32x4*)((const T*)a.src + phys * a.ld_src + k0 + kk);
     }
+    const T* e = (const T*)&v;
+#pragma unroll
+    for (int q = 0; q < kV; ++q) tile[ii][kk + q] = e[q];
   }
   __syncthreads();
-  // write: thread -> (dst row k, 16 consecutive i)
-  {
-    const int kk = tid >> 2;
-    const int ii = (tid & 3) * 16;
-    T* dst = (T*)a.dst + (k0 + kk) * a.ncols + i0 + ii;
+  // write: dst row k, kV consecutive i per vector
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dst[e] = tile[ii + e][kk];
+  for (int it = 0; it < 64 * kVecPerRow / 256; ++it) {
+    const int idx = it * 256 + tid;
+    const int kk = idx / kVecPerRow;
+    const int ii = (idx % kVecPerRow) * kV;
+    u32x4 v;
+    T* e = (T*)&v;
+#pragma unroll
+    for (int q = 0; q < kV; ++q) e[q] = tile[ii + q][kk];
+    *(u32x4*)((T*)a.dst + (k0 + kk) * a.ld_dst + i0 + ii) = v;
   }
 }
 
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      Store2<T>::run(GT + (vl * a.C + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
+      Store2<T>::run(GT + (vl * a.ldGT + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
     }
 
   char* G = (char*)a.G;
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
       const int row = idx >> 5;
       const int q = idx & 31;
       const u32x4 v = *(const u32x4*)(lds + row * 512 + ((q ^ ((row >> 1) & 31)) << 4));
-      *(u32x4*)(G + ((grow0 + row) * a.Vs + gcol0 + 8 * q) * 2) = v;
+      *(u32x4*)(G + ((grow0 + row) * a.ldG + gcol0 + 8 * q) * 2) = v;
     }
   } else {
     // fp32 (small shapes only): direct 16-byte stores
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t vl = vl0 + 32 * mt + 8 * g4 + 4 * h;
-          Store4<T>::run(G + ((int64_t)(il0 + nt) * a.Vs + vl) * Elem<T>::kSize,
+          Store4<T>::run(G + ((int64_t)(il0 + nt) * a.ldG + vl) * Elem<T>::kSize,
                          acc[mt][nt][4 * g4], acc[mt][nt][4 * g4 + 1], acc[mt][nt][4 * g4 + 2],
                          acc[mt][nt][4 * g4 + 3]);
         }
@@ -247,9 +255,7 @@ hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s) {
 // tokens' original positions through valid_idx.  beta = 0 on the first
 // vocabulary block, 1 afterwards.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  __shared__ int rows[kTile];
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, int* rows) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const int TM = (int)((n_act + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
   int tm, tn;
-  if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
+  if (!xcd_tile(slot, TM, TN, 4, 8, tm, tn)) return;
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
 
@@ -273,9 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
     rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
   }
   __syncthreads();
-  const int64_t ld = a.Vs * Elem<T>::kSize;
-  RowSource as{(const char*)a.G, ld, nullptr, (int64_t)tm * kTile, a.C, 0};
-  RowSource bs{(const char*)a.WT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
+  RowSource as{(const char*)a.G, a.ldG * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.C, 0};
+  RowSource bs{(const char*)a.WT, a.ldWT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   Acc acc;
@@ -283,47 +288,33 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: rows[] visible
 
   const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
-  if (a.beta) {
+  // Read-modify-write in four batches (one per mt): all 32 loads of a batch
+  // are in flight together, so the epilogue pays four memory latencies, not
+  // one per element.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt) {
+    float old[16][kNT];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
-        if (r < 0) continue;
-        float* out = a.dH + (int64_t)r * a.d;
+    for (int i = 0; i < 16; ++i) {
+      const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int n = n_base + 32 * nt;
-          if (n < a.d) out[n] += acc[mt][nt][i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int n = n_base + 32 * nt;
+        old[i][nt] = (a.beta && r >= 0 && n < a.d) ? a.dH[(int64_t)r * a.d + n] : 0.f;
       }
-  } else {
+    }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int i = 0; i < 16; ++i) {
+      const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
+      if (r < 0) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
-        if (r < 0) continue;
-        float* out = a.dH + (int64_t)r * a.d;
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int n = n_base + 32 * nt;
-          if (n < a.d) out[n] = acc[mt][nt][i];
-        }
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int n = n_base + 32 * nt;
+        if (n < a.d) a.dH[(int64_t)r * a.d + n] = old[i][nt] + acc[mt][nt][i];
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-}
-
-hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
-  const int TM = (int)(a.C / kTile), TN = (int)((a.d + kTile - 1) / kTile);
-  const int nsb = ((TM + 3) / 4) * ((TN + 7) / 8);
-  const int grid = 256 * ((nsb + 7) / 8);
-  if (dtype == 1)
-    hipLaunchKernelGGL(dh_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------- dW += G^T H
@@ -333,8 +324,7 @@ hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
 // (the count is read on the device).  Each workgroup owns its dW tile, so
 // no atomics are needed and the result is deterministic.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -346,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const int TM = (int)((nv + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
   int tm, tn;
-  if (!xcd_tile(blockIdx.x, TM, TN, 4, 8, tm, tn)) return;
+  if (!xcd_tile(slot, TM, TN, 4, 8, tm, tn)) return;
   const int count = *a.valid_count;
   int64_t kact = (int64_t)count - a.c0;
   if (kact < 0) kact = 0;
@@ -354,9 +344,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const int nstages = (int)((kact + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
   if (nstages == 0 && a.accumulate) return;
 
-  const int64_t ld = a.C * Elem<T>::kSize;
-  RowSource as{(const char*)a.GT, ld, nullptr, (int64_t)tm * kTile, a.Vs, 0};
-  RowSource bs{(const char*)a.HT, ld, nullptr, (int64_t)tn * kTile, a.d, 0};
+  RowSource as{(const char*)a.GT, a.ldGT * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.Vs, 0};
+  RowSource bs{(const char*)a.HT, a.ldHT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   Acc acc;
@@ -366,42 +355,61 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   const int m_base = tm * kTile + wa * kHalf + 4 * h;
   float* out0 = a.dW + a.v0 * a.d;
-  if (a.accumulate) {
+  // read-modify-write (accumulate) in four batches of 32 values, as for dH
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt) {
+    float old[16][kNT];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-        if (ml >= nv) continue;
-        float* out = out0 + (int64_t)ml * a.d;
+    for (int i = 0; i < 16; ++i) {
+      const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int n = n_base + 32 * nt;
-          if (n < a.d) out[n] += acc[mt][nt][i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int n = n_base + 32 * nt;
+        old[i][nt] = (a.accumulate && ml < nv && n < a.d) ? out0[(int64_t)ml * a.d + n] : 0.f;
       }
-  } else {
+    }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int i = 0; i < 16; ++i) {
+      const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+      if (ml >= nv) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-        if (ml >= nv) continue;
-        float* out = out0 + (int64_t)ml * a.d;
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int n = n_base + 32 * nt;
-          if (n < a.d) out[n] = acc[mt][nt][i];
-        }
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int n = n_base + 32 * nt;
+        if (n < a.d) out0[(int64_t)ml * a.d + n] = old[i][nt] + acc[mt][nt][i];
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// ------------------------------------------------------------ launches
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  __shared__ int rows[kTile];
+  dh_tile<T>(a, blockIdx.x, lds, rows);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  dw_tile<T>(a, blockIdx.x, lds);
+}
+
+hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
+  const int TM = (int)(a.C / kTile), TN = (int)((a.d + kTile - 1) / kTile);
+  const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
+  if (dtype == 1)
+    hipLaunchKernelGGL(dh_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s) {
   const int TM = (int)(a.Vs / kTile), TN = (int)((a.d + kTile - 1) / kTile);
-  const int nsb = ((TM + 3) / 4) * ((TN + 7) / 8);
-  const int grid = 256 * ((nsb + 7) / 8);
+  const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
   if (dtype == 1)
     hipLaunchKernelGGL(dw_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
   else
