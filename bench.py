@@ -33,8 +33,68 @@ PEAK_HBM_GBS = 8000.0
 CLASS_FLOPS = {"fwd": 2, "bwd_g": 2, "dh": 2, "dw": 2}
 
 
+KERNEL_SOURCES = ("vocab_cross_entropy_valid_amd/csrc", "vocab_cross_entropy_valid_amd/build.py")
+
+
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources and build flags (identifies the built kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = []
+    for rel in KERNEL_SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.isdir(p):
+            files += sorted(os.path.join(p, f) for f in os.listdir(p)
+                            if f.endswith((".hip", ".h", ".cpp")))
+        else:
+            files.append(p)
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary.
+
+    The summary (profiles/hbm_traffic_<kernel>_kernel_<workload>.md) holds
+    FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same
+    counter reads for a plain copy of known size, and the source digest of
+    the kernels it was taken on.  Returns None when there is no summary or
+    the kernels have changed since.
+    """
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip().lstrip("- ").strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int, dev) -> None:
+    """A plain streaming copy of known size (reads and writes mib MiB), three times."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    _log(f"[bench] copy probe: 3 x {mib} MiB read + {mib} MiB written (elementwise kernel)")
 
 
 def cpu_baseline(H, W, y, target_s: float):
@@ -79,6 +139,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the bare-GEMM reference rate")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this many MiB "
+                         "three times (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -149,13 +212,18 @@ def main():
     if dom in CLASS_FLOPS:
         per_step = CLASS_FLOPS[dom] * n_valid * wl.d * wl.V
         ach = per_step / (kernels[dom]["ms_per_step"] * 1e-3) / 1e12
+        traffic = counter_traffic(dom, wl.name)
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                    "traffic": None if traffic is None else round(traffic),
                     "flops_per_launch": per_step / kernels[dom]["launches_per_step"],
                     "avg_launch_us": round(kernels[dom]["avg_launch_us"], 2)}
     else:
         roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": None, "traffic": None}
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, dev)
 
     gemm = None
     if not args.no_gemm and wl.dtype == "bf16":
@@ -197,7 +265,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic: seeded Gaussian H, W and Zipf labels with padding (no dataset)",
-        "config": {"workload": f"{wl.name} (config {wl.cid})", "N": wl.N, "d": wl.d, "V": wl.V,
+        "config": {"workload": wl.name, "N": wl.N, "d": wl.d, "V": wl.V,
                    "N_valid": n_valid, "ignore_index": -100, "seed": wl.seed},
         "tflops": round(tflops, 2),
         "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -209,14 +209,16 @@ def test_workspace_is_the_only_scratch():
     Ht, Wt, yt = to_dev(H, W, y, "bf16")
     torch.cuda.synchronize()
     ws = torch_api.alloc_workspace(2000, 256, 9000, torch.bfloat16, Ht.device)
+    # requested_bytes counts what was asked for, not the caching allocator's
+    # block sizes (which depend on what earlier tests left in its cache)
     torch.cuda.reset_peak_memory_stats()
-    before = torch.cuda.memory_allocated()
+    before = torch.cuda.memory_stats()["requested_bytes.all.current"]
     fwd = torch_api.forward(Ht, Wt, yt, workspace=ws)
     dH, dW = torch_api.backward(Ht, Wt, yt, fwd, workspace=ws)
     torch.cuda.synchronize()
     outputs = sum(t.numel() * t.element_size() for t in
                   (fwd.loss, fwd.lse, fwd.valid_idx, fwd.valid_count, fwd.loss_sum,
                    fwd.loss_mean, fwd.err_flag, dH, dW))
-    extra = torch.cuda.max_memory_allocated() - before - outputs
-    # only allocator rounding and the 4-byte grad_out scalar remain
-    assert extra <= 64 * 1024, extra
+    extra = torch.cuda.memory_stats()["requested_bytes.all.peak"] - before - outputs
+    # only the 4-byte grad_out scalar remains
+    assert extra <= 1024, extra
