@@ -88,7 +88,7 @@ def test_config1_tiny_fp32():
 @pytest.mark.parametrize("N,d,V,dtype,ign,seed", [
     (600, 256, 3000, "bf16", 0.1, 11),     # ragged N, V (V % 64 != 0)
     (1100, 128, 9000, "bf16", 0.3, 12),    # many vocabulary chunks
-    (300, 64, 20000, "bf16", 0.1, 13),     # several backward vocabulary blocks
+    (300, 64, 40000, "bf16", 0.1, 13),     # several backward vocabulary blocks
     (333, 64, 1500, "f32", 0.2, 14),       # fp32, ragged everywhere
     (257, 192, 257, "bf16", 0.0, 15),      # one past a tile in N and V
     (9000, 64, 700, "bf16", 0.05, 16),     # several backward token chunks

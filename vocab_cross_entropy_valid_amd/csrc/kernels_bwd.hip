@@ -279,7 +279,9 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
     rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
   }
   __syncthreads();
-  RowSource as{(const char*)a.G, a.ldG * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.C, 0};
+  // rows past the valid count clamp to the last valid row (cache hits)
+  // instead of streaming the block's unused rows
+  RowSource as{(const char*)a.G, a.ldG * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, n_act, 0};
   RowSource bs{(const char*)a.WT, a.ldWT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
