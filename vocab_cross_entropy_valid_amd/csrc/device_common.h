@@ -213,24 +213,58 @@ __device__ __forceinline__ void mma_step(Acc& acc, const u32x4 (&fa)[4], const u
     for (int nt = 0; nt < kNT; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
 }
 
+// Instruction order of MFMA step s (bf16).  Left alone, the compiler
+// funnels every A fragment through one register quad and waits on each LDS
+// read right before its two MFMAs.  Instead: each step's fragments live in
+// their own registers, the 6 fragment reads of step s + 1 alternate with the
+// MFMAs of step s, and in step 0 the 8 direct-to-LDS loads of the next stage
+// go out among the first MFMAs (sched_group_barrier masks: 0x008 MFMA,
+// 0x020 VMEM read, 0x100 DS read).
+template <bool kLoad>
+__device__ __forceinline__ void schedule_step(int s) {
+  if (s == 0 && kLoad) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  } else if (s < 3) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+}
+
 // One pipeline stage: 4 MFMA steps on the current LDS buffer; the fragment
 // reads of step s + 1 and (kLoad) the direct-to-LDS loads of the next stage
-// are issued before the MFMAs of step s.
+// are issued among the MFMAs of step s.
 template <typename T, bool kLoad>
 __device__ __forceinline__ void compute_stage(Acc& acc, const char* stage, int a_base, int b_base,
                                               char* nxt, const RowPtrs& pa, const RowPtrs& pb,
                                               uint32_t kbyte, int wave_u) {
-  u32x4 fa[2][4], fb[2][kNT];
+  u32x4 fa[4][4], fb[4][kNT];
   load_frags(fa[0], stage, a_base, 0);
   load_frags_b(fb[0], stage + kOpBytes, b_base, 0);
   if (kLoad) load_stage(nxt, pa, pb, kbyte, wave_u);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < 3) {
-      load_frags(fa[(s + 1) & 1], stage, a_base, s + 1);
-      load_frags_b(fb[(s + 1) & 1], stage + kOpBytes, b_base, s + 1);
+      load_frags(fa[s + 1], stage, a_base, s + 1);
+      load_frags_b(fb[s + 1], stage + kOpBytes, b_base, s + 1);
     }
-    mma_step<T>(acc, fa[s & 1], fb[s & 1]);
+    mma_step<T>(acc, fa[s], fb[s]);
+    if constexpr (sizeof(T) == 2) schedule_step<kLoad>(s);
   }
 }
 

@@ -388,9 +388,11 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  __shared__ int rows[kTile];
-  dh_tile<T>(a, blockIdx.x, lds, rows);
+  // One LDS object only: with a second __shared__ array the compiler can no
+  // longer tell the direct-to-LDS loads of the next stage from the fragment
+  // reads of the current one and waits for every load right after issuing it.
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds + kTile * sizeof(int)];
+  dh_tile<T>(a, blockIdx.x, lds, (int*)(lds + kMainLds));
 }
 
 template <typename T>
