@@ -213,61 +213,6 @@ __device__ __forceinline__ void mma_step(Acc& acc, const u32x4 (&fa)[4], const u
     for (int nt = 0; nt < kNT; ++nt) Mma<T>::run(acc[mt][nt], fa[mt], fb[nt]);
 }
 
-// Instruction order of MFMA step s (bf16).  Left alone, the compiler
-// funnels every A fragment through one register quad and waits on each LDS
-// read right before its two MFMAs.  Instead: each step's fragments live in
-// their own registers, the 6 fragment reads of step s + 1 alternate with the
-// MFMAs of step s, and in step 0 the 8 direct-to-LDS loads of the next stage
-// go out among the first MFMAs (sched_group_barrier masks: 0x008 MFMA,
-// 0x020 VMEM read, 0x100 DS read).
-template <bool kLoad>
-__device__ __forceinline__ void schedule_step(int s) {
-  if (s == 0 && kLoad) {
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  } else if (s < 3) {
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  } else {
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  }
-}
-
-// One pipeline stage: 4 MFMA steps on the current LDS buffer; the fragment
-// reads of step s + 1 and (kLoad) the direct-to-LDS loads of the next stage
-// are issued among the MFMAs of step s.
-template <typename T, bool kLoad>
-__device__ __forceinline__ void compute_stage(Acc& acc, const char* stage, int a_base, int b_base,
-                                              char* nxt, const RowPtrs& pa, const RowPtrs& pb,
-                                              uint32_t kbyte, int wave_u) {
-  u32x4 fa[4][4], fb[4][kNT];
-  load_frags(fa[0], stage, a_base, 0);
-  load_frags_b(fb[0], stage + kOpBytes, b_base, 0);
-  if (kLoad) load_stage(nxt, pa, pb, kbyte, wave_u);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) {
-      load_frags(fa[s + 1], stage, a_base, s + 1);
-      load_frags_b(fb[s + 1], stage + kOpBytes, b_base, s + 1);
-    }
-    mma_step<T>(acc, fa[s], fb[s]);
-    if constexpr (sizeof(T) == 2) schedule_step<kLoad>(s);
-  }
-}
-
 __device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -275,6 +220,74 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
+}
+
+// Instruction order of one stage body (bf16; sched_group_barrier masks:
+// 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).  Left alone, the compiler
+// funnels every A fragment through one register quad and waits on each LDS
+// read right in front of its two MFMAs.  Here: the 6 fragment reads of step
+// 0 go first; the previous stage's step-3 MFMAs (kPrev) cover their latency
+// and carry the 8 direct-to-LDS loads of the next stage (kLoad); then each
+// step's 8 MFMAs alternate with the 6 fragment reads of the following step.
+template <bool kPrev, bool kLoad>
+__device__ __forceinline__ void schedule_body() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  if (kPrev && kLoad) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  } else if (kPrev) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  } else if (kLoad) {
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// Stage k of the main loop, software-pipelined across the barrier: MFMA
+// steps 0-2 of stage k run here, while step 3's fragments are read into f3a /
+// f3b and their MFMAs run at the start of the next body (kPrev), after the
+// barrier, where they hide the barrier skew and the next stage's first LDS
+// reads.  The loads of stage k + 1 (kLoad) target the buffer whose last
+// reads (step 3 of stage k - 1) completed before the previous barrier.  Ends
+// with a barrier when it loaded (stage k + 1 landed, stage k fully read).
+template <typename T, bool kPrev, bool kLoad>
+__device__ __forceinline__ void stage_body(Acc& acc, char* lds, int k, int a_base, int b_base,
+                                           const RowPtrs& pa, const RowPtrs& pb, int wave_u,
+                                           u32x4 (&f3a)[4], u32x4 (&f3b)[kNT]) {
+  const char* cur = lds + (k & 1) * kStageBytes;
+  u32x4 fa[3][4], fb[3][kNT];
+  load_frags(fa[0], cur, a_base, 0);
+  load_frags_b(fb[0], cur + kOpBytes, b_base, 0);
+  if (kLoad)
+    load_stage(lds + ((k + 1) & 1) * kStageBytes, pa, pb, (uint32_t)((k + 1) * kRowBytes), wave_u);
+  if (kPrev) mma_step<T>(acc, f3a, f3b);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s < 2) {
+      load_frags(fa[s + 1], cur, a_base, s + 1);
+      load_frags_b(fb[s + 1], cur + kOpBytes, b_base, s + 1);
+    } else {
+      load_frags(f3a, cur, a_base, 3);
+      load_frags_b(f3b, cur + kOpBytes, b_base, 3);
+    }
+    mma_step<T>(acc, fa[s], fb[s]);
+  }
+  if constexpr (sizeof(T) == 2) schedule_body<kPrev, kLoad>();
+  if (kLoad) {
+    wait_vmem();
+    __syncthreads();
+  }
 }
 
 // acc += A_tile(256 x K) * B_tile(256 x K)^T over nstages stages of 128 bytes.
@@ -295,16 +308,16 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, char* lds, const RowPtrs
   load_stage(lds, pa, pb, 0, wave_u);
   wait_vmem();
   __syncthreads();
-  for (int k = 0; k + 1 < nstages; ++k) {
-    const char* cur = lds + (k & 1) * kStageBytes;
-    char* nxt = lds + ((k + 1) & 1) * kStageBytes;
-    compute_stage<T, true>(acc, cur, a_base, b_base, nxt, pa, pb, (uint32_t)((k + 1) * kRowBytes),
-                           wave_u);
-    wait_vmem();
-    __syncthreads();
+  u32x4 f3a[4], f3b[kNT];
+  if (nstages == 1) {
+    stage_body<T, false, false>(acc, lds, 0, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+  } else {
+    stage_body<T, false, true>(acc, lds, 0, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+    for (int k = 1; k + 1 < nstages; ++k)
+      stage_body<T, true, true>(acc, lds, k, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+    stage_body<T, true, false>(acc, lds, nstages - 1, a_base, b_base, pa, pb, wave_u, f3a, f3b);
   }
-  compute_stage<T, false>(acc, lds + ((nstages - 1) & 1) * kStageBytes, a_base, b_base, nullptr,
-                          pa, pb, 0, wave_u);
+  mma_step<T>(acc, f3a, f3b);
   __syncthreads();
 }
 
