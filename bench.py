@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the bare-GEMM reference rate")
+    ap.add_argument("--shards", type=int, default=1,
+                    help="split the vocabulary into this many contiguous shards: each step runs "
+                         "the shard forwards, the merge and the shard backwards")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -174,6 +177,31 @@ def main():
         fwd = torch_api.forward(Ht, Wt, yt, workspace=ws, check=False)
         torch_api.backward(Ht, Wt, yt, fwd, grad_out=g, dH=dH, dW=dW, workspace=ws)
         return fwd
+
+    if args.shards > 1:
+        # contiguous shards of (nearly) equal size; W slices are views of one table
+        K = args.shards
+        edges = [round(k * wl.V / K) for k in range(K + 1)]
+        shards = [(edges[k], edges[k + 1]) for k in range(K)]
+        Wsh = [Wt[a:b] for a, b in shards]
+        dWsh = [dW[a:b] for a, b in shards]
+        wss = torch_api.alloc_workspace(wl.N, wl.d, max(b - a for a, b in shards), dt, dev)
+        pm = torch.empty(K, wl.N, dtype=torch.float32, device=dev)
+        ps, pt = torch.empty_like(pm), torch.empty_like(pm)
+        vidx = torch.empty(wl.N, dtype=torch.int32, device=dev)
+        vcnt = torch.empty(1, dtype=torch.int32, device=dev)
+        errf = torch.empty(1, dtype=torch.int32, device=dev)
+        parts = [torch_api.ShardPartials(pm[k], ps[k], pt[k], vidx, vcnt, errf)
+                 for k in range(K)]
+
+        def step():  # noqa: F811
+            for k, (a, b) in enumerate(shards):
+                torch_api.forward_shard(Ht, Wsh[k], yt, wl.V, a, workspace=wss, out=parts[k])
+            fwd = torch_api.lse_merge(pm, ps, pt, vidx, vcnt)
+            for k, (a, b) in enumerate(shards):
+                torch_api.backward_shard(Ht, Wsh[k], yt, wl.V, a, fwd, dH, accumulate_dH=k > 0,
+                                         grad_out=g, dW_shard=dWsh[k], workspace=wss)
+            return fwd
 
     _log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -265,7 +293,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic: seeded Gaussian H, W and Zipf labels with padding (no dataset)",
-        "config": {"workload": wl.name, "N": wl.N, "d": wl.d, "V": wl.V,
+        "config": {"workload": wl.name + (f" in {args.shards} vocabulary shards"
+                                          if args.shards > 1 else ""), "N": wl.N, "d": wl.d, "V": wl.V,
                    "N_valid": n_valid, "ignore_index": -100, "seed": wl.seed},
         "tflops": round(tflops, 2),
         "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

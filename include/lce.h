@@ -112,6 +112,61 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
                         int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------- vocabulary shards
+ *
+ * The vocabulary [0, V_total) split into contiguous shards, each with its own
+ * rows of W ("MaximusLLM" page, section 2.1: the vocabulary table cut into
+ * contiguous sub-tables).  Shard k covers [v_begin, v_begin + V_shard) and
+ * W_shard [V_shard, d] holds exactly those rows.  The shards' forward
+ * partials merge with the online-softmax rescale step ("OjasX 0.6.1", Online
+ * Softmax paragraph) into the same loss and lse as lce_forward over the
+ * whole table; each shard's backward gives its own dW rows and a share of dH.
+ * This is the single-device half of splitting the vocabulary across GPUs
+ * (between GPUs the partials travel through one all-reduce, and the dH shares
+ * through a reduce-scatter).  Workspace: lce_workspace_bytes(N, d, V_shard,
+ * dtype).  Labels are global ids in [0, V_total).
+ */
+
+/* Forward of one shard.  Per row n (f32 [N] each, original row order):
+ *  part_max[n]     largest logit of the row over the shard
+ *  part_sum[n]     sum over the shard of exp(logit - part_max[n])  (>= 1)
+ *  part_target[n]  the target logit if labels[n] lies in the shard, else -inf
+ * Ignored rows: part_max = part_sum = 0, part_target unspecified.
+ * valid_idx, valid_count and err_flag as in lce_forward (identical for every
+ * shard; the label range check is against V_total).  Returns
+ * LCE_ERR_INVALID_ARG when the shard does not lie in [0, V_total).
+ */
+lce_status lce_forward_shard(const void* H, const void* W_shard, const int64_t* labels,
+                             int64_t ignore_index, int64_t N, int64_t d, int64_t V_total,
+                             int64_t v_begin, int64_t V_shard, int dtype, float* part_max,
+                             float* part_sum, float* part_target, int32_t* valid_idx,
+                             int32_t* valid_count, int32_t* err_flag, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Merges the partials of n_shards shards that together cover [0, V_total)
+ * exactly once; shard k's three arrays start at part_* + k * shard_stride
+ * (elements, >= N when n_shards > 1).  Writes loss, lse (f32 [N], ignored rows
+ * 0), loss_sum (f64, fixed-order sum over valid rows) and loss_mean (nullable;
+ * NaN when no row is valid), as lce_forward does.  No workspace.
+ */
+lce_status lce_lse_merge(const float* part_max, const float* part_sum, const float* part_target,
+                         int64_t n_shards, int64_t shard_stride, int64_t N,
+                         const int32_t* valid_idx, const int32_t* valid_count, float* loss,
+                         float* lse, double* loss_sum, float* loss_mean, void* stream);
+
+/* Backward of one shard, given the merged lse.  dW_shard [V_shard, d] f32 as
+ * dW in lce_backward.  dH receives this shard's share: overwritten (ignored
+ * rows set to 0) when accumulate_dH == 0, added to otherwise; summing the
+ * shares of every shard gives lce_backward's dH.
+ */
+lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t* labels,
+                              int64_t ignore_index, const float* lse, const int32_t* valid_idx,
+                              const int32_t* valid_count, int64_t N, int64_t d, int64_t V_total,
+                              int64_t v_begin, int64_t V_shard, int dtype, const float* grad_out,
+                              int reduction, float* dH, int accumulate_dH, float* dW_shard,
+                              int accumulate_dW, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Synchronises `stream` and returns LCE_ERR_LABEL_RANGE when *err_flag is set
  * (a valid label outside [0, V) -- the out-of-range index failure described
  * in "6GB显卡预训练11亿参数模型", section 可证伪测试抓到的8个静默bug, #155),

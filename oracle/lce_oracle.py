@@ -213,3 +213,103 @@ def rows_dW(H, W, labels, valid_idx, lse_valid, vocab_rows, w: float,
         G = (P - onehot) * w
         out += G.T @ Hb
     return out
+
+
+# --------------------------------------------------------------------------
+# vocabulary shards
+# --------------------------------------------------------------------------
+#
+# The vocabulary [0, V_total) cut into contiguous slices, each with its own
+# rows of W (MaximusLLM page, section 2.1: the table split into contiguous
+# sub-tables).  A shard's share of the online-softmax state (OjasX page, Online
+# Softmax paragraph) is, per valid row,
+#
+#     m = max_{v in shard} z[n, v]
+#     s = sum_{v in shard} exp(z[n, v] - m)
+#     t = z[n, y[n]] if y[n] lies in the shard, else -inf
+#
+# and the shards combine with the same rescale step the recurrence uses:
+#
+#     M = max_k m_k,  S = sum_k s_k exp(m_k - M),  lse = M + log S,
+#     loss = lse - (the one finite t_k).
+
+
+@dataclasses.dataclass
+class ShardPartials:
+    part_max: np.ndarray     # float64 [N], 0 on ignored rows
+    part_sum: np.ndarray     # float64 [N], 0 on ignored rows
+    part_target: np.ndarray  # float64 [N], -inf off the shard and on ignored rows
+
+
+def shard_partials(H, W_shard, labels, v_begin: int, V_total: int, ignore_index: int = -100,
+                   *, bad_labels: str = "raise",
+                   row_block: int = DEFAULT_ROW_BLOCK) -> ShardPartials:
+    """(m, s, t) of the vocabulary slice [v_begin, v_begin + len(W_shard))."""
+    H = np.asarray(H)
+    labels = np.asarray(labels, dtype=np.int64)
+    N = H.shape[0]
+    Vs = np.asarray(W_shard).shape[0]
+    idx, n_valid = _checked_index(labels, ignore_index, V_total, bad_labels)
+    W64 = np.asarray(W_shard, dtype=np.float64)
+    m = np.zeros(N)
+    s = np.zeros(N)
+    t = np.full(N, -np.inf)
+    for b in range(0, n_valid, row_block):
+        rows = idx[b:b + row_block]
+        Z = logits(H[rows], W64)
+        mb = Z.max(axis=1)
+        m[rows] = mb
+        s[rows] = np.exp(Z - mb[:, None]).sum(axis=1)
+        yl = labels[rows] - v_begin
+        inside = np.flatnonzero((yl >= 0) & (yl < Vs))
+        t[rows[inside]] = Z[inside, yl[inside]]
+    return ShardPartials(m, s, t)
+
+
+def merge_partials(parts, valid_idx):
+    """(loss, lse, loss_sum, loss_mean) from the partials of shards that
+    cover the vocabulary exactly once."""
+    valid_idx = np.asarray(valid_idx)
+    N = parts[0].part_max.shape[0]
+    loss = np.zeros(N)
+    lse = np.zeros(N)
+    if valid_idx.size:
+        Mk = np.stack([p.part_max[valid_idx] for p in parts])
+        Sk = np.stack([p.part_sum[valid_idx] for p in parts])
+        Tk = np.stack([p.part_target[valid_idx] for p in parts])
+        M = Mk.max(axis=0)
+        S = (Sk * np.exp(Mk - M[None, :])).sum(axis=0)
+        lse[valid_idx] = M + np.log(S)
+        loss[valid_idx] = lse[valid_idx] - Tk.max(axis=0)
+    loss_sum = float(loss[valid_idx].sum()) if valid_idx.size else 0.0
+    mean = loss_sum / valid_idx.size if valid_idx.size else float("nan")
+    return loss, lse, loss_sum, mean
+
+
+def shard_backward(H, W_shard, labels, lse, v_begin: int, V_total: int,
+                   ignore_index: int = -100, *, grad: float = 1.0, reduction: str = "mean",
+                   bad_labels: str = "raise", row_block: int = DEFAULT_ROW_BLOCK):
+    """(dH share float64 [N, d], dW_shard float64 [V_shard, d]) for the
+    shard's columns of G, given the global lse of every row."""
+    H = np.asarray(H)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, d = H.shape
+    Vs = np.asarray(W_shard).shape[0]
+    idx, n_valid = _checked_index(labels, ignore_index, V_total, bad_labels)
+    w = _scale(reduction, grad, n_valid)
+    W64 = np.asarray(W_shard, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    dH = np.zeros((N, d))
+    dW = np.zeros((Vs, d))
+    for b in range(0, n_valid, row_block):
+        rows = idx[b:b + row_block]
+        Hb = np.asarray(H[rows], dtype=np.float64)
+        Z = logits(Hb, W64)
+        G = np.exp(Z - lse[rows][:, None])
+        yl = labels[rows] - v_begin
+        inside = np.flatnonzero((yl >= 0) & (yl < Vs))
+        G[inside, yl[inside]] -= 1.0
+        G *= w
+        dH[rows] = G @ W64
+        dW += G.T @ Hb
+    return dH, dW

@@ -302,11 +302,69 @@ def pin_compaction(o):
     assert bad.tolist() == exp_bad
 
 
+# ------------------------------------------------------- vocabulary shards
+
+_PARTITIONS = ([(0, 11)], [(0, 3), (3, 4), (4, 11)], [(0, 5), (5, 11)],
+               [(v, v + 1) for v in range(11)])
+
+
+def pin_shard_merge_identity(o):
+    """logsumexp over a union of disjoint slices equals the logsumexp of the
+    slices' own (max, scaled sum) pairs: merging the partials of any
+    partition of the vocabulary, in any shard order, reproduces the full
+    forward (which the pins above tie to mpmath and PyTorch)."""
+    H, W, y = _case(17, N=13, d=5, V=11, n_ign=3)
+    f = o.forward(H, W, y, IGN)
+    for part in _PARTITIONS:
+        parts = [o.shard_partials(H, W[a:b], y, a, 11, IGN) for a, b in part]
+        for order in (parts, parts[::-1]):
+            loss, lse, loss_sum, mean = o.merge_partials(order, f.valid_idx)
+            np.testing.assert_allclose(lse, f.lse, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(loss, f.loss, rtol=1e-12, atol=1e-12)
+            assert abs(loss_sum - f.loss_sum) <= 1e-12 * abs(f.loss_sum)
+
+
+def pin_shard_partials_definition(o):
+    """One shard holding the whole vocabulary: m + log s is the row's lse, t
+    its target logit, s >= 1 on valid rows and 0 on ignored ones; a shard that
+    does not hold the label reports -inf."""
+    H, W, y = _case(18, N=12, d=4, V=9, n_ign=3)
+    f = o.forward(H, W, y, IGN)
+    p = o.shard_partials(H, W, y, 0, 9, IGN)
+    v = f.valid_idx
+    ign = np.setdiff1d(np.arange(12), v)
+    np.testing.assert_allclose(p.part_max[v] + np.log(p.part_sum[v]), f.lse[v], rtol=1e-14)
+    _, _, zt = o.rows_forward(H, W, y, v)
+    np.testing.assert_allclose(p.part_target[v], zt, rtol=1e-14)
+    assert np.all(p.part_sum[v] >= 1.0) and np.all(p.part_sum[ign] == 0.0)
+    lo = o.shard_partials(H, W[:4], y, 0, 9, IGN)
+    assert np.all(np.isneginf(lo.part_target[v[y[v] >= 4]]))
+    assert np.all(np.isfinite(lo.part_target[v[y[v] < 4]]))
+
+
+def pin_shard_backward_sum(o):
+    """The shards' dH shares sum to the full dH and their dW rows stack to
+    the full dW (G restricted to a shard's columns, with the global lse)."""
+    H, W, y = _case(19, N=10, d=5, V=11, n_ign=2)
+    f = o.forward(H, W, y, IGN)
+    dH, dW = o.backward(H, W, y, IGN, grad=1.7)
+    for part in _PARTITIONS[1:3]:
+        sH = np.zeros_like(dH)
+        rows = []
+        for a, b in part:
+            h, w_ = o.shard_backward(H, W[a:b], y, f.lse, a, 11, IGN, grad=1.7)
+            sH += h
+            rows.append(w_)
+        np.testing.assert_allclose(sH, dH, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(np.concatenate(rows), dW, rtol=1e-12, atol=1e-15)
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
     pin_ignore_inside_range, pin_bad_label, pin_finite_differences,
     pin_mpmath, pin_torch_cross_entropy, pin_row_functions, pin_compaction,
+    pin_shard_merge_identity, pin_shard_partials_definition, pin_shard_backward_sum,
 ]
 
 

@@ -124,3 +124,34 @@ def test_gemm_and_timing_argument_checks():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+@pytest.mark.parametrize("V_total,v_begin,V_shard", [
+    (100, -1, 10), (100, 95, 10), (100, 0, 0), (0, 0, 10), (1 << 31, 0, 10),
+])
+def test_shard_entry_points_reject_bad_ranges_before_launch(V_total, v_begin, V_shard):
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    r = lib.lce_forward_shard(fake, fake, fake, -100, 10, 64, V_total, v_begin, V_shard, 1,
+                              fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert r == _lib.LCE_ERR_INVALID_ARG, r
+    r = lib.lce_backward_shard(fake, fake, fake, -100, fake, fake, fake, 10, 64, V_total,
+                               v_begin, V_shard, 1, fake, 0, fake, 0, fake, 0, fake, 1 << 40,
+                               None)
+    assert r == _lib.LCE_ERR_INVALID_ARG, r
+
+
+def test_shard_workspace_and_merge_argument_checks():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    need = _lib.lce_workspace_bytes(10, 64, 30, 1)
+    r = lib.lce_forward_shard(fake, fake, fake, -100, 10, 64, 100, 40, 30, 1, fake, fake, fake,
+                              fake, fake, fake, fake, need - 1, None)
+    assert r == _lib.LCE_ERR_WORKSPACE
+    # no shards, a stride shorter than N, missing outputs
+    assert lib.lce_lse_merge(fake, fake, fake, 0, 10, 10, fake, fake, fake, fake, fake, None,
+                             None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_lse_merge(fake, fake, fake, 2, 9, 10, fake, fake, fake, fake, fake, None,
+                             None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_lse_merge(fake, fake, fake, 2, 10, 10, fake, fake, None, fake, fake, None,
+                             None) == _lib.LCE_ERR_INVALID_ARG

@@ -72,7 +72,40 @@ def _softmax_wrong_axis(Z, lse, y, w):
     return P_ * w
 
 
+_orig_shard_partials = O.shard_partials
+_orig_shard_backward = O.shard_backward
+
+
+def _merge_without_rescale(parts, valid_idx):
+    # sums the shards' s without bringing them to a common max
+    N = parts[0].part_max.shape[0]
+    loss = np.zeros(N)
+    lse = np.zeros(N)
+    v = np.asarray(valid_idx)
+    M = np.stack([p.part_max[v] for p in parts]).max(axis=0)
+    S = np.stack([p.part_sum[v] for p in parts]).sum(axis=0)
+    lse[v] = M + np.log(S)
+    loss[v] = lse[v] - np.stack([p.part_target[v] for p in parts]).max(axis=0)
+    s = float(loss[v].sum())
+    return loss, lse, s, s / max(v.size, 1)
+
+
+def _shard_label_not_offset(H, W_shard, labels, v_begin, V_total, ignore_index=-100, **kw):
+    # forgets that a shard's row 0 is vocabulary entry v_begin
+    return _orig_shard_partials(H, W_shard, labels, 0, V_total, ignore_index, **kw)
+
+
+def _shard_backward_local_lse(H, W_shard, labels, lse, v_begin, V_total, ignore_index=-100, **kw):
+    # normalises by the shard's own logsumexp instead of the global one
+    p = _orig_shard_partials(H, W_shard, labels, v_begin, V_total, ignore_index)
+    local = np.where(p.part_sum > 0, p.part_max + np.log(np.maximum(p.part_sum, 1e-300)), 0.0)
+    return _orig_shard_backward(H, W_shard, labels, local, v_begin, V_total, ignore_index, **kw)
+
+
 MUTATIONS = {
+    "shard_merge_without_rescale": ("merge_partials", _merge_without_rescale),
+    "shard_label_not_offset": ("shard_partials", _shard_label_not_offset),
+    "shard_backward_local_lse": ("shard_backward", _shard_backward_local_lse),
     "dlogits_without_onehot": ("dlogits", _no_onehot),
     "dlogits_wrong_sign": ("dlogits", _wrong_sign),
     "dlogits_missing_scale": ("dlogits", _unscaled),

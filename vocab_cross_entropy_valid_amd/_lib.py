@@ -40,6 +40,11 @@ SIGNATURES = {
                            _P, _P, _SZ, _P]),
     "lce_backward": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
                             _P, _P, _INT, _P, _SZ, _P]),
+    "lce_forward_shard": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _INT, _P, _P, _P,
+                                 _P, _P, _P, _P, _SZ, _P]),
+    "lce_lse_merge": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "lce_backward_shard": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _INT,
+                                  _P, _INT, _P, _INT, _P, _INT, _P, _SZ, _P]),
     "lce_check_error": (_INT, [_P, _P]),
     "lce_status_string": (ctypes.c_char_p, [_INT]),
     "lce_last_error": (ctypes.c_char_p, []),
@@ -108,6 +113,32 @@ def lce_backward(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, 
     _check(load().lce_backward(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d,
                                V, dtype, grad_out, reduction, dH, dW, accumulate_dW,
                                workspace, workspace_bytes, stream), "lce_backward")
+
+
+def lce_forward_shard(H, W_shard, labels, ignore_index, N, d, V_total, v_begin, V_shard, dtype,
+                      part_max, part_sum, part_target, valid_idx, valid_count, err_flag,
+                      workspace, workspace_bytes, stream) -> None:
+    _check(load().lce_forward_shard(H, W_shard, labels, ignore_index, N, d, V_total, v_begin,
+                                    V_shard, dtype, part_max, part_sum, part_target, valid_idx,
+                                    valid_count, err_flag, workspace, workspace_bytes, stream),
+           "lce_forward_shard")
+
+
+def lce_lse_merge(part_max, part_sum, part_target, n_shards, shard_stride, N, valid_idx,
+                  valid_count, loss, lse, loss_sum, loss_mean, stream) -> None:
+    _check(load().lce_lse_merge(part_max, part_sum, part_target, n_shards, shard_stride, N,
+                                valid_idx, valid_count, loss, lse, loss_sum, loss_mean, stream),
+           "lce_lse_merge")
+
+
+def lce_backward_shard(H, W_shard, labels, ignore_index, lse, valid_idx, valid_count, N, d,
+                       V_total, v_begin, V_shard, dtype, grad_out, reduction, dH, accumulate_dH,
+                       dW_shard, accumulate_dW, workspace, workspace_bytes, stream) -> None:
+    _check(load().lce_backward_shard(H, W_shard, labels, ignore_index, lse, valid_idx,
+                                     valid_count, N, d, V_total, v_begin, V_shard, dtype,
+                                     grad_out, reduction, dH, accumulate_dH, dW_shard,
+                                     accumulate_dW, workspace, workspace_bytes, stream),
+           "lce_backward_shard")
 
 
 def lce_check_error(err_flag, stream) -> None:

@@ -186,27 +186,29 @@ size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype) {
   return make_plan(N, d, V, dtype).total;
 }
 
-lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
-                       int64_t N, int64_t d, int64_t V, int dtype, float* loss, float* lse,
-                       int32_t* valid_idx, int32_t* valid_count, double* loss_sum,
-                       float* loss_mean, int32_t* err_flag, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  lce_status st = check_sizes(N, d, V, dtype);
-  if (st != LCE_OK) return st;
-  if (!W || !valid_count || !loss_sum || !err_flag)
-    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, loss_sum and err_flag must not be NULL");
-  if (N > 0 && (!H || !labels || !loss || !lse || !valid_idx))
-    return fail(LCE_ERR_INVALID_ARG, "H, labels, loss, lse and valid_idx must not be NULL");
-  const Plan p = make_plan(N, d, V, dtype);
-  st = check_workspace(p, workspace, workspace_bytes);
-  if (st != LCE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
+}  // extern "C"
 
+namespace {
+
+// Forward over vocabulary rows [y_off, y_off + V) held by W (the whole
+// vocabulary when y_off = 0 and V = V_total).  With part_max set, writes the
+// shard partials instead of loss / lse and skips the reduction.
+lce_status forward_impl(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                        int64_t N, int64_t d, int64_t V_total, int64_t y_off, int64_t V, int dtype,
+                        float* loss, float* lse, float* part_max, float* part_sum,
+                        float* part_target, int32_t* valid_idx, int32_t* valid_count,
+                        double* loss_sum, float* loss_mean, int32_t* err_flag, void* workspace,
+                        size_t workspace_bytes, hipStream_t s) {
+  const Plan p = make_plan(N, d, V, dtype);
+  lce_status st = check_workspace(p, workspace, workspace_bytes);
+  if (st != LCE_OK) return st;
+  char* ws = (char*)workspace;
+  const bool shard = part_max != nullptr;
+
+  // ignored rows: loss = lse = 0, or part_max = part_sum = 0 for a shard
   hipError_t e = run(LCE_K_COMPACT, s, [&] {
-    return lce::launch_compact(labels, N, ignore_index, V, valid_idx, valid_count, err_flag, loss,
-                               lse, s);
+    return lce::launch_compact(labels, N, ignore_index, V_total, valid_idx, valid_count, err_flag,
+                               shard ? part_max : loss, shard ? part_sum : lse, s);
   });
   if (e != hipSuccess) return hip_fail(e, "compaction launch");
 
@@ -219,6 +221,7 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
   fa.N = N;
   fa.d = d;
   fa.V = V;
+  fa.y_off = y_off;
   fa.n_vtiles = p.n_vtiles;
   fa.tpc = p.tpc;
   fa.J = p.J;
@@ -230,43 +233,127 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
   if (N > 0) {
     e = run(LCE_K_FWD, s, [&] { return lce::launch_fwd(fa, dtype, grid_persistent(), s); });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
-    e = run(LCE_K_MERGE, s, [&] { return lce::launch_fwd_merge(fa, loss, lse, loss_c, N, s); });
+    e = run(LCE_K_MERGE, s, [&] {
+      return shard ? lce::launch_fwd_part(fa, part_max, part_sum, part_target, N, s)
+                   : lce::launch_fwd_merge(fa, loss, lse, loss_c, N, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
-  e = run(LCE_K_REDUCE, s,
-          [&] { return lce::launch_loss_reduce(loss_c, valid_count, loss_sum, loss_mean, s); });
+  if (shard) return LCE_OK;
+  e = run(LCE_K_REDUCE, s, [&] {
+    return lce::launch_loss_reduce(loss_c, nullptr, valid_count, loss_sum, loss_mean, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "reduction launch");
   return LCE_OK;
 }
 
-lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
-                        const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
-                        int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
-                        int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+lce_status check_shard(int64_t V_total, int64_t v_begin, int64_t V_shard) {
+  if (V_total <= 0 || V_total >= ((int64_t)1 << 31))
+    return fail(LCE_ERR_INVALID_ARG, "V_total must be in [1, 2^31)");
+  if (v_begin < 0 || V_shard <= 0 || v_begin + V_shard > V_total)
+    return fail(LCE_ERR_INVALID_ARG, "the shard [v_begin, v_begin + V_shard) must lie in [0, V_total)");
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                       int64_t N, int64_t d, int64_t V, int dtype, float* loss, float* lse,
+                       int32_t* valid_idx, int32_t* valid_count, double* loss_sum,
+                       float* loss_mean, int32_t* err_flag, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   g_err.clear();
   lce_status st = check_sizes(N, d, V, dtype);
   if (st != LCE_OK) return st;
-  if (reduction != LCE_MEAN && reduction != LCE_SUM)
-    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
-  if (!W || !valid_count || !grad_out || !dW)
-    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and dW must not be NULL");
-  if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
-    return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
-  const Plan p = make_plan(N, d, V, dtype);
-  st = check_workspace(p, workspace, workspace_bytes);
+  if (!W || !valid_count || !loss_sum || !err_flag)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, loss_sum and err_flag must not be NULL");
+  if (N > 0 && (!H || !labels || !loss || !lse || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, loss, lse and valid_idx must not be NULL");
+  return forward_impl(H, W, labels, ignore_index, N, d, V, 0, V, dtype, loss, lse, nullptr,
+                      nullptr, nullptr, valid_idx, valid_count, loss_sum, loss_mean, err_flag,
+                      workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_forward_shard(const void* H, const void* W_shard, const int64_t* labels,
+                             int64_t ignore_index, int64_t N, int64_t d, int64_t V_total,
+                             int64_t v_begin, int64_t V_shard, int dtype, float* part_max,
+                             float* part_sum, float* part_target, int32_t* valid_idx,
+                             int32_t* valid_count, int32_t* err_flag, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V_shard, dtype);
   if (st != LCE_OK) return st;
+  st = check_shard(V_total, v_begin, V_shard);
+  if (st != LCE_OK) return st;
+  if (!W_shard || !valid_count || !err_flag)
+    return fail(LCE_ERR_INVALID_ARG, "W_shard, valid_count and err_flag must not be NULL");
+  if (N > 0 && (!H || !labels || !part_max || !part_sum || !part_target || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG,
+                "H, labels, part_max, part_sum, part_target and valid_idx must not be NULL");
+  return forward_impl(H, W_shard, labels, ignore_index, N, d, V_total, v_begin, V_shard, dtype,
+                      nullptr, nullptr, part_max, part_sum, part_target, valid_idx, valid_count,
+                      nullptr, nullptr, err_flag, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_lse_merge(const float* part_max, const float* part_sum, const float* part_target,
+                         int64_t n_shards, int64_t shard_stride, int64_t N,
+                         const int32_t* valid_idx, const int32_t* valid_count, float* loss,
+                         float* lse, double* loss_sum, float* loss_mean, void* stream) {
+  g_err.clear();
+  if (N < 0 || N >= ((int64_t)1 << 31)) return fail(LCE_ERR_INVALID_ARG, "N must be in [0, 2^31)");
+  if (n_shards < 1) return fail(LCE_ERR_INVALID_ARG, "n_shards must be >= 1");
+  if (n_shards > 1 && shard_stride < N)
+    return fail(LCE_ERR_INVALID_ARG, "shard_stride must be >= N");
+  if (!valid_count || !loss_sum)
+    return fail(LCE_ERR_INVALID_ARG, "valid_count and loss_sum must not be NULL");
+  if (N > 0 && (!part_max || !part_sum || !part_target || !valid_idx || !loss || !lse))
+    return fail(LCE_ERR_INVALID_ARG,
+                "part_max, part_sum, part_target, valid_idx, loss and lse must not be NULL");
   hipStream_t s = (hipStream_t)stream;
+  hipError_t e = run(LCE_K_MERGE, s, [&] {
+    return lce::launch_shard_merge(part_max, part_sum, part_target, n_shards, shard_stride, N,
+                                   loss, lse, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "shard merge launch");
+  e = run(LCE_K_REDUCE, s, [&] {
+    return lce::launch_loss_reduce(loss, valid_idx, valid_count, loss_sum, loss_mean, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "reduction launch");
+  return LCE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Backward over vocabulary rows [y_off, y_off + V) held by W (the whole
+// vocabulary when y_off = 0 and V = V_total).  accumulate_dH adds this
+// shard's dH contribution instead of overwriting (ignored rows are then left
+// as they are: the first shard zeroed them).
+lce_status backward_impl(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                         const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                         int64_t N, int64_t d, int64_t V_total, int64_t y_off, int64_t V, int dtype,
+                         const float* grad_out, int reduction, float* dH, int accumulate_dH,
+                         float* dW, int accumulate_dW, void* workspace, size_t workspace_bytes,
+                         hipStream_t s) {
+  const Plan p = make_plan(N, d, V, dtype);
+  lce_status st = check_workspace(p, workspace, workspace_bytes);
+  if (st != LCE_OK) return st;
   char* ws = (char*)workspace;
   void* G = ws + p.off_G;
   void* GT = ws + p.off_GT;
   void* HT = ws + p.off_HT;
   void* WT = ws + p.off_WT;
 
-  hipError_t e = run(LCE_K_ZERO, s, [&] {
-    return lce::launch_zero_ignored(labels, N, ignore_index, V, dH, d, s);
-  });
-  if (e != hipSuccess) return hip_fail(e, "zero-rows launch");
+  hipError_t e = hipSuccess;
+  if (!accumulate_dH) {
+    e = run(LCE_K_ZERO, s, [&] {
+      return lce::launch_zero_ignored(labels, N, ignore_index, V_total, dH, d, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "zero-rows launch");
+  }
 
   // At least one chunk, so that dW is written even when N == 0.
   for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
@@ -313,6 +400,7 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       ga.N = N;
       ga.d = d;
       ga.V = V;
+      ga.y_off = y_off;
       ga.c0 = c0;
       ga.C = p.C;
       ga.v0 = v0;
@@ -338,7 +426,7 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
       ha.v0 = v0;
       ha.V = V;
       ha.dH = dH;
-      ha.beta = v0 > 0 ? 1 : 0;
+      ha.beta = (v0 > 0 || accumulate_dH) ? 1 : 0;
       lce::DwArgs wa{};
       wa.GT = GT;
       wa.HT = HT;
@@ -363,6 +451,52 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
     }
   }
   return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
+                        const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                        int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
+                        int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (reduction != LCE_MEAN && reduction != LCE_SUM)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
+  if (!W || !valid_count || !grad_out || !dW)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and dW must not be NULL");
+  if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
+  return backward_impl(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, 0, V,
+                       dtype, grad_out, reduction, dH, 0, dW, accumulate_dW, workspace,
+                       workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t* labels,
+                              int64_t ignore_index, const float* lse, const int32_t* valid_idx,
+                              const int32_t* valid_count, int64_t N, int64_t d, int64_t V_total,
+                              int64_t v_begin, int64_t V_shard, int dtype, const float* grad_out,
+                              int reduction, float* dH, int accumulate_dH, float* dW_shard,
+                              int accumulate_dW, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V_shard, dtype);
+  if (st != LCE_OK) return st;
+  st = check_shard(V_total, v_begin, V_shard);
+  if (st != LCE_OK) return st;
+  if (reduction != LCE_MEAN && reduction != LCE_SUM)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
+  if (!W_shard || !valid_count || !grad_out || !dW_shard)
+    return fail(LCE_ERR_INVALID_ARG, "W_shard, valid_count, grad_out and dW_shard must not be NULL");
+  if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
+  return backward_impl(H, W_shard, labels, ignore_index, lse, valid_idx, valid_count, N, d, V_total,
+                       v_begin, V_shard, dtype, grad_out, reduction, dH, accumulate_dH ? 1 : 0,
+                       dW_shard, accumulate_dW, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 lce_status lce_check_error(const int32_t* err_flag, void* stream) {

@@ -13,6 +13,7 @@ struct FwdArgs {
   const int32_t* valid_idx;
   const int32_t* valid_count;
   int64_t N, d, V;
+  int64_t y_off;  // label of vocabulary row v of W is y_off + v (a shard's first entry)
   int n_vtiles;  // ceil(V / 256)
   int tpc;       // vocabulary tiles per chunk
   int J;         // chunks: ceil(n_vtiles / tpc)
@@ -32,6 +33,7 @@ struct BwdGArgs {
   const float* grad_out;
   int reduction;  // 0 mean, 1 sum
   int64_t N, d, V;
+  int64_t y_off;   // label of vocabulary row v of W is y_off + v (a shard's first entry)
   int64_t c0, C;   // token chunk of the compact index
   int64_t v0, Vs;  // vocabulary block
   void* G;         // [C][ldG]
@@ -83,8 +85,14 @@ hipError_t launch_compact(const int64_t* labels, int64_t N, int64_t ignore_index
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int grid, hipStream_t s);
 hipError_t launch_fwd_merge(const FwdArgs& a, float* loss, float* lse, float* loss_c,
                             int64_t N, hipStream_t s);
-hipError_t launch_loss_reduce(const float* loss_c, const int32_t* valid_count, double* loss_sum,
-                              float* loss_mean, hipStream_t s);
+hipError_t launch_fwd_part(const FwdArgs& a, float* part_max, float* part_sum, float* part_target,
+                           int64_t N, hipStream_t s);
+hipError_t launch_shard_merge(const float* part_max, const float* part_sum, const float* part_target,
+                              int64_t n_shards, int64_t stride, int64_t N, float* loss, float* lse,
+                              hipStream_t s);
+// gather == nullptr: sums loss[0 .. count); else sums loss[gather[i]], i < count
+hipError_t launch_loss_reduce(const float* loss, const int32_t* gather, const int32_t* valid_count,
+                              double* loss_sum, float* loss_mean, hipStream_t s);
 hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
                                float* dH, int64_t d, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);

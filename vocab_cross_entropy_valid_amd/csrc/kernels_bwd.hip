@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
     const int64_t i = a.c0 + (int64_t)tn * kTile + wb * kWaveN + 2 * j + nt;
     if (i < count) {
       const int r = a.valid_idx[i];
-      y[nt] = (int)a.labels[r];
+      y[nt] = (int)(a.labels[r] - a.y_off);  // outside [0, V) in a shard without it
       lse_t[nt] = a.lse[r];
       w_t[nt] = w;
     } else {

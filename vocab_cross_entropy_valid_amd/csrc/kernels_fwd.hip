@@ -134,7 +134,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const int i = tt * kTile + wb * kWaveN + 2 * j + nt;
-      y[nt] = (i < count) ? (int)a.labels[a.valid_idx[i]] : -1;
+      // label relative to row 0 of W (outside [0, V) in a vocabulary shard
+      // that does not hold it: then it never matches an entry)
+      y[nt] = (i < count) ? (int)(a.labels[a.valid_idx[i]] - a.y_off) : -1;
       m[nt] = -INFINITY;
       s[nt] = 0.f;
       zy[nt] = -INFINITY;
@@ -276,6 +278,88 @@ hipError_t launch_fwd_merge(const FwdArgs& a, float* loss, float* lse, float* lo
   return hipGetLastError();
 }
 
+// ------------------------------------------------- vocabulary shards
+//
+// A shard is a contiguous slice [y_off, y_off + V) of the vocabulary, with its
+// own rows of W (MaximusLLM page, section 2.1: the vocabulary table split into
+// contiguous sub-tables).  Per valid row the shard exports its partial of the
+// online-softmax state (OjasX page, core technology): m = the largest logit
+// in the shard, s = sum over the shard of exp(logit - m), and the target
+// logit when the label lies in the shard (-inf otherwise), in natural-log
+// units, at the row's original position.
+__global__ __launch_bounds__(256) void fwd_part_kernel(FwdArgs a, float* __restrict__ part_max,
+                                                       float* __restrict__ part_sum,
+                                                       float* __restrict__ part_target) {
+  const int count = *a.valid_count;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float M = -INFINITY;
+  for (int c = 0; c < a.J; ++c) M = fmaxf(M, a.pm[(int64_t)c * a.Nb + i]);
+  float S = 0.f;
+  for (int c = 0; c < a.J; ++c) {
+    const int64_t o = (int64_t)c * a.Nb + i;
+    S += a.ps[o] * fast_exp2(a.pm[o] - M);
+  }
+  const int r = a.valid_idx[i];
+  const int64_t yl = a.labels[r] - a.y_off;
+  float zt = -INFINITY;
+  if (yl >= 0 && yl < a.V) zt = a.pz[(int64_t)((int)(yl / kVocabTile) / a.tpc) * a.Nb + i];
+  part_max[r] = M * kLn2;
+  part_sum[r] = S;
+  part_target[r] = zt;
+}
+
+hipError_t launch_fwd_part(const FwdArgs& a, float* part_max, float* part_sum, float* part_target,
+                           int64_t N, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int grid = (int)((N + 255) / 256);
+  hipLaunchKernelGGL(fwd_part_kernel, dim3(grid), dim3(256), 0, s, a, part_max, part_sum,
+                     part_target);
+  return hipGetLastError();
+}
+
+// Merges the partials of n shards that together cover the vocabulary, with
+// the same rescale step as the online softmax: M = max m_i,
+// S = sum s_i exp(m_i - M), lse = M + log S, loss = lse - (the one finite
+// target).  Shard i's arrays start at i * stride.  A row that every shard
+// left with s = 0 is an ignored row: loss = lse = 0.
+__global__ __launch_bounds__(256) void shard_merge_kernel(const float* __restrict__ part_max,
+                                                          const float* __restrict__ part_sum,
+                                                          const float* __restrict__ part_target,
+                                                          int64_t n_shards, int64_t stride,
+                                                          int64_t N, float* __restrict__ loss,
+                                                          float* __restrict__ lse) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= N) return;
+  float M = -INFINITY;
+  for (int64_t k = 0; k < n_shards; ++k)
+    if (part_sum[k * stride + r] > 0.f) M = fmaxf(M, part_max[k * stride + r]);
+  if (M == -INFINITY) {
+    loss[r] = 0.f;
+    lse[r] = 0.f;
+    return;
+  }
+  float S = 0.f, zt = -INFINITY;
+  for (int64_t k = 0; k < n_shards; ++k) {
+    const int64_t o = k * stride + r;
+    S += part_sum[o] * fast_exp2((part_max[o] - M) * kLog2e);
+    zt = fmaxf(zt, part_target[o]);
+  }
+  const float l = M + fast_log2(S) * kLn2;
+  lse[r] = l;
+  loss[r] = l - zt;
+}
+
+hipError_t launch_shard_merge(const float* part_max, const float* part_sum, const float* part_target,
+                              int64_t n_shards, int64_t stride, int64_t N, float* loss, float* lse,
+                              hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int grid = (int)((N + 255) / 256);
+  hipLaunchKernelGGL(shard_merge_kernel, dim3(grid), dim3(256), 0, s, part_max, part_sum,
+                     part_target, n_shards, stride, N, loss, lse);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------- loss reduction
 //
 // Sum of per-token losses over valid rows in a fixed order (strided fp64
@@ -283,6 +367,7 @@ hipError_t launch_fwd_merge(const FwdArgs& a, float* loss, float* lse, float* lo
 // bitwise reproducible.  Writes the sum and the mean over valid rows (NaN
 // when no row is valid, as PyTorch's mean cross-entropy does).
 __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ loss_c,
+                                                           const int32_t* __restrict__ gather,
                                                            const int32_t* __restrict__ valid_count,
                                                            double* __restrict__ loss_sum,
                                                            float* __restrict__ loss_mean) {
@@ -290,7 +375,7 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restri
   const int tid = threadIdx.x;
   const int count = *valid_count;
   double acc = 0.0;
-  for (int i = tid; i < count; i += 1024) acc += (double)loss_c[i];
+  for (int i = tid; i < count; i += 1024) acc += (double)loss_c[gather ? gather[i] : i];
   part[tid] = acc;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
@@ -303,10 +388,10 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restri
   }
 }
 
-hipError_t launch_loss_reduce(const float* loss_c, const int32_t* valid_count, double* loss_sum,
-                              float* loss_mean, hipStream_t s) {
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, loss_c, valid_count, loss_sum,
-                     loss_mean);
+hipError_t launch_loss_reduce(const float* loss, const int32_t* gather, const int32_t* valid_count,
+                              double* loss_sum, float* loss_mean, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, loss, gather, valid_count,
+                     loss_sum, loss_mean);
   return hipGetLastError();
 }
 

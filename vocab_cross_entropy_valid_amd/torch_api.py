@@ -135,6 +135,99 @@ def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, fwd: Forwar
     return dH, dW
 
 
+# ------------------------------------------------------ vocabulary shards
+
+@dataclasses.dataclass
+class ShardPartials:
+    part_max: torch.Tensor     # f32 [N]: largest logit over the shard (0 on ignored rows)
+    part_sum: torch.Tensor     # f32 [N]: sum over the shard of exp(logit - part_max)
+    part_target: torch.Tensor  # f32 [N]: target logit if the label is in the shard, else -inf
+    valid_idx: torch.Tensor
+    valid_count: torch.Tensor
+    err_flag: torch.Tensor
+
+
+def forward_shard(H: torch.Tensor, W_shard: torch.Tensor, labels: torch.Tensor, V_total: int,
+                  v_begin: int, ignore_index: int = -100,
+                  workspace: Optional[torch.Tensor] = None,
+                  out: Optional[ShardPartials] = None) -> ShardPartials:
+    """lce_forward_shard: W_shard holds vocabulary rows [v_begin, v_begin + V_shard)."""
+    _check_inputs(H, W_shard, labels)
+    N, d = H.shape
+    Vs = W_shard.shape[0]
+    dev = H.device
+    if workspace is None:
+        workspace = alloc_workspace(N, d, Vs, H.dtype, dev)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = ShardPartials(
+            part_max=torch.empty(N, **f32), part_sum=torch.empty(N, **f32),
+            part_target=torch.empty(N, **f32),
+            valid_idx=torch.empty(N, dtype=torch.int32, device=dev),
+            valid_count=torch.empty(1, dtype=torch.int32, device=dev),
+            err_flag=torch.empty(1, dtype=torch.int32, device=dev))
+    _lib.lce_forward_shard(_ptr(H), _ptr(W_shard), _ptr(labels), int(ignore_index), N, d,
+                           int(V_total), int(v_begin), Vs, _DTYPES[H.dtype], _ptr(out.part_max),
+                           _ptr(out.part_sum), _ptr(out.part_target), _ptr(out.valid_idx),
+                           _ptr(out.valid_count), _ptr(out.err_flag), _ptr(workspace),
+                           workspace.numel(), _stream(dev))
+    return out
+
+
+def lse_merge(part_max: torch.Tensor, part_sum: torch.Tensor, part_target: torch.Tensor,
+              valid_idx: torch.Tensor, valid_count: torch.Tensor) -> ForwardOut:
+    """lce_lse_merge over stacked shard partials of shape [n_shards, N]."""
+    if part_max.dim() != 2 or part_max.shape != part_sum.shape or part_max.shape != part_target.shape:
+        raise ValueError("partials must be three [n_shards, N] tensors")
+    for t in (part_max, part_sum, part_target):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("partials must be contiguous float32 GPU tensors")
+    n_shards, N = part_max.shape
+    dev = part_max.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = ForwardOut(
+        loss=torch.empty(N, **f32), lse=torch.empty(N, **f32), valid_idx=valid_idx,
+        valid_count=valid_count, loss_sum=torch.empty(1, dtype=torch.float64, device=dev),
+        loss_mean=torch.empty(1, **f32), err_flag=torch.zeros(1, dtype=torch.int32, device=dev))
+    _lib.lce_lse_merge(_ptr(part_max), _ptr(part_sum), _ptr(part_target), n_shards, N, N,
+                       _ptr(valid_idx), _ptr(valid_count), _ptr(out.loss), _ptr(out.lse),
+                       _ptr(out.loss_sum), _ptr(out.loss_mean), _stream(dev))
+    return out
+
+
+def backward_shard(H: torch.Tensor, W_shard: torch.Tensor, labels: torch.Tensor, V_total: int,
+                   v_begin: int, merged: ForwardOut, dH: torch.Tensor, accumulate_dH: bool,
+                   grad_out: Optional[torch.Tensor] = None, reduction: str = "mean",
+                   ignore_index: int = -100, dW_shard: Optional[torch.Tensor] = None,
+                   accumulate_dW: bool = False, workspace: Optional[torch.Tensor] = None):
+    """lce_backward_shard; returns dW_shard (dH is updated in place)."""
+    _check_inputs(H, W_shard, labels)
+    N, d = H.shape
+    Vs = W_shard.shape[0]
+    dev = H.device
+    if reduction not in _RED:
+        raise ValueError("reduction must be 'mean' or 'sum'")
+    if grad_out is None:
+        grad_out = torch.ones(1, dtype=torch.float32, device=dev)
+    grad_out = grad_out.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    if workspace is None:
+        workspace = alloc_workspace(N, d, Vs, H.dtype, dev)
+    if dW_shard is None:
+        if accumulate_dW:
+            raise ValueError("accumulate_dW needs dW_shard")
+        dW_shard = torch.empty(Vs, d, dtype=torch.float32, device=dev)
+    for t, shp in ((dH, (N, d)), (dW_shard, (Vs, d))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError("dH and dW_shard must be contiguous float32 [N, d] and [V_shard, d]")
+    _lib.lce_backward_shard(_ptr(H), _ptr(W_shard), _ptr(labels), int(ignore_index),
+                            _ptr(merged.lse), _ptr(merged.valid_idx), _ptr(merged.valid_count),
+                            N, d, int(V_total), int(v_begin), Vs, _DTYPES[H.dtype],
+                            _ptr(grad_out), _RED[reduction], _ptr(dH), 1 if accumulate_dH else 0,
+                            _ptr(dW_shard), 1 if accumulate_dW else 0, _ptr(workspace),
+                            workspace.numel(), _stream(dev))
+    return dW_shard
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, W, labels, ignore_index, reduction, check):
