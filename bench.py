@@ -142,6 +142,10 @@ def main():
     ap.add_argument("--shards", type=int, default=1,
                     help="split the vocabulary into this many contiguous shards: each step runs "
                          "the shard forwards, the merge and the shard backwards")
+    ap.add_argument("--tied-input", action="store_true",
+                    help="also run the input side of a tied table each step: the masked "
+                         "embedding gather of the shifted labels and the scatter-sum of a "
+                         "synthetic dX into dW")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -203,6 +207,32 @@ def main():
                                          grad_out=g, dW_shard=dWsh[k], workspace=wss)
             return fwd
 
+    tied = None
+    if args.tied_input:
+        # next-token inputs: position n reads the previous position's label; the
+        # first position and the padded ones read the padding id -1
+        ids = np.concatenate([[-1], y[:-1]]).astype(np.int64)
+        ids[ids == -100] = -1
+        idt = torch.from_numpy(ids).to(dev)
+        dXt = torch.randn(wl.N, wl.d, dtype=torch.float32, device=dev)
+        ews = torch.empty(_lib.lce_embed_workspace_bytes(wl.N, wl.d, wl.V), dtype=torch.uint8,
+                          device=dev)
+        n_in = int(np.count_nonzero(ids != -1))
+        uniq = int(np.unique(ids[ids != -1]).size)
+        esz = 2 if wl.dtype == "bf16" else 4
+        tied = {"pad_id": -1, "valid_inputs": n_in, "distinct_ids": uniq,
+                # gather: valid rows of W read, every row of X written; backward: valid
+                # rows of dX read, each touched dW row read and written
+                "algorithmic_bytes": n_in * wl.d * esz + wl.N * wl.d * esz
+                + n_in * wl.d * 4 + 2 * uniq * wl.d * 4}
+        base_step = step
+
+        def step():  # noqa: F811
+            emb = torch_api.embed_forward(Wt, idt, -1)
+            fwd = base_step()
+            torch_api.embed_backward(dXt, idt, emb, dW, accumulate_dW=True, workspace=ews)
+            return fwd
+
     _log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         fwd = step()
@@ -250,6 +280,12 @@ def main():
         roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": None, "traffic": None}
 
+    if tied is not None and "embed" in kernels:
+        k = kernels["embed"]
+        tied["embed_ms_per_step"] = round(k["ms_per_step"], 4)
+        tied["GB/s"] = round(tied["algorithmic_bytes"] / (k["ms_per_step"] * 1e-3) / 1e9, 1)
+        tied["peak_GB/s"] = PEAK_HBM_GBS
+
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, dev)
 
@@ -294,7 +330,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic: seeded Gaussian H, W and Zipf labels with padding (no dataset)",
         "config": {"workload": wl.name + (f" in {args.shards} vocabulary shards"
-                                          if args.shards > 1 else ""), "N": wl.N, "d": wl.d, "V": wl.V,
+                                          if args.shards > 1 else "")
+                   + (" with the tied input side" if args.tied_input else ""), "N": wl.N, "d": wl.d, "V": wl.V,
                    "N_valid": n_valid, "ignore_index": -100, "seed": wl.seed},
         "tflops": round(tflops, 2),
         "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -304,6 +341,7 @@ def main():
         "roofline": roofline,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "gemm_engine_reference": gemm,
+        "tied_input": tied,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -167,6 +167,38 @@ lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t*
                               int accumulate_dW, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ------------------------------------------- tied table: input side
+ *
+ * The same table W [V, d] read as the input embedding ("6GB显卡预训练11亿参数模型",
+ * section 使用的预训练配置: tied embeddings).  Only positions whose id is not
+ * pad_id are looked up; the others get a zero vector, and the valid index is
+ * built on the device in the same launch sequence, with no host round trip
+ * ("MaximusLLM" page, section 2.3: padding-aware sparse index engine).
+ */
+
+/* X [N, d] (dtype of W) = W[input_ids[n]] for valid n, 0 elsewhere.  valid_idx
+ * (int32 [N], ascending), valid_count and err_flag as lce_forward builds them
+ * from labels, with pad_id in place of ignore_index: an id outside [0, V)
+ * that is not pad_id sets err_flag and the row is treated as padding. */
+lce_status lce_embed_forward(const void* W, const int64_t* input_ids, int64_t pad_id, int64_t N,
+                             int64_t d, int64_t V, int dtype, void* X, int32_t* valid_idx,
+                             int32_t* valid_count, int32_t* err_flag, void* stream);
+
+/* Bytes of device workspace lce_embed_backward needs (0 for unsupported
+ * sizes).  O(N + N * d / 32): sort keys, segment lists and chunk partials. */
+size_t lce_embed_workspace_bytes(int64_t N, int64_t d, int64_t V);
+
+/* dW [V, d] f32 += sum of dX [N, d] f32 rows over valid positions with that
+ * id (accumulate_dW != 0: add to dW, e.g. after lce_backward filled in the
+ * output side of a tied table; 0: rows with no occurrence become 0).  The
+ * valid rows are stably sorted by id, rows sharing an id are summed in a
+ * fixed order (ascending position inside 64-row chunks, then the chunks in
+ * order): results are bitwise reproducible, no floating-point atomics. */
+lce_status lce_embed_backward(const float* dX, const int64_t* input_ids, const int32_t* valid_idx,
+                              const int32_t* valid_count, int64_t N, int64_t d, int64_t V,
+                              float* dW, int accumulate_dW, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream` and returns LCE_ERR_LABEL_RANGE when *err_flag is set
  * (a valid label outside [0, V) -- the out-of-range index failure described
  * in "6GB显卡预训练11亿参数模型", section 可证伪测试抓到的8个静默bug, #155),
@@ -199,7 +231,8 @@ typedef enum {
   LCE_K_DH = 7,        /* dH += G W                                      */
   LCE_K_DW = 8,        /* dW += G^T H                                    */
   LCE_K_GEMM = 9,      /* lce_gemm_nt                                    */
-  LCE_K_COUNT = 10
+  LCE_K_EMBED = 10,    /* embedding gather / gradient scatter-sum        */
+  LCE_K_COUNT = 11
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -313,3 +313,38 @@ def shard_backward(H, W_shard, labels, lse, v_begin: int, V_total: int,
         dH[rows] = G @ W64
         dW += G.T @ Hb
     return dH, dW
+
+
+# --------------------------------------------------------------------------
+# tied table: input side
+# --------------------------------------------------------------------------
+#
+# The same table W read as the input embedding.  Positions whose id is the
+# padding id are not looked up and get a zero vector (MaximusLLM page,
+# section 2.3); the gradient of the lookup sends each valid row of dX back to
+# the table row it came from.
+
+
+def embed_forward(W, input_ids, pad_id: int):
+    """(X float64 [N, d], valid_idx int32): X[n] = W[id[n]] for valid n, else 0."""
+    W = np.asarray(W, dtype=np.float64)
+    ids = np.asarray(input_ids, dtype=np.int64)
+    idx, _, bad = compact_valid(ids, pad_id, W.shape[0])
+    if bad.size:
+        raise ValueError(f"{bad.size} input id(s) outside [0, {W.shape[0]})")
+    X = np.zeros((ids.shape[0], W.shape[1]))
+    X[idx] = W[ids[idx]]
+    return X, idx
+
+
+def embed_backward(dX, input_ids, pad_id: int, V: int):
+    """dW float64 [V, d]: dW[v] = sum of dX[n] over valid n with id[n] = v."""
+    dX = np.asarray(dX, dtype=np.float64)
+    ids = np.asarray(input_ids, dtype=np.int64)
+    idx, _, bad = compact_valid(ids, pad_id, V)
+    if bad.size:
+        raise ValueError(f"{bad.size} input id(s) outside [0, {V})")
+    dW = np.zeros((V, dX.shape[1]))
+    for n in idx:
+        dW[ids[n]] += dX[n]
+    return dW

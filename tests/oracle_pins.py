@@ -359,12 +359,68 @@ def pin_shard_backward_sum(o):
         np.testing.assert_allclose(np.concatenate(rows), dW, rtol=1e-12, atol=1e-15)
 
 
+# ------------------------------------------------ tied table: input side
+
+def _ids_case(seed, N=40, V=13, pad=0, n_pad=9):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, V, N).astype(np.int64)
+    ids[rng.choice(N, n_pad, replace=False)] = pad
+    ids[:3] = 5                      # an id repeated at the start
+    return ids
+
+
+def pin_embed_adjoint(o):
+    """The lookup is linear in W (X = E W with E the masked one-hot matrix),
+    so its gradient is the adjoint: <dX, E W'> = <E^T dX, W'> for any W'."""
+    rng = np.random.default_rng(20)
+    ids = _ids_case(20)
+    W = rng.standard_normal((13, 6))
+    dX = rng.standard_normal((40, 6))
+    X, _ = o.embed_forward(W, ids, 0)
+    dW = o.embed_backward(dX, ids, 0, 13)
+    lhs = float((dX * X).sum())
+    rhs = float((dW * W).sum())
+    assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + 1.0)
+
+
+def pin_embed_dense(o):
+    """Forward and backward against the dense one-hot matrix E [N, V] (E[n, v]
+    = 1 when n is not padding and id[n] = v): X = E W and dW = E^T dX by
+    numpy's matrix product; padding rows of X are zero."""
+    rng = np.random.default_rng(21)
+    ids = _ids_case(21, pad=3)
+    W = rng.standard_normal((13, 5))
+    dX = rng.standard_normal((40, 5))
+    E = np.zeros((40, 13))
+    keep = ids != 3
+    E[np.flatnonzero(keep), ids[keep]] = 1.0
+    X, idx = o.embed_forward(W, ids, 3)
+    np.testing.assert_allclose(X, E @ W, rtol=0, atol=0)
+    np.testing.assert_allclose(o.embed_backward(dX, ids, 3, 13), E.T @ dX, rtol=1e-13, atol=1e-13)
+    assert idx.tolist() == np.flatnonzero(keep).tolist()
+    assert not X[~keep].any()
+
+
+def pin_embed_bad_id(o):
+    """An id outside [0, V) that is not the padding id is an error."""
+    ids = _ids_case(22)
+    ids[7] = 13
+    for fn in (lambda: o.embed_forward(np.zeros((13, 2)), ids, 0),
+               lambda: o.embed_backward(np.zeros((40, 2)), ids, 0, 13)):
+        try:
+            fn()
+        except ValueError:
+            continue
+        raise AssertionError("out-of-range id accepted")
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
     pin_ignore_inside_range, pin_bad_label, pin_finite_differences,
     pin_mpmath, pin_torch_cross_entropy, pin_row_functions, pin_compaction,
     pin_shard_merge_identity, pin_shard_partials_definition, pin_shard_backward_sum,
+    pin_embed_adjoint, pin_embed_dense, pin_embed_bad_id,
 ]
 
 

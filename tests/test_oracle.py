@@ -102,7 +102,39 @@ def _shard_backward_local_lse(H, W_shard, labels, lse, v_begin, V_total, ignore_
     return _orig_shard_backward(H, W_shard, labels, local, v_begin, V_total, ignore_index, **kw)
 
 
+def _embed_bwd_keeps_padding(dX, input_ids, pad_id, V):
+    dX = np.asarray(dX, dtype=np.float64)
+    ids = np.asarray(input_ids, dtype=np.int64)
+    dW = np.zeros((V, dX.shape[1]))
+    for n in range(ids.shape[0]):
+        if 0 <= ids[n] < V:
+            dW[ids[n]] += dX[n]
+    return dW
+
+
+def _embed_bwd_overwrites(dX, input_ids, pad_id, V):
+    # a repeated id keeps only its last row instead of the sum
+    dX = np.asarray(dX, dtype=np.float64)
+    ids = np.asarray(input_ids, dtype=np.int64)
+    dW = np.zeros((V, dX.shape[1]))
+    for n in np.flatnonzero(ids != pad_id):
+        dW[ids[n]] = dX[n]
+    return dW
+
+
+def _embed_fwd_off_by_one(W, input_ids, pad_id):
+    W = np.asarray(W, dtype=np.float64)
+    ids = np.asarray(input_ids, dtype=np.int64)
+    idx = np.flatnonzero(ids != pad_id).astype(np.int32)
+    X = np.zeros((ids.shape[0], W.shape[1]))
+    X[idx] = W[(ids[idx] + 1) % W.shape[0]]
+    return X, idx
+
+
 MUTATIONS = {
+    "embed_backward_keeps_padding": ("embed_backward", _embed_bwd_keeps_padding),
+    "embed_backward_overwrites_repeats": ("embed_backward", _embed_bwd_overwrites),
+    "embed_forward_id_off_by_one": ("embed_forward", _embed_fwd_off_by_one),
     "shard_merge_without_rescale": ("merge_partials", _merge_without_rescale),
     "shard_label_not_offset": ("shard_partials", _shard_label_not_offset),
     "shard_backward_local_lse": ("shard_backward", _shard_backward_local_lse),

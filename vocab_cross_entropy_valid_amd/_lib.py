@@ -27,7 +27,7 @@ LCE_MEAN = 0
 LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
-                  "bwd_g", "dh", "dw", "gemm")
+                  "bwd_g", "dh", "dw", "gemm", "embed")
 
 # name -> (restype, argtypes), in the order of include/lce.h
 _P = ctypes.c_void_p
@@ -45,6 +45,9 @@ SIGNATURES = {
     "lce_lse_merge": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "lce_backward_shard": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _INT,
                                   _P, _INT, _P, _INT, _P, _INT, _P, _SZ, _P]),
+    "lce_embed_forward": (_INT, [_P, _P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
+    "lce_embed_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "lce_embed_backward": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
     "lce_check_error": (_INT, [_P, _P]),
     "lce_status_string": (ctypes.c_char_p, [_INT]),
     "lce_last_error": (ctypes.c_char_p, []),
@@ -139,6 +142,23 @@ def lce_backward_shard(H, W_shard, labels, ignore_index, lse, valid_idx, valid_c
                                      grad_out, reduction, dH, accumulate_dH, dW_shard,
                                      accumulate_dW, workspace, workspace_bytes, stream),
            "lce_backward_shard")
+
+
+def lce_embed_forward(W, input_ids, pad_id, N, d, V, dtype, X, valid_idx, valid_count, err_flag,
+                      stream) -> None:
+    _check(load().lce_embed_forward(W, input_ids, pad_id, N, d, V, dtype, X, valid_idx,
+                                    valid_count, err_flag, stream), "lce_embed_forward")
+
+
+def lce_embed_workspace_bytes(N: int, d: int, V: int) -> int:
+    return int(load().lce_embed_workspace_bytes(N, d, V))
+
+
+def lce_embed_backward(dX, input_ids, valid_idx, valid_count, N, d, V, dW, accumulate_dW,
+                       workspace, workspace_bytes, stream) -> None:
+    _check(load().lce_embed_backward(dX, input_ids, valid_idx, valid_count, N, d, V, dW,
+                                     accumulate_dW, workspace, workspace_bytes, stream),
+           "lce_embed_backward")
 
 
 def lce_check_error(err_flag, stream) -> None:

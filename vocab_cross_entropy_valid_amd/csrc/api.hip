@@ -499,6 +499,63 @@ lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t*
                        dW_shard, accumulate_dW, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+size_t lce_embed_workspace_bytes(int64_t N, int64_t d, int64_t V) {
+  if (check_sizes(N, d, V, LCE_F32) != LCE_OK) return 0;
+  const lce::EmbedPlan p = lce::make_embed_plan(N, d, V);
+  return p.sort_bytes ? p.total : 0;
+}
+
+lce_status lce_embed_forward(const void* W, const int64_t* input_ids, int64_t pad_id, int64_t N,
+                             int64_t d, int64_t V, int dtype, void* X, int32_t* valid_idx,
+                             int32_t* valid_count, int32_t* err_flag, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (!W || !valid_count || !err_flag)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count and err_flag must not be NULL");
+  if (N > 0 && (!input_ids || !X || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG, "input_ids, X and valid_idx must not be NULL");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = run(LCE_K_COMPACT, s, [&] {
+    return lce::launch_compact(input_ids, N, pad_id, V, valid_idx, valid_count, err_flag, nullptr,
+                               nullptr, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "compaction launch");
+  const int64_t esz = dtype == LCE_BF16 ? 2 : 4;
+  e = run(LCE_K_EMBED, s,
+          [&] { return lce::launch_embed_gather(W, input_ids, pad_id, N, V, d * esz, X, s); });
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return LCE_OK;
+}
+
+lce_status lce_embed_backward(const float* dX, const int64_t* input_ids, const int32_t* valid_idx,
+                              const int32_t* valid_count, int64_t N, int64_t d, int64_t V,
+                              float* dW, int accumulate_dW, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, LCE_F32);
+  if (st != LCE_OK) return st;
+  if (!valid_count || !dW) return fail(LCE_ERR_INVALID_ARG, "valid_count and dW must not be NULL");
+  if (N > 0 && (!dX || !input_ids || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG, "dX, input_ids and valid_idx must not be NULL");
+  const lce::EmbedPlan p = lce::make_embed_plan(N, d, V);
+  if (!p.sort_bytes) return fail(LCE_ERR_HIP, "sort workspace query failed");
+  if (workspace_bytes < p.total)
+    return fail(LCE_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                       " bytes is smaller than the required " +
+                                       std::to_string(p.total));
+  if (!workspace) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = run(LCE_K_EMBED, s, [&] {
+    return lce::launch_embed_backward(p, dX, input_ids, valid_idx, valid_count, N, d, V, dW,
+                                      accumulate_dW ? 1 : 0, workspace, 4 * grid_persistent(), s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "embedding backward launch");
+  return LCE_OK;
+}
+
 lce_status lce_check_error(const int32_t* err_flag, void* stream) {
   g_err.clear();
   if (!err_flag) return fail(LCE_ERR_INVALID_ARG, "err_flag is NULL");

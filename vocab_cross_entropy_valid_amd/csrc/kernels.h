@@ -99,6 +99,22 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
 hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s);
+// Workspace layout of the embedding backward (byte offsets, 256-aligned).
+struct EmbedPlan {
+  int end_bit;  // sort key bits: 2^end_bit > V (V itself is the padding sentinel)
+  size_t off_key, off_val, off_key_s, off_val_s, off_seg_start, off_seg_chunk0, off_seg_part0;
+  size_t off_chunk_seg, off_meta, off_sort, off_part;
+  size_t sort_bytes;
+  int64_t max_chunks, max_parts;
+  size_t total;
+};
+EmbedPlan make_embed_plan(int64_t N, int64_t d, int64_t V);
+hipError_t launch_embed_gather(const void* W, const int64_t* ids, int64_t pad_id, int64_t N,
+                               int64_t V, int64_t row_bytes, void* X, hipStream_t s);
+hipError_t launch_embed_backward(const EmbedPlan& p, const float* dX, const int64_t* ids,
+                                 const int32_t* valid_idx, const int32_t* valid_count, int64_t N,
+                                 int64_t d, int64_t V, float* dW, int accumulate, void* ws,
+                                 int grid, hipStream_t s);
 hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                           int dtype, hipStream_t s);
 

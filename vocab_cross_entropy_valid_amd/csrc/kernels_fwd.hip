@@ -17,7 +17,7 @@ namespace lce {
 // the popcount of the ballot bits below it (mbcnt), and the 16 wave totals
 // are scanned in LDS.  A kept label outside [0, V) raises err_flag and the
 // row is treated as ignored, so no later kernel indexes W with it.
-// Ignored rows get loss = lse = 0 here.
+// Ignored rows get loss = lse = 0 here (when loss is not null).
 __global__ __launch_bounds__(1024) void compact_kernel(const int64_t* __restrict__ labels, int64_t N,
                                                        int64_t ignore_index, int64_t V,
                                                        int32_t* __restrict__ valid_idx,
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const int64_t* __restrict
     const bool in_range = (y >= 0) && (y < V);
     err |= (keep && !in_range) ? 1 : 0;
     const bool valid = keep && in_range;
-    if (in && !valid) {
+    if (in && !valid && loss) {
       loss[n] = 0.f;
       lse[n] = 0.f;
     }

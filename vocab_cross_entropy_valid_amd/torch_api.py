@@ -228,6 +228,61 @@ def backward_shard(H: torch.Tensor, W_shard: torch.Tensor, labels: torch.Tensor,
     return dW_shard
 
 
+# -------------------------------------------- tied table: input side
+
+@dataclasses.dataclass
+class EmbedOut:
+    X: torch.Tensor            # [N, d], dtype of W; zero rows at padding positions
+    valid_idx: torch.Tensor    # int32 [N]; first valid_count entries meaningful
+    valid_count: torch.Tensor  # int32 [1]
+    err_flag: torch.Tensor     # int32 [1]
+
+
+def embed_forward(W: torch.Tensor, input_ids: torch.Tensor, pad_id: int) -> EmbedOut:
+    """lce_embed_forward: X = W[input_ids] where input_ids != pad_id, else 0."""
+    if W.dim() != 2 or input_ids.dim() != 1 or input_ids.dtype != torch.int64:
+        raise ValueError("W must be [V, d] and input_ids int64 [N]")
+    if W.dtype not in _DTYPES or not (W.is_cuda and input_ids.is_cuda):
+        raise ValueError("W must be a bfloat16 or float32 GPU tensor, input_ids on the GPU")
+    if not (W.is_contiguous() and input_ids.is_contiguous()):
+        raise ValueError("W and input_ids must be contiguous")
+    V, d = W.shape
+    N = input_ids.shape[0]
+    dev = W.device
+    out = EmbedOut(X=torch.empty(N, d, dtype=W.dtype, device=dev),
+                   valid_idx=torch.empty(N, dtype=torch.int32, device=dev),
+                   valid_count=torch.empty(1, dtype=torch.int32, device=dev),
+                   err_flag=torch.empty(1, dtype=torch.int32, device=dev))
+    _lib.lce_embed_forward(_ptr(W), _ptr(input_ids), int(pad_id), N, d, V, _DTYPES[W.dtype],
+                           _ptr(out.X), _ptr(out.valid_idx), _ptr(out.valid_count),
+                           _ptr(out.err_flag), _stream(dev))
+    return out
+
+
+def embed_backward(dX: torch.Tensor, input_ids: torch.Tensor, emb: EmbedOut, dW: torch.Tensor,
+                   accumulate_dW: bool = True,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lce_embed_backward: dW (+)= scatter-sum of dX rows by input id."""
+    if dX.dtype != torch.float32 or dW.dtype != torch.float32:
+        raise ValueError("dX and dW must be float32")
+    if not (dX.is_contiguous() and dW.is_contiguous()):
+        raise ValueError("dX and dW must be contiguous")
+    N, d = dX.shape
+    V = dW.shape[0]
+    if dW.shape[1] != d or input_ids.shape[0] != N:
+        raise ValueError("shape mismatch")
+    dev = dX.device
+    if workspace is None:
+        n = _lib.lce_embed_workspace_bytes(N, d, V)
+        if n == 0:
+            raise ValueError(f"unsupported sizes N={N} d={d} V={V}")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _lib.lce_embed_backward(_ptr(dX), _ptr(input_ids), _ptr(emb.valid_idx), _ptr(emb.valid_count),
+                            N, d, V, _ptr(dW), 1 if accumulate_dW else 0, _ptr(workspace),
+                            workspace.numel(), _stream(dev))
+    return dW
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, W, labels, ignore_index, reduction, check):
