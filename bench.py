@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--shards", type=int, default=1,
                     help="split the vocabulary into this many contiguous shards: each step runs "
                          "the shard forwards, the merge and the shard backwards")
+    ap.add_argument("--fused-opt", choices=["sgd", "adamw"], default=None,
+                    help="backward with the optimizer applied in the dW epilogue (no dW table); "
+                         "fp32 master weights and AdamW state are allocated")
     ap.add_argument("--tied-input", action="store_true",
                     help="also run the input side of a tied table each step: the masked "
                          "embedding gather of the shifted labels and the scatter-sum of a "
@@ -205,6 +208,31 @@ def main():
             for k, (a, b) in enumerate(shards):
                 torch_api.backward_shard(Ht, Wsh[k], yt, wl.V, a, fwd, dH, accumulate_dH=k > 0,
                                          grad_out=g, dW_shard=dWsh[k], workspace=wss)
+            return fwd
+
+    fused = None
+    if args.fused_opt:
+        if args.tied_input or args.shards > 1:
+            print("--fused-opt runs alone (not with --tied-input or --shards)", file=sys.stderr)
+            sys.exit(2)
+        if wl.N > 8192:
+            print("--fused-opt needs N <= 8192 (one token chunk)", file=sys.stderr)
+            sys.exit(2)
+        master = Wt.float()
+        ea = torch.zeros_like(master) if args.fused_opt == "adamw" else None
+        eas = torch.zeros_like(master) if args.fused_opt == "adamw" else None
+        del dW
+        dW = None
+        fused = {"optimizer": args.fused_opt, "state_bytes": master.numel() * 4 *
+                 (3 if args.fused_opt == "adamw" else 1), "dW_table_bytes_avoided": wl.V * wl.d * 4}
+        t_step = [0]
+
+        def step():  # noqa: F811
+            t_step[0] += 1
+            fwd = torch_api.forward(Ht, Wt, yt, workspace=ws, check=False)
+            torch_api.backward_step(Ht, Wt, yt, fwd, args.fused_opt, 1e-6, 0.0, step=t_step[0],
+                                    W_master=master, exp_avg=ea, exp_avg_sq=eas, grad_out=g,
+                                    dH=dH, workspace=ws)
             return fwd
 
     tied = None
@@ -331,7 +359,8 @@ def main():
         "data": "synthetic: seeded Gaussian H, W and Zipf labels with padding (no dataset)",
         "config": {"workload": wl.name + (f" in {args.shards} vocabulary shards"
                                           if args.shards > 1 else "")
-                   + (" with the tied input side" if args.tied_input else ""), "N": wl.N, "d": wl.d, "V": wl.V,
+                   + (" with the tied input side" if args.tied_input else "")
+                   + (f" with {args.fused_opt} fused into dW" if args.fused_opt else ""), "N": wl.N, "d": wl.d, "V": wl.V,
                    "N_valid": n_valid, "ignore_index": -100, "seed": wl.seed},
         "tflops": round(tflops, 2),
         "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -342,6 +371,7 @@ def main():
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "gemm_engine_reference": gemm,
         "tied_input": tied,
+        "fused_optimizer": fused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

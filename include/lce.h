@@ -112,6 +112,45 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
                         int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------ fused optimizer update
+ *
+ * The backward pass with the optimizer applied to each dW tile as it is
+ * produced, so no dW table is ever stored: updating the weights inside the
+ * backward pass and keeping no persistent gradient buffers ("OjasX 0.6.1",
+ * section 核心技术 / Core Technology, zero-byte .grad buffers).
+ */
+typedef enum { LCE_OPT_SGD = 1, LCE_OPT_ADAMW = 2 } lce_opt_kind;
+
+typedef struct {
+  int kind;             /* LCE_OPT_SGD or LCE_OPT_ADAMW */
+  float lr;             /* >= 0 */
+  float weight_decay;   /* >= 0: SGD adds wd * p to the gradient, AdamW decays p by lr * wd */
+  float beta1, beta2;   /* AdamW, in [0, 1) */
+  float eps;            /* AdamW, > 0 */
+  int64_t step;         /* AdamW step number t >= 1 (bias correction 1 - beta^t) */
+} lce_optimizer;
+
+/* lce_backward (same inputs, same dH) whose dW goes straight into the
+ * optimizer, PyTorch's formulas, in fp32:
+ *   SGD    p -= lr (g + wd p)
+ *   AdamW  p *= 1 - lr wd;  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *          p -= lr / (1 - b1^t) * m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+ * p is W_master (fp32 [V, d]); for bf16 W the updated p is written back to W
+ * rounded to nearest even, and W_master is required; for fp32 W, W_master may
+ * be NULL and W itself is updated.  exp_avg / exp_avg_sq: fp32 [V, d] AdamW
+ * state, updated in place (NULL for SGD).  Every row of W is updated (g = 0
+ * for rows no valid token touches).  Needs N <= 8192 (one token chunk, so
+ * each dW tile is complete when it is applied): LCE_ERR_UNSUPPORTED
+ * otherwise.  A W row is rewritten only after its last read in this pass;
+ * dH uses the weights from before the update.
+ */
+lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int64_t ignore_index,
+                             const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                             int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
+                             int reduction, float* dH, float* W_master, float* exp_avg,
+                             float* exp_avg_sq, const lce_optimizer* opt, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- vocabulary shards
  *
  * The vocabulary [0, V_total) split into contiguous shards, each with its own

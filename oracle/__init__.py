@@ -2,6 +2,6 @@
 from .lce_oracle import (  # noqa: F401
     ForwardResult, ShardPartials, backward, compact_valid, dlogits, embed_backward,
     embed_forward, forward, logits,
-    logsumexp_rows, merge_partials, rows_dH, rows_dW, rows_forward, shard_backward,
+    logsumexp_rows, merge_partials, optimizer_step, rows_dH, rows_dW, rows_forward, shard_backward,
     shard_partials, target_logits, valid_mask,
 )

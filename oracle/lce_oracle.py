@@ -348,3 +348,34 @@ def embed_backward(dX, input_ids, pad_id: int, V: int):
     for n in idx:
         dW[ids[n]] += dX[n]
     return dW
+
+
+# --------------------------------------------------------------------------
+# optimizer step applied to the weight gradient
+# --------------------------------------------------------------------------
+#
+# The update that consumes dW inside the backward pass instead of keeping a
+# gradient buffer (OjasX page, core technology: no persistent .grad).  The
+# formulas are PyTorch's: SGD without momentum, p -= lr (g + wd p); AdamW
+# with decoupled weight decay and bias correction.
+
+
+def optimizer_step(p, g, kind: str, lr: float, weight_decay: float = 0.0, beta1: float = 0.9,
+                   beta2: float = 0.999, eps: float = 1e-8, step: int = 1, exp_avg=None,
+                   exp_avg_sq=None):
+    """(p_new, exp_avg_new, exp_avg_sq_new) in float64 (states None for SGD)."""
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    if kind == "sgd":
+        return p - lr * (g + weight_decay * p), None, None
+    if kind != "adamw":
+        raise ValueError(f"kind must be 'sgd' or 'adamw', got {kind!r}")
+    m = np.asarray(exp_avg, dtype=np.float64)
+    v = np.asarray(exp_avg_sq, dtype=np.float64)
+    p = p * (1.0 - lr * weight_decay)
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    p = p - (lr / bc1) * m / (np.sqrt(v) / np.sqrt(bc2) + eps)
+    return p, m, v

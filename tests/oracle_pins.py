@@ -414,6 +414,42 @@ def pin_embed_bad_id(o):
         raise AssertionError("out-of-range id accepted")
 
 
+# --------------------------------------------------- optimizer step
+
+def pin_sgd_matches_torch(o):
+    """One SGD step (weight decay, no momentum) equals torch.optim.SGD in fp64."""
+    import torch
+    rng = np.random.default_rng(23)
+    p0 = rng.standard_normal((7, 5))
+    g = rng.standard_normal((7, 5))
+    t = torch.tensor(p0, dtype=torch.float64, requires_grad=True)
+    t.grad = torch.tensor(g)
+    torch.optim.SGD([t], lr=0.3, weight_decay=0.05).step()
+    p1, _, _ = o.optimizer_step(p0, g, "sgd", 0.3, 0.05)
+    np.testing.assert_allclose(p1, t.detach().numpy(), rtol=1e-14, atol=1e-15)
+
+
+def pin_adamw_matches_torch(o):
+    """AdamW at step t = 4 from given moment estimates equals torch.optim.AdamW
+    in fp64 (decoupled weight decay, bias correction)."""
+    import torch
+    rng = np.random.default_rng(24)
+    p0 = rng.standard_normal((6, 4))
+    g = rng.standard_normal((6, 4)) * 1e-3
+    m0 = rng.standard_normal((6, 4)) * 1e-3
+    v0 = rng.random((6, 4)) * 1e-6
+    t = torch.tensor(p0, dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.AdamW([t], lr=1e-2, betas=(0.8, 0.95), eps=1e-7, weight_decay=0.1)
+    opt.state[t] = {"step": torch.tensor(3.0, dtype=torch.float64),
+                    "exp_avg": torch.tensor(m0), "exp_avg_sq": torch.tensor(v0)}
+    t.grad = torch.tensor(g)
+    opt.step()
+    p1, m1, v1 = o.optimizer_step(p0, g, "adamw", 1e-2, 0.1, 0.8, 0.95, 1e-7, 4, m0, v0)
+    np.testing.assert_allclose(p1, t.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(m1, opt.state[t]["exp_avg"].numpy(), rtol=1e-13)
+    np.testing.assert_allclose(v1, opt.state[t]["exp_avg_sq"].numpy(), rtol=1e-13)
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
@@ -421,6 +457,7 @@ PINS = [
     pin_mpmath, pin_torch_cross_entropy, pin_row_functions, pin_compaction,
     pin_shard_merge_identity, pin_shard_partials_definition, pin_shard_backward_sum,
     pin_embed_adjoint, pin_embed_dense, pin_embed_bad_id,
+    pin_sgd_matches_torch, pin_adamw_matches_torch,
 ]
 
 

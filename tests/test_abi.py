@@ -155,3 +155,25 @@ def test_shard_workspace_and_merge_argument_checks():
                              None) == _lib.LCE_ERR_INVALID_ARG
     assert lib.lce_lse_merge(fake, fake, fake, 2, 10, 10, fake, fake, None, fake, fake, None,
                              None) == _lib.LCE_ERR_INVALID_ARG
+
+
+def test_backward_step_argument_checks_before_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(N=10, dtype=1, master=fake, m=fake, v=fake, **kw):
+        o = _lib.LceOptimizer(kind=kw.get("kind", _lib.LCE_OPT_ADAMW), lr=kw.get("lr", 1e-3),
+                              weight_decay=0.0, beta1=kw.get("beta1", 0.9), beta2=0.999,
+                              eps=kw.get("eps", 1e-8), step=kw.get("step", 1))
+        return lib.lce_backward_step(fake, fake, fake, -100, fake, fake, fake, N, 64, 100, dtype,
+                                     fake, 0, fake, master, m, v, ctypes.byref(o), fake, 1 << 40,
+                                     None)
+    assert call(N=8193) == _lib.LCE_ERR_UNSUPPORTED        # more than one token chunk
+    assert call(master=None) == _lib.LCE_ERR_INVALID_ARG   # bf16 without master weights
+    assert call(kind=7) == _lib.LCE_ERR_INVALID_ARG
+    assert call(step=0) == _lib.LCE_ERR_INVALID_ARG
+    assert call(beta1=1.0) == _lib.LCE_ERR_INVALID_ARG
+    assert call(eps=0.0) == _lib.LCE_ERR_INVALID_ARG
+    assert call(lr=-1.0) == _lib.LCE_ERR_INVALID_ARG
+    assert call(m=None) == _lib.LCE_ERR_INVALID_ARG
+    assert call(kind=_lib.LCE_OPT_SGD, m=None, v=None, N=8193) == _lib.LCE_ERR_UNSUPPORTED

@@ -131,7 +131,41 @@ def _embed_fwd_off_by_one(W, input_ids, pad_id):
     return X, idx
 
 
+_orig_opt = O.optimizer_step
+
+
+def _adamw_without_bias_correction(p, g, kind, lr, weight_decay=0.0, beta1=0.9, beta2=0.999,
+                                   eps=1e-8, step=1, exp_avg=None, exp_avg_sq=None):
+    if kind != "adamw":
+        return _orig_opt(p, g, kind, lr, weight_decay, beta1, beta2, eps, step, exp_avg,
+                         exp_avg_sq)
+    p = np.asarray(p, dtype=np.float64) * (1.0 - lr * weight_decay)
+    m = beta1 * np.asarray(exp_avg) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(exp_avg_sq) + (1.0 - beta2) * g * g
+    return p - lr * m / (np.sqrt(v) + eps), m, v
+
+
+def _adamw_coupled_decay(p, g, kind, lr, weight_decay=0.0, beta1=0.9, beta2=0.999,
+                         eps=1e-8, step=1, exp_avg=None, exp_avg_sq=None):
+    # Adam with L2 decay folded into the gradient instead of AdamW's decoupled decay
+    if kind != "adamw":
+        return _orig_opt(p, g, kind, lr, weight_decay, beta1, beta2, eps, step, exp_avg,
+                         exp_avg_sq)
+    p = np.asarray(p, dtype=np.float64)
+    return _orig_opt(p, np.asarray(g) + weight_decay * p, kind, lr, 0.0, beta1, beta2, eps, step,
+                     exp_avg, exp_avg_sq)
+
+
+def _sgd_ascends(p, g, kind, lr, weight_decay=0.0, *a, **k):
+    if kind != "sgd":
+        return _orig_opt(p, g, kind, lr, weight_decay, *a, **k)
+    return np.asarray(p) + lr * (np.asarray(g) + weight_decay * np.asarray(p)), None, None
+
+
 MUTATIONS = {
+    "adamw_without_bias_correction": ("optimizer_step", _adamw_without_bias_correction),
+    "adamw_coupled_weight_decay": ("optimizer_step", _adamw_coupled_decay),
+    "sgd_ascends": ("optimizer_step", _sgd_ascends),
     "embed_backward_keeps_padding": ("embed_backward", _embed_bwd_keeps_padding),
     "embed_backward_overwrites_repeats": ("embed_backward", _embed_bwd_overwrites),
     "embed_forward_id_off_by_one": ("embed_forward", _embed_fwd_off_by_one),

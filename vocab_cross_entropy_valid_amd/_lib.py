@@ -21,6 +21,9 @@ LCE_ERR_WORKSPACE = 3
 LCE_ERR_LABEL_RANGE = 4
 LCE_ERR_HIP = 5
 
+LCE_OPT_SGD = 1
+LCE_OPT_ADAMW = 2
+
 LCE_F32 = 0
 LCE_BF16 = 1
 LCE_MEAN = 0
@@ -28,6 +31,13 @@ LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
                   "bwd_g", "dh", "dw", "gemm", "embed")
+
+class LceOptimizer(ctypes.Structure):
+    """lce_optimizer of include/lce.h."""
+    _fields_ = [("kind", ctypes.c_int), ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("step", ctypes.c_int64)]
+
 
 # name -> (restype, argtypes), in the order of include/lce.h
 _P = ctypes.c_void_p
@@ -40,6 +50,8 @@ SIGNATURES = {
                            _P, _P, _SZ, _P]),
     "lce_backward": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
                             _P, _P, _INT, _P, _SZ, _P]),
+    "lce_backward_step": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
+                                 _P, _P, _P, _P, ctypes.POINTER(LceOptimizer), _P, _SZ, _P]),
     "lce_forward_shard": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _INT, _P, _P, _P,
                                  _P, _P, _P, _P, _SZ, _P]),
     "lce_lse_merge": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
@@ -116,6 +128,15 @@ def lce_backward(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, 
     _check(load().lce_backward(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d,
                                V, dtype, grad_out, reduction, dH, dW, accumulate_dW,
                                workspace, workspace_bytes, stream), "lce_backward")
+
+
+def lce_backward_step(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, dtype,
+                      grad_out, reduction, dH, W_master, exp_avg, exp_avg_sq, opt, workspace,
+                      workspace_bytes, stream) -> None:
+    _check(load().lce_backward_step(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d,
+                                    V, dtype, grad_out, reduction, dH, W_master, exp_avg,
+                                    exp_avg_sq, ctypes.byref(opt), workspace, workspace_bytes,
+                                    stream), "lce_backward_step")
 
 
 def lce_forward_shard(H, W_shard, labels, ignore_index, N, d, V_total, v_begin, V_shard, dtype,

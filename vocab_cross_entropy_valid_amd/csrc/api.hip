@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -337,7 +338,7 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
                          int64_t N, int64_t d, int64_t V_total, int64_t y_off, int64_t V, int dtype,
                          const float* grad_out, int reduction, float* dH, int accumulate_dH,
                          float* dW, int accumulate_dW, void* workspace, size_t workspace_bytes,
-                         hipStream_t s) {
+                         hipStream_t s, const lce::DwArgs* step = nullptr) {
   const Plan p = make_plan(N, d, V, dtype);
   lce_status st = check_workspace(p, workspace, workspace_bytes);
   if (st != LCE_OK) return st;
@@ -441,6 +442,20 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       wa.V = V;
       wa.dW = dW;
       wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
+      if (step) {  // optimizer epilogue instead of the dW store
+        wa.opt_kind = step->opt_kind;
+        wa.lr = step->lr;
+        wa.wd = step->wd;
+        wa.beta1 = step->beta1;
+        wa.beta2 = step->beta2;
+        wa.eps = step->eps;
+        wa.bc1 = step->bc1;
+        wa.bc2s = step->bc2s;
+        wa.master = step->master;
+        wa.exp_avg = step->exp_avg;
+        wa.exp_avg_sq = step->exp_avg_sq;
+        wa.w16 = step->w16;
+      }
       // dH first: right after the recompute the G block is still largely in
       // the Infinity Cache (measured faster; dW's time does not depend on
       // the order)
@@ -474,6 +489,59 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
   return backward_impl(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, 0, V,
                        dtype, grad_out, reduction, dH, 0, dW, accumulate_dW, workspace,
                        workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int64_t ignore_index,
+                             const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
+                             int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
+                             int reduction, float* dH, float* W_master, float* exp_avg,
+                             float* exp_avg_sq, const lce_optimizer* opt, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (reduction != LCE_MEAN && reduction != LCE_SUM)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
+  if (!W || !valid_count || !grad_out || !opt)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and opt must not be NULL");
+  if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
+  // each dW tile must be complete in one launch: every valid row in one token chunk
+  if (N > kChunkMax)
+    return fail(LCE_ERR_UNSUPPORTED, "the fused update needs N <= " + std::to_string(kChunkMax) +
+                                         " (all rows in one token chunk)");
+  if (dtype == LCE_BF16 && !W_master)
+    return fail(LCE_ERR_INVALID_ARG, "bf16 weights need fp32 master weights (W_master)");
+  if (!(opt->lr >= 0.f) || !(opt->weight_decay >= 0.f))
+    return fail(LCE_ERR_INVALID_ARG, "lr and weight_decay must be >= 0");
+  lce::DwArgs step{};
+  if (opt->kind == LCE_OPT_SGD) {
+    step.opt_kind = 1;
+  } else if (opt->kind == LCE_OPT_ADAMW) {
+    if (!exp_avg || !exp_avg_sq)
+      return fail(LCE_ERR_INVALID_ARG, "AdamW needs exp_avg and exp_avg_sq");
+    if (opt->step < 1) return fail(LCE_ERR_INVALID_ARG, "AdamW step must be >= 1");
+    if (!(opt->beta1 >= 0.f && opt->beta1 < 1.f && opt->beta2 >= 0.f && opt->beta2 < 1.f) ||
+        !(opt->eps > 0.f))
+      return fail(LCE_ERR_INVALID_ARG, "AdamW needs betas in [0, 1) and eps > 0");
+    step.opt_kind = 2;
+    step.beta1 = opt->beta1;
+    step.beta2 = opt->beta2;
+    step.eps = opt->eps;
+    step.bc1 = (float)(1.0 - std::pow((double)opt->beta1, (double)opt->step));
+    step.bc2s = (float)std::sqrt(1.0 - std::pow((double)opt->beta2, (double)opt->step));
+    step.exp_avg = exp_avg;
+    step.exp_avg_sq = exp_avg_sq;
+  } else {
+    return fail(LCE_ERR_INVALID_ARG, "opt->kind must be LCE_OPT_SGD or LCE_OPT_ADAMW");
+  }
+  step.lr = opt->lr;
+  step.wd = opt->weight_decay;
+  step.master = W_master ? W_master : (float*)W;
+  step.w16 = dtype == LCE_BF16 ? (uint16_t*)W : nullptr;
+  return backward_impl(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, 0, V,
+                       dtype, grad_out, reduction, dH, 0, nullptr, 0, workspace, workspace_bytes,
+                       (hipStream_t)stream, &step);
 }
 
 lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t* labels,

@@ -62,6 +62,14 @@ struct DwArgs {
   int64_t c0, v0, V;
   float* dW;
   int accumulate;
+  // optimizer epilogue (opt_kind > 0): the dW tile is applied here and never
+  // stored.  bc1 = 1 - beta1^t, bc2s = sqrt(1 - beta2^t).
+  int opt_kind;  // 0 none (the zero-initialised default), 1 SGD, 2 AdamW
+  float lr, wd, beta1, beta2, eps, bc1, bc2s;
+  float* master;      // fp32 [V, d] weights the update applies to
+  float* exp_avg;     // fp32 [V, d] (AdamW)
+  float* exp_avg_sq;  // fp32 [V, d] (AdamW)
+  uint16_t* w16;      // bf16 [V, d] operand copy refreshed from master (nullable)
 };
 
 struct TransposeArgs {

@@ -325,7 +325,7 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
 // hidden units (B = H^T rows); K runs over the chunk's valid tokens only
 // (the count is read on the device).  Each workgroup owns its dW tile, so
 // no atomics are needed and the result is deterministic.
-template <typename T>
+template <typename T, int kStep>  // 0: store dW; 1: SGD; 2: AdamW
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -356,6 +356,59 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 
   const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   const int m_base = tm * kTile + wa * kHalf + 4 * h;
+  if constexpr (kStep > 0) {
+    // The gradient tile goes straight into the optimizer (no dW table; OjasX
+    // page, core technology: no persistent .grad buffers).  PyTorch's
+    // formulas: SGD p -= lr (g + wd p); AdamW p *= 1 - lr wd, m = b1 m +
+    // (1 - b1) g, v = b2 v + (1 - b2) g^2, p -= (lr / bc1) m / (sqrt(v) / bc2s
+    // + eps).  Batches of 16 values per lane keep the loads in flight together.
+    const int64_t row0 = a.v0;
+    constexpr int kB = kStep == 2 ? 8 : 16;  // values per lane in flight (AdamW holds three)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int i0 = 0; i0 < 16; i0 += kB) {
+          const int n = n_base + 32 * nt;
+          float p[kB], m[kB], v[kB];
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+            const int i = i0 + b;
+            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+            const bool in = ml < nv && n < a.d;
+            const int64_t o = (row0 + ml) * a.d + n;
+            p[b] = in ? a.master[o] : 0.f;
+            if constexpr (kStep == 2) {
+              m[b] = in ? a.exp_avg[o] : 0.f;
+              v[b] = in ? a.exp_avg_sq[o] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+            const int i = i0 + b;
+            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+            if (ml >= nv || n >= a.d) continue;
+            const int64_t o = (row0 + ml) * a.d + n;
+            const float g = acc[mt][nt][i];
+            float q;
+            if constexpr (kStep == 1) {
+              q = p[b] - a.lr * (g + a.wd * p[b]);
+            } else {
+              const float pd = p[b] * (1.f - a.lr * a.wd);
+              const float m1 = a.beta1 * m[b] + (1.f - a.beta1) * g;
+              const float v1 = a.beta2 * v[b] + (1.f - a.beta2) * g * g;
+              q = pd - (a.lr / a.bc1) * m1 / (__builtin_sqrtf(v1) / a.bc2s + a.eps);
+              a.exp_avg[o] = m1;
+              a.exp_avg_sq[o] = v1;
+            }
+            a.master[o] = q;
+            if (a.w16) a.w16[o] = (uint16_t)bf16_bits(q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    return;
+  }
   float* out0 = a.dW + a.v0 * a.d;
   // read-modify-write (accumulate) in four batches of 32 values, as for dH
 #pragma unroll
@@ -398,7 +451,13 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  dw_tile<T>(a, blockIdx.x, lds);
+  dw_tile<T, 0>(a, blockIdx.x, lds);
+}
+
+template <typename T, int kOpt>
+__global__ __launch_bounds__(kThreads, 1) void dw_step_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  dw_tile<T, kOpt>(a, blockIdx.x, lds);
 }
 
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
@@ -414,10 +473,21 @@ hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
 hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s) {
   const int TM = (int)(a.Vs / kTile), TN = (int)((a.d + kTile - 1) / kTile);
   const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
-  if (dtype == 1)
+  if (a.opt_kind == 1) {
+    if (dtype == 1)
+      hipLaunchKernelGGL((dw_step_kernel<bf16_t, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((dw_step_kernel<float, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (a.opt_kind == 2) {
+    if (dtype == 1)
+      hipLaunchKernelGGL((dw_step_kernel<bf16_t, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((dw_step_kernel<float, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (dtype == 1) {
     hipLaunchKernelGGL(dw_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(dw_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -135,6 +135,48 @@ def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, fwd: Forwar
     return dH, dW
 
 
+# ----------------------------------------------- fused optimizer update
+
+def backward_step(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, fwd: ForwardOut,
+                  kind: str, lr: float, weight_decay: float = 0.0, betas=(0.9, 0.999),
+                  eps: float = 1e-8, step: int = 1, W_master: Optional[torch.Tensor] = None,
+                  exp_avg: Optional[torch.Tensor] = None,
+                  exp_avg_sq: Optional[torch.Tensor] = None,
+                  grad_out: Optional[torch.Tensor] = None, reduction: str = "mean",
+                  ignore_index: int = -100, dH: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lce_backward_step: dH is returned, W (and W_master, exp_avg, exp_avg_sq)
+    are updated in place by SGD (kind='sgd') or AdamW (kind='adamw')."""
+    _check_inputs(H, W, labels)
+    N, d = H.shape
+    V = W.shape[0]
+    dev = H.device
+    if reduction not in _RED:
+        raise ValueError("reduction must be 'mean' or 'sum'")
+    kinds = {"sgd": _lib.LCE_OPT_SGD, "adamw": _lib.LCE_OPT_ADAMW}
+    if kind not in kinds:
+        raise ValueError("kind must be 'sgd' or 'adamw'")
+    for t in (W_master, exp_avg, exp_avg_sq):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (V, d)
+                              or not t.is_contiguous()):
+            raise ValueError("W_master, exp_avg and exp_avg_sq must be contiguous float32 [V, d]")
+    if grad_out is None:
+        grad_out = torch.ones(1, dtype=torch.float32, device=dev)
+    grad_out = grad_out.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    if workspace is None:
+        workspace = alloc_workspace(N, d, V, H.dtype, dev)
+    if dH is None:
+        dH = torch.empty(N, d, dtype=torch.float32, device=dev)
+    opt = _lib.LceOptimizer(kind=kinds[kind], lr=lr, weight_decay=weight_decay,
+                            beta1=betas[0], beta2=betas[1], eps=eps, step=step)
+    _lib.lce_backward_step(_ptr(H), _ptr(W), _ptr(labels), int(ignore_index), _ptr(fwd.lse),
+                           _ptr(fwd.valid_idx), _ptr(fwd.valid_count), N, d, V, _DTYPES[H.dtype],
+                           _ptr(grad_out), _RED[reduction], _ptr(dH), _ptr(W_master),
+                           _ptr(exp_avg), _ptr(exp_avg_sq), opt, _ptr(workspace),
+                           workspace.numel(), _stream(dev))
+    return dH
+
+
 # ------------------------------------------------------ vocabulary shards
 
 @dataclasses.dataclass
