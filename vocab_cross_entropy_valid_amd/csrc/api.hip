@@ -461,7 +461,8 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       // the order)
       e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
       if (e != hipSuccess) return hip_fail(e, "dH launch");
-      e = run(LCE_K_DW, s, [&] { return lce::launch_dw(wa, dtype, s); });
+      e = run(LCE_K_DW, s,
+              [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
       if (e != hipSuccess) return hip_fail(e, "dW launch");
     }
   }

@@ -39,6 +39,7 @@ struct BwdGArgs {
   void* G;         // [C][ldG]
   void* GT;        // [Vs][ldGT]
   int64_t ldG, ldGT;  // row strides in elements (padded off powers of two)
+  int nslots;      // tile slots, one workgroup each
 };
 
 struct DhArgs {
@@ -62,6 +63,7 @@ struct DwArgs {
   int64_t c0, v0, V;
   float* dW;
   int accumulate;
+  int nslots;      // tile slots (the launch walks them persistently)
   // optimizer epilogue (opt_kind > 0): the dW tile is applied here and never
   // stored.  bc1 = 1 - beta1^t, bc2s = sqrt(1 - beta2^t).
   int opt_kind;  // 0 none (the zero-initialised default), 1 SGD, 2 AdamW
@@ -104,9 +106,10 @@ hipError_t launch_loss_reduce(const float* loss, const int32_t* gather, const in
 hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
                                float* dH, int64_t d, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
-hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s);
+hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
-hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s);
+// grid: persistent workgroups (a multiple of 8; each walks slots grid apart)
+hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s);
 // Workspace layout of the embedding backward (byte offsets, 256-aligned).
 struct EmbedPlan {
   int end_bit;  // sort key bits: 2^end_bit > V (V itself is the padding sentinel)

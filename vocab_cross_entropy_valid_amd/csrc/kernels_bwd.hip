@@ -9,6 +9,8 @@
 // logits in backward).  Here the chunk is a C-row slice of the compact token
 // index times a Vs-entry slice of the vocabulary, so the workspace is
 // O((C + d) * (Vs + C)) and independent of N and V.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -103,8 +105,7 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
 // past the valid tokens are 0.  G is written row-major [token][vocab] for the
 // dH contraction and transposed [vocab][token] for the dW contraction.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+__device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   const int TM = (int)((nv + kTile - 1) / kTile);
   const int TN = (int)((n_act + kTile - 1) / kTile);
   int tm, tn;
-  if (!xcd_tile(blockIdx.x, TM, TN, 8, 4, tm, tn)) return;
+  if (!xcd_tile(slot, TM, TN, 8, 4, tm, tn)) return;
 
   const int64_t ld = a.d * Elem<T>::kSize;
   RowSource as{(const char*)a.W, ld, nullptr, a.v0 + (int64_t)tm * kTile, a.V, 0};
@@ -237,10 +238,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
   }
 }
 
-hipError_t launch_bwd_g(const BwdGArgs& a, int dtype, hipStream_t s) {
+// One tile per workgroup (a persistent loop here costs more than it saves:
+// the loop pushes the kernel's register use into spills in the main loop).
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(BwdGArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  bwd_g_tile<T>(a, blockIdx.x, lds);
+}
+
+hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s) {
   const int TM = (int)(a.Vs / kTile), TN = (int)(a.C / kTile);
   const int nsb = ((TM + 7) / 8) * ((TN + 3) / 4);
-  const int grid = 256 * ((nsb + 7) / 8);
+  a.nslots = 256 * ((nsb + 7) / 8);
+  const int grid = a.nslots;  // one workgroup per slot
   if (dtype == 1)
     hipLaunchKernelGGL(bwd_g_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
   else
@@ -451,13 +461,22 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  dw_tile<T, 0>(a, blockIdx.x, lds);
+  // persistent: the next tile starts without waiting for a new workgroup to
+  // be dispatched (1.7% faster than one tile per workgroup; the previous
+  // tile's stores still count in the next tile's first vmcnt wait)
+  for (int slot = blockIdx.x; slot < a.nslots; slot += gridDim.x) {
+    dw_tile<T, 0>(a, slot, lds);
+    __syncthreads();
+  }
 }
 
 template <typename T, int kOpt>
 __global__ __launch_bounds__(kThreads, 1) void dw_step_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  dw_tile<T, kOpt>(a, blockIdx.x, lds);
+  for (int slot = blockIdx.x; slot < a.nslots; slot += gridDim.x) {
+    dw_tile<T, kOpt>(a, slot, lds);
+    __syncthreads();
+  }
 }
 
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
@@ -470,9 +489,10 @@ hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const DwArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s) {
   const int TM = (int)(a.Vs / kTile), TN = (int)((a.d + kTile - 1) / kTile);
-  const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
+  a.nslots = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
+  grid = std::min(grid, a.nslots);
   if (a.opt_kind == 1) {
     if (dtype == 1)
       hipLaunchKernelGGL((dw_step_kernel<bf16_t, 1>), dim3(grid), dim3(kThreads), 0, s, a);

@@ -224,9 +224,11 @@ EmbedPlan make_embed_plan(int64_t N, int64_t d, int64_t V) {
   p.end_bit = 1;
   while (p.end_bit < 32 && ((uint64_t)1 << p.end_bit) <= (uint64_t)V) ++p.end_bit;
   size_t sort_bytes = 0;
-  rocprim::radix_sort_pairs(nullptr, sort_bytes, (uint32_t*)nullptr, (uint32_t*)nullptr,
-                            (int32_t*)nullptr, (int32_t*)nullptr, (unsigned)n, 0,
-                            (unsigned)p.end_bit, (hipStream_t)0);
+  // size query only (no launch); it needs a device, and reports 0 without one
+  if (rocprim::radix_sort_pairs(nullptr, sort_bytes, (uint32_t*)nullptr, (uint32_t*)nullptr,
+                                (int32_t*)nullptr, (int32_t*)nullptr, (unsigned)n, 0,
+                                (unsigned)p.end_bit, (hipStream_t)0) != hipSuccess)
+    sort_bytes = 0;
   size_t o = 0;
   p.off_key = o; o += al(n * 4);
   p.off_val = o; o += al(n * 4);
