@@ -222,3 +222,50 @@ def test_workspace_is_the_only_scratch():
     extra = torch.cuda.memory_stats()["requested_bytes.all.peak"] - before - outputs
     # only the 4-byte grad_out scalar remains
     assert extra <= 1024, extra
+
+
+def test_empty_input():
+    """N = 0: no valid row, loss sum 0, mean NaN, dW written as zeros; the
+    shard, merge and embedding entry points accept it too."""
+    import torch
+    from vocab_cross_entropy_valid_amd import torch_api
+    announce("empty input")
+    dev = torch.device("cuda:0")
+    H = torch.empty(0, 128, dtype=torch.bfloat16, device=dev)
+    W = torch.randn(700, 128, device=dev).to(torch.bfloat16)
+    y = torch.empty(0, dtype=torch.int64, device=dev)
+    fwd = torch_api.forward(H, W, y)
+    assert int(fwd.valid_count.item()) == 0
+    assert float(fwd.loss_sum.item()) == 0.0 and np.isnan(float(fwd.loss_mean.item()))
+    dW = torch.full((700, 128), 3.0, device=dev)
+    dH, dW = torch_api.backward(H, W, y, fwd, dW=dW)
+    torch.cuda.synchronize()
+    assert dH.shape == (0, 128) and float(dW.abs().max()) == 0.0
+    p = torch_api.forward_shard(H, W[:300].contiguous(), y, 700, 0)
+    m = torch_api.lse_merge(p.part_max.reshape(1, 0), p.part_sum.reshape(1, 0),
+                            p.part_target.reshape(1, 0), p.valid_idx, p.valid_count)
+    assert float(m.loss_sum.item()) == 0.0 and np.isnan(float(m.loss_mean.item()))
+    e = torch_api.embed_forward(W, y, 0)
+    assert e.X.shape == (0, 128) and int(e.valid_count.item()) == 0
+    dWe = torch.full((700, 128), 2.0, device=dev)
+    torch_api.embed_backward(torch.empty(0, 128, device=dev), y, e, dWe, accumulate_dW=False)
+    assert float(dWe.abs().max()) == 0.0
+
+
+def test_tiny_vocabulary_and_minimum_d():
+    """V smaller than one 32-row MFMA block, d at its minimum (64)."""
+    announce("tiny vocabulary")
+    H, W, y = workloads.custom(97, 64, 5, seed=81)
+    _check(run_path(H, W, y, "bf16"), H, W, y, "bf16")
+
+
+def test_labels_at_the_vocabulary_tail():
+    """Labels on the last entries of a ragged vocabulary (V % 256 != 0) and on
+    entry 0; the last tile's columns past V must not leak into the sums."""
+    announce("vocabulary tail labels")
+    H, W, y = workloads.custom(600, 128, 1000, seed=82, ignore_frac=0.0)
+    y[:200] = 999
+    y[200:300] = 998
+    y[300:350] = 0
+    y[350:360] = 768                 # first entry of the last tile
+    _check(run_path(H, W, y, "bf16"), H, W, y, "bf16")

@@ -192,11 +192,13 @@ size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype) {
 namespace {
 
 // Forward over vocabulary rows [y_off, y_off + V) held by W (the whole
-// vocabulary when y_off = 0 and V = V_total).  With part_max set, writes the
-// shard partials instead of loss / lse and skips the reduction.
-lce_status forward_impl(const void* H, const void* W, const int64_t* labels, int64_t ignore_index,
-                        int64_t N, int64_t d, int64_t V_total, int64_t y_off, int64_t V, int dtype,
-                        float* loss, float* lse, float* part_max, float* part_sum,
+// vocabulary when y_off = 0 and V = V_total).  In shard mode, writes the
+// shard partials instead of loss / lse and skips the reduction (loss_sum is
+// then NULL).  The mode is passed, not inferred from part_max: with N = 0 the
+// partial arrays may legitimately be NULL.
+lce_status forward_impl(bool shard, const void* H, const void* W, const int64_t* labels,
+                        int64_t ignore_index, int64_t N, int64_t d, int64_t V_total, int64_t y_off,
+                        int64_t V, int dtype, float* loss, float* lse, float* part_max, float* part_sum,
                         float* part_target, int32_t* valid_idx, int32_t* valid_count,
                         double* loss_sum, float* loss_mean, int32_t* err_flag, void* workspace,
                         size_t workspace_bytes, hipStream_t s) {
@@ -204,7 +206,6 @@ lce_status forward_impl(const void* H, const void* W, const int64_t* labels, int
   lce_status st = check_workspace(p, workspace, workspace_bytes);
   if (st != LCE_OK) return st;
   char* ws = (char*)workspace;
-  const bool shard = part_max != nullptr;
 
   // ignored rows: loss = lse = 0, or part_max = part_sum = 0 for a shard
   hipError_t e = run(LCE_K_COMPACT, s, [&] {
@@ -272,7 +273,7 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
     return fail(LCE_ERR_INVALID_ARG, "W, valid_count, loss_sum and err_flag must not be NULL");
   if (N > 0 && (!H || !labels || !loss || !lse || !valid_idx))
     return fail(LCE_ERR_INVALID_ARG, "H, labels, loss, lse and valid_idx must not be NULL");
-  return forward_impl(H, W, labels, ignore_index, N, d, V, 0, V, dtype, loss, lse, nullptr,
+  return forward_impl(false, H, W, labels, ignore_index, N, d, V, 0, V, dtype, loss, lse, nullptr,
                       nullptr, nullptr, valid_idx, valid_count, loss_sum, loss_mean, err_flag,
                       workspace, workspace_bytes, (hipStream_t)stream);
 }
@@ -293,7 +294,7 @@ lce_status lce_forward_shard(const void* H, const void* W_shard, const int64_t* 
   if (N > 0 && (!H || !labels || !part_max || !part_sum || !part_target || !valid_idx))
     return fail(LCE_ERR_INVALID_ARG,
                 "H, labels, part_max, part_sum, part_target and valid_idx must not be NULL");
-  return forward_impl(H, W_shard, labels, ignore_index, N, d, V_total, v_begin, V_shard, dtype,
+  return forward_impl(true, H, W_shard, labels, ignore_index, N, d, V_total, v_begin, V_shard, dtype,
                       nullptr, nullptr, part_max, part_sum, part_target, valid_idx, valid_count,
                       nullptr, nullptr, err_flag, workspace, workspace_bytes, (hipStream_t)stream);
 }
