@@ -265,7 +265,7 @@ hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s) {
 // tokens' original positions through valid_idx.  beta = 0 on the first
 // vocabulary block, 1 afterwards.
 template <typename T>
-__device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, int* rows) {
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -284,11 +284,6 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
 
-  if (tid < kTile) {
-    const int64_t m = (int64_t)tm * kTile + tid;
-    rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
-  }
-  __syncthreads();
   // rows past the valid count clamp to the last valid row (cache hits)
   // instead of streaming the block's unused rows
   RowSource as{(const char*)a.G, a.ldG * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, n_act, 0};
@@ -297,7 +292,15 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
   const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   Acc acc;
   zero_acc(acc);
-  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: rows[] visible
+  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: LDS is free
+
+  // destination rows of the tile's tokens, in the (now free) stage buffers
+  int* rows = (int*)lds;
+  if (tid < kTile) {
+    const int64_t m = (int64_t)tm * kTile + tid;
+    rows[tid] = m < n_act ? a.valid_idx[a.c0 + m] : -1;
+  }
+  __syncthreads();
 
   const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   // Read-modify-write in four batches (one per mt): all 32 loads of a batch
@@ -454,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   // One LDS object only: with a second __shared__ array the compiler can no
   // longer tell the direct-to-LDS loads of the next stage from the fragment
   // reads of the current one and waits for every load right after issuing it.
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds + kTile * sizeof(int)];
-  dh_tile<T>(a, blockIdx.x, lds, (int*)(lds + kMainLds));
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  dh_tile<T>(a, blockIdx.x, lds);
 }
 
 template <typename T>

@@ -101,8 +101,10 @@ hipError_t launch_compact(const int64_t* labels, int64_t N, int64_t ignore_index
 // the two waves that split the tile's vocabulary.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds + kTile * 3 * sizeof(float)];
-  float* mg = (float*)(lds + kMainLds);
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  // wave-pair merge area: used only after an item's last main loop, which
+  // ends with a barrier, so it shares the stage buffers
+  float* mg = (float*)lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
