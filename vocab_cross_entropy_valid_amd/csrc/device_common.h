@@ -185,25 +185,24 @@ __device__ __forceinline__ void load_op(char* buf, const RowPtrs& p, uint32_t kb
                                              p.off[i], kbyte, 0, 0);
 }
 
-// Fragment reads of MFMA step s (32 bytes of K).  base = per-lane offset of
-// row (wave half + lane % 32), slot bits holding h ^ (r & 7) ^ (r >> 3);
-// step s XORs 2 s into the slot, mt adds 32 rows (4 KB) and XORs 4 into the
-// slot for odd mt (slot bits are byte-offset bits 4..6, hence XOR, not add).
-__device__ __forceinline__ void load_frags(u32x4 (&f)[4], const char* op, int base, int s) {
-  const int e = base ^ (32 * s);
-  const int o = base ^ ((32 * s) ^ 64);
-  f[0] = *(const u32x4*)(op + e);
-  f[1] = *(const u32x4*)(op + o + 4096);
-  f[2] = *(const u32x4*)(op + e + 8192);
-  f[3] = *(const u32x4*)(op + o + 12288);
-}
-
-// B fragments of a 64-row wave slice: two 32-row blocks
-__device__ __forceinline__ void load_frags_b(u32x4 (&f)[kNT], const char* op, int base, int s) {
-  const int e = base ^ (32 * s);
-  const int o = base ^ ((32 * s) ^ 64);
-  f[0] = *(const u32x4*)(op + e);
-  f[1] = *(const u32x4*)(op + o + 4096);
+// Fragment reads of MFMA step s (32 bytes of K): 4 A fragments (32-row
+// blocks mt) and 2 B fragments.  a_base / b_base = per-lane offset of row
+// (wave slice + lane % 32), slot bits holding h ^ (r & 7) ^ (r >> 3); step s
+// XORs 2 s into the slot, a 32-row block adds 4 KB and XORs 4 into the slot
+// for odd blocks (slot bits are byte-offset bits 4..6, hence XOR, not add).
+// Issued in the order the MFMAs consume them (mma_step runs (mt, nt) =
+// (0,0) (0,1) (1,0) (1,1) ...): the first MFMA of a step then waits for 2 of
+// the 6 reads instead of 5 (1.5-6% faster).
+__device__ __forceinline__ void load_frags_ab(u32x4 (&fa)[4], u32x4 (&fb)[kNT], const char* ca,
+                                              const char* cb, int a_base, int b_base, int s) {
+  const int ea = a_base ^ (32 * s), oa = a_base ^ ((32 * s) ^ 64);
+  const int eb = b_base ^ (32 * s), ob = b_base ^ ((32 * s) ^ 64);
+  fa[0] = *(const u32x4*)(ca + ea);
+  fb[0] = *(const u32x4*)(cb + eb);
+  fb[1] = *(const u32x4*)(cb + ob + 4096);
+  fa[1] = *(const u32x4*)(ca + oa + 4096);
+  fa[2] = *(const u32x4*)(ca + ea + 8192);
+  fa[3] = *(const u32x4*)(ca + oa + 12288);
 }
 
 typedef f32x16 Acc[4][kNT];
@@ -284,20 +283,14 @@ __device__ __forceinline__ void stage_body(Acc& acc, char* lds, int k, int sa, i
   const char* ca = lds + kLdsA + sa * kOpBytes;
   const char* cb = lds + kLdsB + (k & 1) * kOpBytes;
   u32x4 fa[3][4], fb[3][kNT];
-  load_frags(fa[0], ca, a_base, 0);
-  load_frags_b(fb[0], cb, b_base, 0);
+  load_frags_ab(fa[0], fb[0], ca, cb, a_base, b_base, 0);
   if (kLB) load_op(lds + kLdsB + ((k + 1) & 1) * kOpBytes, pb, (uint32_t)((k + 1) * kRowBytes), wave_u);
   if (kLA) load_op(lds + kLdsA + sa2 * kOpBytes, pa, (uint32_t)((k + 2) * kRowBytes), wave_u);
   if (kPrev) mma_step<T>(acc, f3a, f3b);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
-    if (s < 2) {
-      load_frags(fa[s + 1], ca, a_base, s + 1);
-      load_frags_b(fb[s + 1], cb, b_base, s + 1);
-    } else {
-      load_frags(f3a, ca, a_base, 3);
-      load_frags_b(f3b, cb, b_base, 3);
-    }
+    if (s < 2) load_frags_ab(fa[s + 1], fb[s + 1], ca, cb, a_base, b_base, s + 1);
+    else load_frags_ab(f3a, f3b, ca, cb, a_base, b_base, 3);
     mma_step<T>(acc, fa[s], fb[s]);
   }
   if constexpr (sizeof(T) == 2) schedule_body<kPrev, (kLB ? 4 : 0) + (kLA ? 4 : 0)>();
