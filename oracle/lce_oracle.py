@@ -379,3 +379,54 @@ def optimizer_step(p, g, kind: str, lr: float, weight_decay: float = 0.0, beta1:
     bc2 = 1.0 - beta2 ** step
     p = p - (lr / bc1) * m / (np.sqrt(v) / np.sqrt(bc2) + eps)
     return p, m, v
+
+
+# --------------------------------------------------------------------------
+# attention through an online softmax
+# --------------------------------------------------------------------------
+#
+# "OjasX 0.6.1", section 核心技术 / "Core Technology": the [B, H, S, S] attention
+# score matrix is never stored; score tiles stream through registers and
+# on-chip memory, and the running max / normaliser recurrence (the page's
+# Online Softmax paragraph) gives exactly the full-softmax result.  The
+# operation itself is stated on the KV-cache page (KV Cache基础):
+# Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V.  Reading taken here: the
+# causal mask of a decoder (a query attends to keys at its own position and
+# before) as an option, scale 1 / sqrt(d) by default.  The oracle is the
+# definition: full scores, full softmax, one matrix product.
+
+
+@dataclasses.dataclass
+class AttentionResult:
+    O: np.ndarray     # [B, H, S, D] float64
+    lse: np.ndarray   # [B, H, S] natural-log sum of exp of the (masked, scaled) scores
+
+
+def attention_scores(Q, K, scale: float) -> np.ndarray:
+    """scale * Q K^T over the last two axes, float64."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    return (Q @ np.swapaxes(K, -1, -2)) * scale
+
+
+def causal_allowed(S: int) -> np.ndarray:
+    """[S, S] boolean: key k may be attended by query q iff k <= q."""
+    q = np.arange(S)[:, None]
+    k = np.arange(S)[None, :]
+    return k <= q
+
+
+def attention_forward(Q, K, V, causal: bool = False, scale: Optional[float] = None):
+    """O = softmax(scale Q K^T [masked]) V and the per-row logsumexp."""
+    Q = np.asarray(Q, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    S, D = Q.shape[-2], Q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    Z = attention_scores(Q, K, scale)
+    if causal:
+        Z = np.where(causal_allowed(S), Z, -np.inf)
+    lead = Z.shape[:-1]
+    lse = logsumexp_rows(Z.reshape(-1, Z.shape[-1])).reshape(lead)
+    P = np.exp(Z - lse[..., None])
+    return AttentionResult(O=P @ V, lse=lse)

@@ -450,6 +450,111 @@ def pin_adamw_matches_torch(o):
     np.testing.assert_allclose(v1, opt.state[t]["exp_avg_sq"].numpy(), rtol=1e-13)
 
 
+# ---------------------------------------------------------------- attention
+#
+# The attention oracle (online-softmax attention, "OjasX 0.6.1", section
+# 核心技术 / "Core Technology"; softmax(Q K^T / sqrt(d)) V as the KV-cache page
+# writes it) against closed forms, invariants and torch's own fp64 routine.
+
+def _qkv(seed, B=2, H=3, S=7, D=8, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal((B, H, S, D)) * scale for _ in range(3)]
+
+
+def pin_attn_uniform(o):
+    """Q = 0: every allowed key has the same score, so O is the mean of the
+    allowed V rows and lse = log(number of allowed keys)."""
+    _, K, V = _qkv(501)
+    Q = np.zeros_like(K)
+    S = K.shape[-2]
+    r = o.attention_forward(Q, K, V, causal=False)
+    np.testing.assert_allclose(r.O, np.broadcast_to(V.mean(axis=-2, keepdims=True), V.shape),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r.lse, np.full(r.lse.shape, np.log(S)), rtol=1e-14)
+    r = o.attention_forward(Q, K, V, causal=True)
+    counts = np.arange(1, S + 1, dtype=np.float64)
+    prefix_mean = np.cumsum(V, axis=-2) / counts[:, None]
+    np.testing.assert_allclose(r.O, prefix_mean, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r.lse, np.broadcast_to(np.log(counts), r.lse.shape), rtol=1e-14)
+
+
+def pin_attn_single_key(o):
+    """One key: O = V and lse = the single scaled score, causal or not."""
+    Q, K, V = _qkv(502, S=1, D=16)
+    for causal in (False, True):
+        r = o.attention_forward(Q, K, V, causal=causal)
+        np.testing.assert_allclose(r.O, V, rtol=1e-14)
+        np.testing.assert_allclose(r.lse, (Q * K).sum(-1) / 4.0, rtol=1e-13)
+
+
+def pin_attn_key_shift(o):
+    """Adding one vector u to every key adds scale q.u to each score of row q:
+    O is unchanged, lse moves by exactly that amount."""
+    Q, K, V = _qkv(503, S=9, D=16)
+    u = np.random.default_rng(5031).standard_normal(16) * 3.0
+    for causal in (False, True):
+        a = o.attention_forward(Q, K, V, causal=causal)
+        b = o.attention_forward(Q, K + u, V, causal=causal)
+        np.testing.assert_allclose(b.O, a.O, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(b.lse - a.lse, (Q @ u) / 4.0, rtol=1e-11, atol=1e-12)
+
+
+def pin_attn_permutation(o):
+    """Without a mask, permuting keys and values together changes nothing."""
+    Q, K, V = _qkv(504, S=11)
+    perm = np.random.default_rng(5041).permutation(11)
+    a = o.attention_forward(Q, K, V)
+    b = o.attention_forward(Q, K[..., perm, :], V[..., perm, :])
+    np.testing.assert_allclose(b.O, a.O, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(b.lse, a.lse, rtol=1e-13)
+
+
+def pin_attn_rows_sum_to_one(o):
+    """V = 1: each output is a convex combination of ones, so exactly 1."""
+    Q, K, _ = _qkv(505, S=13, scale=2.0)
+    V = np.ones_like(Q)
+    for causal in (False, True):
+        np.testing.assert_allclose(o.attention_forward(Q, K, V, causal=causal).O, 1.0,
+                                   rtol=1e-13)
+
+
+def pin_attn_causal_prefix(o):
+    """Causal row q equals unmasked attention over keys 0..q only."""
+    Q, K, V = _qkv(506, S=10)
+    r = o.attention_forward(Q, K, V, causal=True)
+    for q in (0, 3, 9):
+        p = o.attention_forward(Q[..., q:q + 1, :], K[..., :q + 1, :], V[..., :q + 1, :])
+        np.testing.assert_allclose(r.O[..., q, :], p.O[..., 0, :], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(r.lse[..., q], p.lse[..., 0], rtol=1e-13)
+
+
+def pin_attn_dominant_key(o):
+    """A key whose score exceeds all others by ~1e3 takes all the weight (and
+    the scores are far beyond exp's range without the max shift)."""
+    Q, K, V = _qkv(507, B=1, H=1, S=6, D=4)
+    Q[..., :, :] = 0.0
+    Q[..., :, 0] = 1.0
+    K[..., :, 0] = 0.0
+    K[..., 2, 0] = 2000.0     # score 1000 after scale 1/2
+    r = o.attention_forward(Q, K, V)
+    np.testing.assert_allclose(r.O, np.broadcast_to(V[..., 2:3, :], V.shape), rtol=1e-12,
+                               atol=1e-300)
+    assert np.all(np.isfinite(r.lse)) and np.allclose(r.lse, 1000.0, rtol=1e-12)
+
+
+def pin_attn_torch_sdpa(o):
+    """torch's scaled_dot_product_attention in float64 (a library routine),
+    with and without the causal mask, default scale 1 / sqrt(D)."""
+    import torch
+    import torch.nn.functional as F
+    Q, K, V = _qkv(508, S=17, D=16)
+    for causal in (False, True):
+        ref = F.scaled_dot_product_attention(torch.tensor(Q), torch.tensor(K), torch.tensor(V),
+                                             is_causal=causal).numpy()
+        np.testing.assert_allclose(o.attention_forward(Q, K, V, causal=causal).O, ref,
+                                   rtol=1e-11, atol=1e-12)
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
@@ -458,6 +563,9 @@ PINS = [
     pin_shard_merge_identity, pin_shard_partials_definition, pin_shard_backward_sum,
     pin_embed_adjoint, pin_embed_dense, pin_embed_bad_id,
     pin_sgd_matches_torch, pin_adamw_matches_torch,
+    pin_attn_uniform, pin_attn_single_key, pin_attn_key_shift, pin_attn_permutation,
+    pin_attn_rows_sum_to_one, pin_attn_causal_prefix, pin_attn_dominant_key,
+    pin_attn_torch_sdpa,
 ]
 
 

@@ -162,7 +162,61 @@ def _sgd_ascends(p, g, kind, lr, weight_decay=0.0, *a, **k):
     return np.asarray(p) + lr * (np.asarray(g) + weight_decay * np.asarray(p)), None, None
 
 
+# attention
+def _attn_scale_dropped(Q, K, scale):
+    return np.asarray(Q, dtype=np.float64) @ np.swapaxes(np.asarray(K, dtype=np.float64), -1, -2)
+
+
+def _attn_mask_transposed(S):
+    return np.arange(S)[None, :] >= np.arange(S)[:, None]
+
+
+def _attn_mask_strict(S):
+    return np.arange(S)[None, :] < np.arange(S)[:, None]
+
+
+_orig_attn = O.attention_forward
+
+
+def _attn_softmax_over_queries(Q, K, V, causal=False, scale=None):
+    Q = np.asarray(Q, dtype=np.float64)
+    S, D = Q.shape[-2], Q.shape[-1]
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    Z = O.attention_scores(Q, K, scale)
+    if causal:
+        Z = np.where(O.causal_allowed(S), Z, -np.inf)
+    Zt = np.swapaxes(Z, -1, -2)
+    lse = O.logsumexp_rows(Zt.reshape(-1, S)).reshape(Zt.shape[:-1])
+    P = np.swapaxes(np.exp(Zt - lse[..., None]), -1, -2)
+    return O.AttentionResult(O=P @ np.asarray(V, dtype=np.float64), lse=lse)
+
+
+def _attn_lse_base2(Q, K, V, causal=False, scale=None):
+    r = _orig_attn(Q, K, V, causal, scale)
+    return O.AttentionResult(O=r.O, lse=r.lse / np.log(2.0))
+
+
+def _attn_unshifted(Q, K, V, causal=False, scale=None):
+    Q = np.asarray(Q, dtype=np.float64)
+    S, D = Q.shape[-2], Q.shape[-1]
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    Z = O.attention_scores(Q, K, scale)
+    if causal:
+        Z = np.where(O.causal_allowed(S), Z, -np.inf)
+    with np.errstate(over="ignore", invalid="ignore"):
+        E = np.exp(Z)
+        lse = np.log(E.sum(-1))
+        return O.AttentionResult(O=(E / E.sum(-1, keepdims=True)) @ np.asarray(V, dtype=np.float64),
+                                 lse=lse)
+
+
 MUTATIONS = {
+    "attn_scale_dropped": ("attention_scores", _attn_scale_dropped),
+    "attn_mask_transposed": ("causal_allowed", _attn_mask_transposed),
+    "attn_mask_excludes_diagonal": ("causal_allowed", _attn_mask_strict),
+    "attn_softmax_over_queries": ("attention_forward", _attn_softmax_over_queries),
+    "attn_lse_base2": ("attention_forward", _attn_lse_base2),
+    "attn_without_max_shift": ("attention_forward", _attn_unshifted),
     "adamw_without_bias_correction": ("optimizer_step", _adamw_without_bias_correction),
     "adamw_coupled_weight_decay": ("optimizer_step", _adamw_coupled_decay),
     "sgd_ascends": ("optimizer_step", _sgd_ascends),

@@ -189,3 +189,32 @@ def checksum(*arrays: np.ndarray) -> str:
         for s in range(0, len(mv), step):
             h.update(mv[s:s + step])
     return h.hexdigest()
+
+
+# --------------------------------------------------------------- attention
+#
+# Online-softmax attention inputs shaped like a Llama-3-8B attention layer
+# at the MaximusLLM page's training batch (section 1 and its KV-cache
+# figures: batch 8 x seq 2048, 32 heads, head_dim 128).  Q, K, V ~ N(0, 1)
+# rounded to bf16, layout [B, H, S, D]; rng = default_rng(seed), draw order
+# Q, K, V.  The decoder's causal mask is the default.
+
+
+@dataclasses.dataclass(frozen=True)
+class AttentionWorkload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal: bool
+    seed: int
+
+
+ATTENTION = AttentionWorkload("llama3_8b_attention_b8x2048", 8, 32, 2048, 128, True, 2001)
+
+
+def attention_inputs(B: int, H: int, S: int, D: int, seed: int, std: float = 1.0):
+    """(Q, K, V) as float32 arrays holding bf16-representable values."""
+    rng = np.random.default_rng(seed)
+    return tuple(_normals(rng, (B, H, S, D), std, "bf16") for _ in range(3))
