@@ -250,6 +250,33 @@ const char* lce_status_string(lce_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* lce_last_error(void);
 
+/* ------------------------------------------------ online-softmax attention
+ *
+ * O = softmax(scale * Q K^T) V over the keys of each query, with an optional
+ * causal mask (query i attends to keys 0..i), and the natural-log
+ * logsumexp of each row of masked, scaled scores.  The [B, H, S, S] score
+ * matrix is never stored: score tiles stream through registers and LDS with
+ * the running max / normaliser recurrence ("OjasX 0.6.1", section 核心技术 /
+ * "Core Technology", zero-byte attention score matrix, and its Online Softmax
+ * paragraph).  The operation is the one the KV-cache page writes (section
+ * KV Cache基础): softmax(Q K^T / sqrt(d_k)) V.
+ *
+ * Q, K, V: device pointers, bf16, layout [B, H, S, D] (D contiguous), read
+ *          only.  D must be 64 or 128 (else LCE_ERR_UNSUPPORTED).
+ * causal:  0 or 1.
+ * scale:   > 0, or 0 for 1 / sqrt(D); negative or non-finite is
+ *          LCE_ERR_INVALID_ARG.
+ * O:       device, f32 [B, H, S, D], written.
+ * lse:     device, f32 [B, H, S], written (the backward pass recomputes the
+ *          probabilities from it).
+ * B, H, S >= 0; nothing is launched when any of them is 0.  Accumulation in
+ * f32; the probabilities enter the second product rounded to bf16 and the
+ * normaliser sums those rounded values.  Allocates nothing; launches on
+ * `stream` only. */
+lce_status lce_attention_forward(const void* Q, const void* K, const void* V, int64_t B, int64_t H,
+                                 int64_t S, int64_t D, int causal, float scale, float* O,
+                                 float* lse, void* stream);
+
 /* ---------------------------------------------------------- measurement */
 
 /* C[M, N] = A[M, K] B[N, K]^T with the same MFMA tile engine as the path
@@ -271,7 +298,8 @@ typedef enum {
   LCE_K_DW = 8,        /* dW += G^T H                                    */
   LCE_K_GEMM = 9,      /* lce_gemm_nt                                    */
   LCE_K_EMBED = 10,    /* embedding gather / gradient scatter-sum        */
-  LCE_K_COUNT = 11
+  LCE_K_ATTN = 11,     /* online-softmax attention forward               */
+  LCE_K_COUNT = 12
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -177,3 +177,26 @@ def test_backward_step_argument_checks_before_launch():
     assert call(lr=-1.0) == _lib.LCE_ERR_INVALID_ARG
     assert call(m=None) == _lib.LCE_ERR_INVALID_ARG
     assert call(kind=_lib.LCE_OPT_SGD, m=None, v=None, N=8193) == _lib.LCE_ERR_UNSUPPORTED
+
+
+def test_attention_argument_checks_before_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(B=1, H=2, S=100, D=128, causal=1, scale=0.0, q=fake, o=fake):
+        return lib.lce_attention_forward(q, fake, fake, B, H, S, D, causal, scale, o, fake, None)
+
+    assert call(D=96) == _lib.LCE_ERR_UNSUPPORTED
+    assert call(D=256) == _lib.LCE_ERR_UNSUPPORTED
+    assert call(S=-1) == _lib.LCE_ERR_INVALID_ARG
+    assert call(B=-2) == _lib.LCE_ERR_INVALID_ARG
+    assert call(causal=2) == _lib.LCE_ERR_INVALID_ARG
+    assert call(scale=-0.5) == _lib.LCE_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == _lib.LCE_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == _lib.LCE_ERR_INVALID_ARG
+    assert call(q=None) == _lib.LCE_ERR_INVALID_ARG
+    assert call(o=None) == _lib.LCE_ERR_INVALID_ARG
+    assert call(S=1 << 31) == _lib.LCE_ERR_UNSUPPORTED
+    # empty problems launch nothing, so NULL pointers are fine
+    assert lib.lce_attention_forward(None, None, None, 1, 2, 0, 128, 1, 0.0, None, None, None) == 0
+    assert lib.lce_attention_forward(None, None, None, 0, 2, 64, 64, 0, 0.0, None, None, None) == 0

@@ -30,7 +30,7 @@ LCE_MEAN = 0
 LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
-                  "bwd_g", "dh", "dw", "gemm", "embed")
+                  "bwd_g", "dh", "dw", "gemm", "embed", "attn")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""
@@ -60,6 +60,8 @@ SIGNATURES = {
     "lce_embed_forward": (_INT, [_P, _P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
     "lce_embed_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "lce_embed_backward": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "lce_attention_forward": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, ctypes.c_float,
+                                     _P, _P, _P]),
     "lce_check_error": (_INT, [_P, _P]),
     "lce_status_string": (ctypes.c_char_p, [_INT]),
     "lce_last_error": (ctypes.c_char_p, []),
@@ -180,6 +182,11 @@ def lce_embed_backward(dX, input_ids, valid_idx, valid_count, N, d, V, dW, accum
     _check(load().lce_embed_backward(dX, input_ids, valid_idx, valid_count, N, d, V, dW,
                                      accumulate_dW, workspace, workspace_bytes, stream),
            "lce_embed_backward")
+
+
+def lce_attention_forward(Q, K, V, B, H, S, D, causal, scale, O, lse, stream) -> None:
+    _check(load().lce_attention_forward(Q, K, V, B, H, S, D, causal, scale, O, lse, stream),
+           "lce_attention_forward")
 
 
 def lce_check_error(err_flag, stream) -> None:

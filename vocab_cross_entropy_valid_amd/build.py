@@ -19,7 +19,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblce.so")
 ARCH = os.environ.get("LCE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kernels_fwd.hip", "kernels_bwd.hip", "kernels_embed.hip", "api.hip"]
+SOURCES = ["kernels_fwd.hip", "kernels_bwd.hip", "kernels_embed.hip", "kernels_attn.hip",
+           "api.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

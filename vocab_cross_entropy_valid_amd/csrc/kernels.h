@@ -129,4 +129,20 @@ hipError_t launch_embed_backward(const EmbedPlan& p, const float* dX, const int6
 hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                           int dtype, hipStream_t s);
 
+
+// Online-softmax attention forward over [B*H, S, D] bf16 Q, K, V.
+struct AttnArgs {
+  const uint16_t* Q;  // bf16 bits
+  const uint16_t* K;
+  const uint16_t* V;
+  float* O;          // [B*H, S, D]
+  float* lse;        // [B*H, S], natural log
+  int64_t BH;
+  int S;
+  int causal;
+  float scale_log2;  // scale * log2(e)
+};
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s);
+
 }  // namespace lce

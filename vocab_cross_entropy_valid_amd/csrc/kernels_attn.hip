@@ -1,0 +1,294 @@
+// Attention forward through an online softmax: O = softmax(scale Q K^T) V
+// with an optional causal mask, and the per-row logsumexp, without storing
+// the [B, H, S, S] score matrix ("OjasX 0.6.1", section 核心技术 / "Core
+// Technology": zero-byte attention score matrix; the same page's Online
+// Softmax paragraph gives the running max / normaliser recurrence used
+// here; softmax(Q K^T / sqrt(d_k)) V as the KV-cache page, section
+// KV Cache基础, writes the operation).
+//
+// Work decomposition: a workgroup of 4 waves takes 128 queries of one
+// (batch, head), 32 per wave, and streams the keys in blocks of 64.
+//
+//  * Scores are computed transposed, S^T = K Q^T (A = K rows, B = Q rows),
+//    on v_mfma_f32_32x32x16_bf16: lane l owns query l % 32 and, for key
+//    block half mt, keys 32 mt + 8 (i / 4) + 4 (l / 32) + i % 4 (i = 0..15).
+//    The running max and sum of a query then stay in its lane, plus one
+//    exchange with lane l ^ 32.
+//  * The output is accumulated transposed too, O^T += V^T P^T, so that lane l
+//    again owns query l % 32 and the rescale by exp(m_old - m_new) needs no
+//    data from other lanes.  The probabilities go straight from the score
+//    registers into the B operand: the 8 values lane (q, h) feeds to one
+//    MFMA are keys 4h + {0..3, 8..11} of a 16-key slice, and V^T is laid out
+//    in LDS in units of 4 consecutive keys so that the A operand holds the
+//    same keys in the same order (a product over K does not care in which
+//    order K is enumerated, as long as A and B agree).
+//  * Q stays in registers for the whole key loop (B operand of S^T).  K and
+//    V of the next key block are loaded into registers while the current
+//    block computes, then written to LDS: K row-major with 16-byte chunks
+//    XOR-swizzled by the row, V transposed into [dim][key] rows of 128 bytes
+//    with 8-byte units XOR-swizzled by (dim / 2) % 16, so that the fragment
+//    reads of 32 consecutive rows hit distinct banks.
+//  * Scores past the sequence end, and for a causal mask past the query, are
+//    -inf before the max; a key block that lies wholly after a wave's
+//    queries is skipped by that wave.  exp2 with the scale folded into
+//    log2(e) scale.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lce {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kQBlock = 128;  // queries per workgroup
+constexpr int kKBlock = 64;   // keys per block
+
+template <int D>
+struct AttnLds {
+  static constexpr int kChunks = D / 8;             // 16-byte chunks per K row
+  static constexpr int kKBytes = kKBlock * D * 2;   // K block
+  static constexpr int kVBytes = D * kKBlock * 2;   // V^T block: D rows of 128 B
+  static constexpr int kBytes = kKBytes + kVBytes;
+};
+
+__device__ __forceinline__ int k_offset(int row, int chunk, int chunks) {
+  return row * chunks * 16 + ((chunk ^ (row & (chunks - 1))) << 4);
+}
+
+// byte offset of 8-byte unit u (keys 4u .. 4u + 3) of V^T row dv
+__device__ __forceinline__ int vt_offset(int dv, int u) {
+  return dv * (kKBlock * 2) + ((u ^ ((dv >> 1) & 15)) << 3);
+}
+
+template <int D>
+struct BlockRegs {
+  static constexpr int kKLoads = kKBlock * D / 8 / kAttnThreads;              // 16-B K loads
+  static constexpr int kVUnits = (D / 8) * (kKBlock / 4);                     // (dv group, key group)
+  static constexpr int kVIters = (kVUnits + kAttnThreads - 1) / kAttnThreads;
+  u32x4 k[kKLoads];
+  u32x4 v[kVIters][4];
+};
+
+// Global -> registers for key block kb (rows past S read as zeros).
+template <int D>
+__device__ __forceinline__ void load_block(BlockRegs<D>& r, const bf16_t* Kh, const bf16_t* Vh, int S,
+                                           int kb, int tid) {
+  constexpr int C = AttnLds<D>::kChunks;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < BlockRegs<D>::kKLoads; ++j) {
+    const int idx = j * kAttnThreads + tid;
+    const int row = idx / C;
+    const int c = idx % C;
+    const int key = kb * kKBlock + row;
+    r.k[j] = key < S ? *(const u32x4*)(Kh + (int64_t)key * D + 8 * c) : z;
+  }
+#pragma unroll
+  for (int it = 0; it < BlockRegs<D>::kVIters; ++it) {
+    const int unit = it * kAttnThreads + tid;
+    const int kg = unit & 15;  // keys 4 kg .. 4 kg + 3
+    const int dg = unit >> 4;  // dims 8 dg .. 8 dg + 7
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int key = kb * kKBlock + 4 * kg + q;
+      r.v[it][q] = (unit < BlockRegs<D>::kVUnits && key < S)
+                       ? *(const u32x4*)(Vh + (int64_t)key * D + 8 * dg)
+                       : z;
+    }
+  }
+}
+
+// Registers -> LDS: K as is (swizzled), V transposed into 4-key units.
+template <int D>
+__device__ __forceinline__ void store_block(const BlockRegs<D>& r, char* lds, int tid) {
+  constexpr int C = AttnLds<D>::kChunks;
+#pragma unroll
+  for (int j = 0; j < BlockRegs<D>::kKLoads; ++j) {
+    const int idx = j * kAttnThreads + tid;
+    *(u32x4*)(lds + k_offset(idx / C, idx % C, C)) = r.k[j];
+  }
+  char* vt = lds + AttnLds<D>::kKBytes;
+#pragma unroll
+  for (int it = 0; it < BlockRegs<D>::kVIters; ++it) {
+    const int unit = it * kAttnThreads + tid;
+    if (unit >= BlockRegs<D>::kVUnits) continue;
+    const int kg = unit & 15;
+    const int dg = unit >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e (dim 8 dg + e) of the 4 key rows
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (r.v[it][0][w] >> sh) & 0xFFFFu, x1 = (r.v[it][1][w] >> sh) & 0xFFFFu;
+      const uint32_t x2 = (r.v[it][2][w] >> sh) & 0xFFFFu, x3 = (r.v[it][3][w] >> sh) & 0xFFFFu;
+      u32x2 u;
+      u[0] = x0 | (x1 << 16);
+      u[1] = x2 | (x3 << 16);
+      *(u32x2*)(vt + vt_offset(8 * dg + e, kg)) = u;
+    }
+  }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[AttnLds<D>::kBytes];
+  constexpr int C = AttnLds<D>::kChunks;
+  constexpr int KS = D / 16;  // MFMA k-steps of the score product
+  constexpr int MD = D / 32;  // 32-row blocks of O^T
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int S = a.S;
+  const int nqb = (S + kQBlock - 1) / kQBlock;
+  // heaviest (last) query blocks of every head first
+  const int qb = nqb - 1 - (int)(blockIdx.x / a.BH);
+  const int64_t bh = blockIdx.x % a.BH;
+  const int64_t head = bh * (int64_t)S * D;
+  const bf16_t* Qh = a.Q + head;
+  const bf16_t* Kh = a.K + head;
+  const bf16_t* Vh = a.V + head;
+
+  const int q0 = qb * kQBlock + 32 * wave;  // first query of this wave
+  const int q = q0 + j;                     // this lane's query
+  const int qc = q < S ? q : S - 1;
+  u32x4 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *(const u32x4*)(Qh + (int64_t)qc * D + 16 * s + 8 * h);
+
+  const int kend = a.causal ? min(S, (qb + 1) * kQBlock) : S;
+  const int nkb = (kend + kKBlock - 1) / kKBlock;
+
+  f32x16 o[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[m][i] = 0.f;
+  float mrun = -INFINITY;  // running max, log2 units
+  float lrun = 0.f;        // this lane's part of the running sum
+  const float c = a.scale_log2;
+
+  BlockRegs<D> r;
+  load_block<D>(r, Kh, Vh, S, 0, tid);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // the previous block's fragment reads are done
+    store_block<D>(r, lds, tid);
+    __syncthreads();
+    if (kb + 1 < nkb) load_block<D>(r, Kh, Vh, S, kb + 1, tid);
+    const int k0 = kb * kKBlock;
+    if (a.causal && k0 > q0 + 31) continue;  // block wholly after this wave's queries
+
+    // S^T = K Q^T for the 64 keys of the block
+    f32x16 sc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[mt][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const u32x4 af = *(const u32x4*)(lds + k_offset(32 * mt + j, 2 * s + h, C));
+        Mma<bf16_t>::run(sc[mt], af, qf[s]);
+      }
+    }
+
+    // mask: keys past the end, and past the query under a causal mask
+    const bool tail = k0 + kKBlock > S;
+    const bool diag = a.causal && k0 + kKBlock - 1 > q0;
+    if (tail || diag) {
+      const int lim = a.causal ? min(q, S - 1) : S - 1;  // last allowed key
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > lim) sc[mt][i] = -INFINITY;
+        }
+    }
+
+    // online softmax update (log2 domain, scale folded in)
+    float bmax = sc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sc[mt][i]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float mnew = fmaxf(mrun, bmax * c);
+    // mnew = -inf only if every key so far is masked for this query (never
+    // for a valid query: key 0 is always allowed); keep p = 0 then
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(mrun - mref);
+    mrun = mnew;
+    float psum = 0.f;
+    u32x4 pf[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w], c, -mref));
+          const float p1 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w + 1], c, -mref));
+          const uint32_t b0 = bf16_bits(p0), b1 = bf16_bits(p1);
+          // the normaliser sums the rounded values the MFMA multiplies
+          psum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
+          pf[mt][g][w] = b0 | (b1 << 16);
+        }
+    lrun = lrun * alpha + psum;
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[m][i] *= alpha;
+
+    // O^T += V^T P^T
+    const char* vt = lds + AttnLds<D>::kKBytes;
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      const int dv = 32 * m + j;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int u0 = 8 * mt + 4 * g + h;  // keys 4 u0 .. 4 u0 + 3, then 4 (u0 + 2) ..
+          const u32x2 lo = *(const u32x2*)(vt + vt_offset(dv, u0));
+          const u32x2 hi = *(const u32x2*)(vt + vt_offset(dv, u0 + 2));
+          u32x4 af;
+          af[0] = lo[0];
+          af[1] = lo[1];
+          af[2] = hi[0];
+          af[3] = hi[1];
+          Mma<bf16_t>::run(o[m], af, pf[mt][g]);
+        }
+    }
+  }
+
+  const float ltot = lrun + __shfl_xor(lrun, 32);
+  if (q >= S) return;
+  const float inv = 1.f / ltot;
+  float* Oq = a.O + head + (int64_t)q * D;
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v = {o[m][4 * r4] * inv, o[m][4 * r4 + 1] * inv, o[m][4 * r4 + 2] * inv,
+                 o[m][4 * r4 + 3] * inv};
+      *(f32x4*)(Oq + 32 * m + 8 * r4 + 4 * h) = v;
+    }
+  if (h == 0) a.lse[bh * S + q] = (mrun + fast_log2(ltot)) * kLn2;
+}
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
+  if (a.S <= 0 || a.BH <= 0) return hipSuccess;
+  const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
+  const dim3 grid((unsigned)(nqb * a.BH));
+  if (D == 128)
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lce

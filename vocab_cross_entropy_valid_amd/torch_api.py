@@ -363,3 +363,29 @@ def linear_cross_entropy(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
     if return_aux:
         return loss, (per_tok, lse, cnt)
     return loss
+
+
+@dataclasses.dataclass
+class AttentionOut:
+    O: torch.Tensor    # f32 [B, H, S, D]
+    lse: torch.Tensor  # f32 [B, H, S], natural log
+
+
+def attention_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = True,
+                      scale: Optional[float] = None, out: Optional[AttentionOut] = None
+                      ) -> AttentionOut:
+    """lce_attention_forward: online-softmax attention over bf16 [B, H, S, D] tensors."""
+    for t in (Q, K, V):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("Q, K and V must be contiguous bf16 [B, H, S, D] GPU tensors")
+    if Q.shape != K.shape or Q.shape != V.shape:
+        raise ValueError("Q, K and V must have the same shape")
+    B, H, S, D = Q.shape
+    dev = Q.device
+    if out is None:
+        out = AttentionOut(O=torch.empty(B, H, S, D, dtype=torch.float32, device=dev),
+                           lse=torch.empty(B, H, S, dtype=torch.float32, device=dev))
+    _lib.lce_attention_forward(_ptr(Q), _ptr(K), _ptr(V), B, H, S, D, 1 if causal else 0,
+                               0.0 if scale is None else float(scale), _ptr(out.O), _ptr(out.lse),
+                               _stream(dev))
+    return out
