@@ -130,6 +130,96 @@ def cpu_baseline(H, W, y, target_s: float):
                       f"backward, {t:.1f} s; host cores available: {cores}"}
 
 
+ATTN_METRIC = "online-softmax attention forward TFLOP/s and % bf16 MFMA peak, causal, B=8 H=32 S=2048 D=128"
+
+
+def attention_pairs(S: int, causal: bool) -> int:
+    """(query, key) pairs the mask leaves: each costs 4 D FLOPs (QK^T and PV)."""
+    return S * (S + 1) // 2 if causal else S * S
+
+
+def cpu_baseline_attention(wl, Q, K, V, target_s: float):
+    """The fp64 attention oracle on whole heads of the same workload, timed."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    flops_head = 4.0 * wl.D * attention_pairs(wl.S, wl.causal)
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < wl.B * wl.H:
+        b, h = divmod(heads, wl.H)
+        oracle.attention_forward(Q[b, h], K[b, h], V[b, h], causal=wl.causal)
+        heads += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    t = time.perf_counter() - t0
+    return {"value": heads * flops_head / t / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} of the {wl.B * wl.H} heads (S {wl.S}, D {wl.D}, causal), fp64 "
+                      f"full-score softmax, {t:.1f} s; host cores available: {cores}"}
+
+
+def bench_attention(args) -> None:
+    """Times lce_attention_forward on the Llama-3-8B-shaped attention batch."""
+    import torch
+
+    import workloads
+    from vocab_cross_entropy_valid_amd import _lib, torch_api
+
+    wl = workloads.ATTENTION
+    _log(f"[bench] generating {wl.name}: B={wl.B} H={wl.H} S={wl.S} D={wl.D} causal={wl.causal}")
+    Q, K, V = workloads.attention_inputs(wl.B, wl.H, wl.S, wl.D, wl.seed)
+    dev = torch.device("cuda:0")
+    t = [torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (Q, K, V)]
+    out = torch_api.AttentionOut(
+        O=torch.empty(wl.B, wl.H, wl.S, wl.D, dtype=torch.float32, device=dev),
+        lse=torch.empty(wl.B, wl.H, wl.S, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        torch_api.attention_forward(*t, causal=wl.causal, out=out)
+    torch.cuda.synchronize()
+    _lib.lce_timing_reset()
+    _lib.lce_timing_enable(True)
+    _log(f"[bench] timing {args.steps} attention launches")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        torch_api.attention_forward(*t, causal=wl.causal, out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.lce_timing_enable(False)
+    ms, n = _lib.lce_timing_query(_lib.KERNEL_CLASSES.index("attn"))
+    _lib.lce_timing_reset()
+    assert bool(torch.isfinite(out.O).all())
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, dev)
+    flops = 4.0 * wl.D * attention_pairs(wl.S, wl.causal) * wl.B * wl.H
+    ms_step = 1e3 * elapsed / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    avg_us = 1e3 * ms / n
+    ach = flops / (avg_us * 1e-6) / 1e12
+    res = {
+        "metric": ATTN_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0, 1) Q, K, V rounded to bf16 (no dataset)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "D": wl.D,
+                   "causal": wl.causal},
+        "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "positions_per_s": round(wl.B * wl.S / (ms_step * 1e-3), 1),
+        "score_matrix_bytes_avoided": 4 * wl.B * wl.H * wl.S * wl.S,
+        "roofline": {"kernel": "attn", "bound": "mfma", "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counter_traffic("attn", wl.name), "flops_per_launch": flops,
+                     "avg_launch_us": round(avg_us, 2)},
+    }
+    if args.cpu_seconds > 0:
+        _log("[bench] timing the CPU attention oracle on whole heads")
+        res["cpu_baseline"] = cpu_baseline_attention(wl, Q, K, V, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,12 +242,19 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--attention", action="store_true",
+                    help="measure online-softmax attention (batch 8 x 32 heads x 2048 x 128, "
+                         "causal) instead of the loss path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(rows shard across GPUs with no communication in forward; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.attention:
+        bench_attention(args)
+        return
 
     import numpy as np
     import torch

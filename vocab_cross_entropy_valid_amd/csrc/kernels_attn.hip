@@ -19,19 +19,28 @@
 //    data from other lanes.  The probabilities go straight from the score
 //    registers into the B operand: the 8 values lane (q, h) feeds to one
 //    MFMA are keys 4h + {0..3, 8..11} of a 16-key slice, and V^T is laid out
-//    in LDS in units of 4 consecutive keys so that the A operand holds the
-//    same keys in the same order (a product over K does not care in which
-//    order K is enumerated, as long as A and B agree).
+//    in LDS so that the A operand reads exactly those keys in that order as
+//    one 16-byte chunk (a product over K does not care in which order K is
+//    enumerated, as long as A and B agree).
 //  * Q stays in registers for the whole key loop (B operand of S^T).  K and
 //    V of the next key block are loaded into registers while the current
 //    block computes, then written to LDS: K row-major with 16-byte chunks
 //    XOR-swizzled by the row, V transposed into [dim][key] rows of 128 bytes
-//    with 8-byte units XOR-swizzled by (dim / 2) % 16, so that the fragment
-//    reads of 32 consecutive rows hit distinct banks.
+//    with 16-byte chunks XOR-swizzled by (dim / 2) % 8, so that the fragment
+//    reads of consecutive rows hit distinct banks.
 //  * Scores past the sequence end, and for a causal mask past the query, are
 //    -inf before the max; a key block that lies wholly after a wave's
 //    queries is skipped by that wave.  exp2 with the scale folded into
 //    log2(e) scale.
+//  * The softmax is what bounds this kernel (VALU work per score next to
+//    1/64 of an MFMA), so it is kept lean: probabilities are packed to bf16
+//    by the hardware conversion, and the reference max of a query moves only
+//    when a block exceeds it by more than 2^8 (the probabilities then stay
+//    <= 256, harmless in bf16 and fp32), so the 64 output accumulators are
+//    rescaled only in the rare blocks where some lane of the wave moved.
+//    The result does not depend on the reference (it cancels in O / sum and
+//    is added back to the logsumexp).
+//  * K / V tiles are double buffered in LDS: one barrier per key block.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,16 +57,39 @@ struct AttnLds {
   static constexpr int kChunks = D / 8;             // 16-byte chunks per K row
   static constexpr int kKBytes = kKBlock * D * 2;   // K block
   static constexpr int kVBytes = D * kKBlock * 2;   // V^T block: D rows of 128 B
-  static constexpr int kBytes = kKBytes + kVBytes;
+  static constexpr int kBuf = kKBytes + kVBytes;     // one key block
+  static constexpr int kBytes = 2 * kBuf;            // double buffered
 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 values -> packed bf16 (round to nearest even): one vector
+// conversion, so that the backend emits a single v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+
+constexpr float kRescaleSlack = 8.f;  // log2 units
 
 __device__ __forceinline__ int k_offset(int row, int chunk, int chunks) {
   return row * chunks * 16 + ((chunk ^ (row & (chunks - 1))) << 4);
 }
 
-// byte offset of 8-byte unit u (keys 4u .. 4u + 3) of V^T row dv
-__device__ __forceinline__ int vt_offset(int dv, int u) {
-  return dv * (kKBlock * 2) + ((u ^ ((dv >> 1) & 15)) << 3);
+// V^T row dv holds the block's 64 keys as 16 units of 4 keys.  One MFMA
+// A fragment needs units u0 and u0 + 2 (u0 = 8 mt + 4 g + h: keys 4 u0 + {0..3}
+// and 4 u0 + {8..11}), so each such pair is one 16-byte chunk, numbered
+// c = (u0 >> 1) | (u0 & 1), and the chunks are XOR-swizzled by (dv / 2) % 8:
+// the fragment read is one ds_read_b128 and each 16 lanes of it (rows of one
+// parity, 8 distinct chunks) hit distinct banks.
+__device__ __forceinline__ int vt_chunk_offset(int dv, int c) {
+  return dv * (kKBlock * 2) + ((c ^ ((dv >> 1) & 7)) << 4);
+}
+
+// byte offset of unit u of row dv
+__device__ __forceinline__ int vt_unit_offset(int dv, int u) {
+  const int u0 = u & ~2;  // first unit of its pair
+  return vt_chunk_offset(dv, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
 }
 
 template <int D>
@@ -123,7 +155,7 @@ __device__ __forceinline__ void store_block(const BlockRegs<D>& r, char* lds, in
       u32x2 u;
       u[0] = x0 | (x1 << 16);
       u[1] = x2 | (x3 << 16);
-      *(u32x2*)(vt + vt_offset(8 * dg + e, kg)) = u;
+      *(u32x2*)(vt + vt_unit_offset(8 * dg + e, kg)) = u;
     }
   }
 }
@@ -172,97 +204,106 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
 
   BlockRegs<D> r;
   load_block<D>(r, Kh, Vh, S, 0, tid);
+  store_block<D>(r, lds, tid);
+  __syncthreads();
+  if (nkb > 1) load_block<D>(r, Kh, Vh, S, 1, tid);
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // the previous block's fragment reads are done
-    store_block<D>(r, lds, tid);
-    __syncthreads();
-    if (kb + 1 < nkb) load_block<D>(r, Kh, Vh, S, kb + 1, tid);
+    const char* buf = lds + (kb & 1) * AttnLds<D>::kBuf;
     const int k0 = kb * kKBlock;
-    if (a.causal && k0 > q0 + 31) continue;  // block wholly after this wave's queries
+    // a block wholly after this wave's queries contributes nothing
+    if (!(a.causal && k0 > q0 + 31)) {
+      // S^T = K Q^T for the 64 keys of the block
+      f32x16 sc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[mt][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const u32x4 af = *(const u32x4*)(buf + k_offset(32 * mt + j, 2 * s + h, C));
+          Mma<bf16_t>::run(sc[mt], af, qf[s]);
+        }
+      }
 
-    // S^T = K Q^T for the 64 keys of the block
-    f32x16 sc[2];
+      // mask: keys past the end, and past the query under a causal mask
+      const bool tail = k0 + kKBlock > S;
+      const bool diag = a.causal && k0 + kKBlock - 1 > q0;
+      if (tail || diag) {
+        const int lim = a.causal ? min(q, S - 1) : S - 1;  // last allowed key
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[mt][i] = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key > lim) sc[mt][i] = -INFINITY;
+          }
+      }
+
+      // online softmax update (log2 domain, scale folded in); the reference
+      // max moves only when the block exceeds it by more than the slack
+      float bmax = sc[0][0];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const u32x4 af = *(const u32x4*)(lds + k_offset(32 * mt + j, 2 * s + h, C));
-        Mma<bf16_t>::run(sc[mt], af, qf[s]);
+        for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sc[mt][i]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * c;
+      const bool up = bmax > mrun + kRescaleSlack;  // also the first finite block
+      float alpha = 1.f;
+      if (up) {
+        alpha = fast_exp2(mrun - bmax);  // 0 while mrun = -inf
+        mrun = bmax;
+      }
+      // mrun = -inf only while every key so far is masked for this query
+      // (never for a valid query: key 0 is always allowed); keep p = 0 then
+      const float mref = mrun == -INFINITY ? 0.f : mrun;
+      float psum = 0.f;
+      const bf16x2_t kOnes = {(__bf16)1.f, (__bf16)1.f};
+      u32x4 pf[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w], c, -mref));
+            const float p1 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w + 1], c, -mref));
+            const uint32_t pk = cvt_pk_bf16(p0, p1);
+            // the normaliser sums the rounded values the MFMA multiplies:
+            // one packed dot product with (1, 1)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), kOnes, psum,
+                                                   false);
+            pf[mt][g][w] = pk;
+          }
+      lrun = lrun * alpha + psum;
+      if (__ballot(up)) {
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[m][i] *= alpha;
+      }
+
+      // O^T += V^T P^T
+      const char* vt = buf + AttnLds<D>::kKBytes;
+#pragma unroll
+      for (int m = 0; m < MD; ++m) {
+        const int dv = 32 * m + j;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            // units u0 = 8 mt + 4 g + h and u0 + 2: chunk 4 mt + 2 g + h
+            const u32x4 af = *(const u32x4*)(vt + vt_chunk_offset(dv, 4 * mt + 2 * g + h));
+            Mma<bf16_t>::run(o[m], af, pf[mt][g]);
+          }
       }
     }
-
-    // mask: keys past the end, and past the query under a causal mask
-    const bool tail = k0 + kKBlock > S;
-    const bool diag = a.causal && k0 + kKBlock - 1 > q0;
-    if (tail || diag) {
-      const int lim = a.causal ? min(q, S - 1) : S - 1;  // last allowed key
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > lim) sc[mt][i] = -INFINITY;
-        }
-    }
-
-    // online softmax update (log2 domain, scale folded in)
-    float bmax = sc[0][0];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sc[mt][i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float mnew = fmaxf(mrun, bmax * c);
-    // mnew = -inf only if every key so far is masked for this query (never
-    // for a valid query: key 0 is always allowed); keep p = 0 then
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(mrun - mref);
-    mrun = mnew;
-    float psum = 0.f;
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w], c, -mref));
-          const float p1 = fast_exp2(fmaf(sc[mt][8 * g + 2 * w + 1], c, -mref));
-          const uint32_t b0 = bf16_bits(p0), b1 = bf16_bits(p1);
-          // the normaliser sums the rounded values the MFMA multiplies
-          psum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
-          pf[mt][g][w] = b0 | (b1 << 16);
-        }
-    lrun = lrun * alpha + psum;
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[m][i] *= alpha;
-
-    // O^T += V^T P^T
-    const char* vt = lds + AttnLds<D>::kKBytes;
-#pragma unroll
-    for (int m = 0; m < MD; ++m) {
-      const int dv = 32 * m + j;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int u0 = 8 * mt + 4 * g + h;  // keys 4 u0 .. 4 u0 + 3, then 4 (u0 + 2) ..
-          const u32x2 lo = *(const u32x2*)(vt + vt_offset(dv, u0));
-          const u32x2 hi = *(const u32x2*)(vt + vt_offset(dv, u0 + 2));
-          u32x4 af;
-          af[0] = lo[0];
-          af[1] = lo[1];
-          af[2] = hi[0];
-          af[3] = hi[1];
-          Mma<bf16_t>::run(o[m], af, pf[mt][g]);
-        }
-    }
+    // next block into the other buffer (last read in block kb - 1, which
+    // every wave finished before the previous barrier)
+    if (kb + 1 < nkb) store_block<D>(r, lds + ((kb + 1) & 1) * AttnLds<D>::kBuf, tid);
+    __syncthreads();
+    if (kb + 2 < nkb) load_block<D>(r, Kh, Vh, S, kb + 2, tid);
   }
 
   const float ltot = lrun + __shfl_xor(lrun, 32);
