@@ -148,13 +148,14 @@ __device__ __forceinline__ void store_block(const BlockRegs<D>& r, char* lds, in
     const int dg = unit >> 4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // element e (dim 8 dg + e) of the 4 key rows
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (r.v[it][0][w] >> sh) & 0xFFFFu, x1 = (r.v[it][1][w] >> sh) & 0xFFFFu;
-      const uint32_t x2 = (r.v[it][2][w] >> sh) & 0xFFFFu, x3 = (r.v[it][3][w] >> sh) & 0xFFFFu;
+      // element e (dim 8 dg + e) of the 4 key rows, two keys per word:
+      // v_perm_b32 picks the low (even e) or high (odd e) halves of word
+      // e / 2 of two rows (bytes 0-3 come from the second operand)
+      const int w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       u32x2 u;
-      u[0] = x0 | (x1 << 16);
-      u[1] = x2 | (x3 << 16);
+      u[0] = __builtin_amdgcn_perm(r.v[it][1][w], r.v[it][0][w], sel);
+      u[1] = __builtin_amdgcn_perm(r.v[it][3][w], r.v[it][2][w], sel);
       *(u32x2*)(vt + vt_unit_offset(8 * dg + e, kg)) = u;
     }
   }
@@ -170,7 +171,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int MD = D / 32;  // 32-row blocks of O^T
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform in a scalar register, so that conditions on the wave's
+  // queries (masking, skipping) become scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31;
   const int h = lane >> 5;
   const int S = a.S;
@@ -278,6 +281,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
           }
       lrun = lrun * alpha + psum;
       if (__ballot(up)) {
+        // keeps the compiler from hoisting the 64 multiplies out of the
+        // branch (alpha = 1 on lanes that did not move makes that legal)
+        asm volatile("");
 #pragma unroll
         for (int m = 0; m < MD; ++m)
 #pragma unroll
