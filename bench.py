@@ -33,28 +33,29 @@ PEAK_HBM_GBS = 8000.0
 CLASS_FLOPS = {"fwd": 2, "bwd_g": 2, "dh": 2, "dw": 2}
 
 
-KERNEL_SOURCES = ("vocab_cross_entropy_valid_amd/csrc", "vocab_cross_entropy_valid_amd/build.py")
+_CSRC = "vocab_cross_entropy_valid_amd/csrc/"
+# Sources that determine each kernel class's device code: its own file, the
+# shared device header, the argument structs and the build flags.
+_SHARED_SOURCES = (_CSRC + "device_common.h", _CSRC + "kernels.h",
+                   "vocab_cross_entropy_valid_amd/build.py")
+KERNEL_FILE = {"compact": "kernels_fwd.hip", "fwd": "kernels_fwd.hip", "merge": "kernels_fwd.hip",
+               "reduce": "kernels_fwd.hip", "zero": "kernels_bwd.hip",
+               "transpose": "kernels_bwd.hip", "bwd_g": "kernels_bwd.hip", "dh": "kernels_bwd.hip",
+               "dw": "kernels_bwd.hip", "gemm": "kernels_bwd.hip", "embed": "kernels_embed.hip",
+               "attn": "kernels_attn.hip"}
 
 
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the kernel sources and build flags (identifies the built kernels)."""
+def kernel_source_digest(kernel: str) -> str:
+    """sha256 over the sources that determine one kernel class's device code."""
     import hashlib
     h = hashlib.sha256()
-    files = []
-    for rel in KERNEL_SOURCES:
-        p = os.path.join(ROOT, rel)
-        if os.path.isdir(p):
-            files += sorted(os.path.join(p, f) for f in os.listdir(p)
-                            if f.endswith((".hip", ".h", ".cpp")))
-        else:
-            files.append(p)
-    for f in files:
-        h.update(os.path.relpath(f, ROOT).encode())
-        with open(f, "rb") as fh:
+    for rel in (_CSRC + KERNEL_FILE[kernel],) + _SHARED_SOURCES:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -77,7 +78,7 @@ def counter_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip().lstrip("- ").strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_digest():
+    if vals.get("source_sha256") != kernel_source_digest(kernel):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -227,7 +228,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables it)")
