@@ -430,3 +430,39 @@ def attention_forward(Q, K, V, causal: bool = False, scale: Optional[float] = No
     lse = logsumexp_rows(Z.reshape(-1, Z.shape[-1])).reshape(lead)
     P = np.exp(Z - lse[..., None])
     return AttentionResult(O=P @ V, lse=lse)
+
+
+@dataclasses.dataclass
+class AttentionGrads:
+    dQ: np.ndarray
+    dK: np.ndarray
+    dV: np.ndarray
+
+
+def attention_row_dot(dO, O) -> np.ndarray:
+    """D[q] = sum_d dO[q, d] O[q, d]: the softmax Jacobian's rank-one term,
+    equal to sum_k P[q, k] dP[q, k]."""
+    return (np.asarray(dO, dtype=np.float64) * np.asarray(O, dtype=np.float64)).sum(-1)
+
+
+def attention_backward(Q, K, V, dO, causal: bool = False, scale: Optional[float] = None):
+    """Exact gradient of O = softmax(scale Q K^T [masked]) V for an upstream dO:
+    dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
+    dK = scale dS^T Q, with P recomputed from the scores and the lse (the
+    probabilities are never kept from the forward pass)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    S, D = Q.shape[-2], Q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    fwd = attention_forward(Q, K, V, causal, scale)
+    Z = attention_scores(Q, K, scale)
+    if causal:
+        Z = np.where(causal_allowed(S), Z, -np.inf)
+    P = np.exp(Z - fwd.lse[..., None])
+    dV = np.swapaxes(P, -1, -2) @ dO
+    dP = dO @ np.swapaxes(V, -1, -2)
+    dS = P * (dP - attention_row_dot(dO, fwd.O)[..., None])
+    return AttentionGrads(dQ=scale * (dS @ K), dK=scale * (np.swapaxes(dS, -1, -2) @ Q), dV=dV)

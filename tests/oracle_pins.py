@@ -555,6 +555,65 @@ def pin_attn_torch_sdpa(o):
                                    rtol=1e-11, atol=1e-12)
 
 
+def pin_attn_backward_finite_differences(o):
+    """Central differences of L = sum(dO * O) for every entry of Q, K and V."""
+    Q, K, V = _qkv(511, B=1, H=1, S=4, D=3)
+    dO = np.random.default_rng(5111).standard_normal(Q.shape)
+    h = 1e-6
+    for causal in (False, True):
+        g = o.attention_backward(Q, K, V, dO, causal=causal)
+        for X, G in ((Q, g.dQ), (K, g.dK), (V, g.dV)):
+            for idx in np.ndindex(X.shape):
+                old = X[idx]
+                X[idx] = old + h
+                lp = (dO * o.attention_forward(Q, K, V, causal=causal).O).sum()
+                X[idx] = old - h
+                lm = (dO * o.attention_forward(Q, K, V, causal=causal).O).sum()
+                X[idx] = old
+                assert abs((lp - lm) / (2 * h) - G[idx]) <= 1e-7 * max(1.0, abs(G[idx])), idx
+
+
+def pin_attn_backward_torch(o):
+    """torch float64 autograd through scaled_dot_product_attention."""
+    import torch
+    import torch.nn.functional as F
+    Q, K, V = _qkv(512, S=9, D=8)
+    dO = np.random.default_rng(5121).standard_normal(Q.shape)
+    for causal in (False, True):
+        t = [torch.tensor(x, requires_grad=True) for x in (Q, K, V)]
+        F.scaled_dot_product_attention(*t, is_causal=causal).backward(torch.tensor(dO))
+        g = o.attention_backward(Q, K, V, dO, causal=causal)
+        for got, ref in ((g.dQ, t[0].grad), (g.dK, t[1].grad), (g.dV, t[2].grad)):
+            np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_attn_backward_closed_forms(o):
+    """Q = 0 and dO = 1: P is uniform over the allowed keys, so dV[k] = sum_q
+    P[q, k] = 1 without a mask and H_S - H_k (harmonic numbers) with the
+    causal mask.  Equal V rows: O does not depend on P, so dQ = dK = 0.  Rows
+    of dS sum to zero, so the keys' dK sum to zero."""
+    _, K, V = _qkv(513, S=7)
+    Q = np.zeros_like(K)
+    ones = np.ones_like(Q)
+    S = K.shape[-2]
+    g = o.attention_backward(Q, K, V, ones, causal=False)
+    np.testing.assert_allclose(g.dV, 1.0, rtol=1e-13)
+    g = o.attention_backward(Q, K, V, ones, causal=True)
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, S + 1))])
+    expect = (Hn[S] - Hn[:S])[:, None]
+    np.testing.assert_allclose(g.dV, np.broadcast_to(expect, g.dV.shape), rtol=1e-13)
+    Q, K, _ = _qkv(514, S=6)
+    Vc = np.broadcast_to(np.random.default_rng(5141).standard_normal(8), Q.shape).copy()
+    dO = np.random.default_rng(5142).standard_normal(Q.shape)
+    for causal in (False, True):
+        g = o.attention_backward(Q, K, Vc, dO, causal=causal)
+        np.testing.assert_allclose(g.dQ, 0.0, atol=1e-13)
+        np.testing.assert_allclose(g.dK, 0.0, atol=1e-13)
+        Q2, K2, V2 = _qkv(515, S=6)
+        g = o.attention_backward(Q2, K2, V2, dO, causal=causal)
+        np.testing.assert_allclose(g.dK.sum(axis=-2), 0.0, atol=1e-12)
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
@@ -565,7 +624,8 @@ PINS = [
     pin_sgd_matches_torch, pin_adamw_matches_torch,
     pin_attn_uniform, pin_attn_single_key, pin_attn_key_shift, pin_attn_permutation,
     pin_attn_rows_sum_to_one, pin_attn_causal_prefix, pin_attn_dominant_key,
-    pin_attn_torch_sdpa,
+    pin_attn_torch_sdpa, pin_attn_backward_finite_differences, pin_attn_backward_torch,
+    pin_attn_backward_closed_forms,
 ]
 
 

@@ -210,7 +210,36 @@ def _attn_unshifted(Q, K, V, causal=False, scale=None):
                                  lse=lse)
 
 
+_orig_attn_bwd = O.attention_backward
+
+
+def _attn_bwd_no_rowdot(dO, Oo):
+    return np.zeros(np.asarray(dO).shape[:-1])
+
+
+def _attn_bwd_dk_unscaled(Q, K, V, dO, causal=False, scale=None):
+    g = _orig_attn_bwd(Q, K, V, dO, causal, scale)
+    D = np.asarray(Q).shape[-1]
+    s = 1.0 / np.sqrt(D) if scale is None else scale
+    return O.AttentionGrads(dQ=g.dQ, dK=g.dK / s, dV=g.dV)
+
+
+def _attn_bwd_dv_untransposed(Q, K, V, dO, causal=False, scale=None):
+    g = _orig_attn_bwd(Q, K, V, dO, causal, scale)
+    Qd = np.asarray(Q, dtype=np.float64)
+    s = 1.0 / np.sqrt(Qd.shape[-1]) if scale is None else scale
+    Z = O.attention_scores(Qd, K, s)
+    if causal:
+        Z = np.where(O.causal_allowed(Qd.shape[-2]), Z, -np.inf)
+    f = O.attention_forward(Q, K, V, causal, scale)
+    P = np.exp(Z - f.lse[..., None])
+    return O.AttentionGrads(dQ=g.dQ, dK=g.dK, dV=P @ np.asarray(dO, dtype=np.float64))
+
+
 MUTATIONS = {
+    "attn_bwd_without_row_dot": ("attention_row_dot", _attn_bwd_no_rowdot),
+    "attn_bwd_dk_unscaled": ("attention_backward", _attn_bwd_dk_unscaled),
+    "attn_bwd_dv_untransposed": ("attention_backward", _attn_bwd_dv_untransposed),
     "attn_scale_dropped": ("attention_scores", _attn_scale_dropped),
     "attn_mask_transposed": ("causal_allowed", _attn_mask_transposed),
     "attn_mask_excludes_diagonal": ("causal_allowed", _attn_mask_strict),
