@@ -277,6 +277,27 @@ lce_status lce_attention_forward(const void* Q, const void* K, const void* V, in
                                  int64_t S, int64_t D, int causal, float scale, float* O,
                                  float* lse, void* stream);
 
+/* Gradient of lce_attention_forward for an upstream dO: dQ, dK, dV.  The
+ * probabilities are recomputed tile by tile from Q, K and the forward's lse
+ * (the [S, S] matrix is not stored in the backward pass either; same
+ * passages as lce_attention_forward):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  D = rowsum(dO * O),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Q, K, V: as for lce_attention_forward (bf16 [B, H, S, D], D = 64 or 128).
+ * O, lse:  the forward's outputs (f32), read only.
+ * dO:      device, bf16 [B, H, S, D], read only.
+ * dQ, dK, dV: device, f32 [B, H, S, D], written (not accumulated).
+ * delta:   device scratch, f32 [B, H, S], overwritten with D.
+ * causal, scale: as for the forward (and must match it).
+ * Two kernels on `stream`, no atomics: results are deterministic.  The
+ * probabilities and dS enter the products rounded to bf16.  Allocates
+ * nothing; errors as for the forward. */
+lce_status lce_attention_backward(const void* Q, const void* K, const void* V, const float* O,
+                                  const float* lse, const void* dO, int64_t B, int64_t H,
+                                  int64_t S, int64_t D, int causal, float scale, float* dQ,
+                                  float* dK, float* dV, float* delta, void* stream);
+
 /* ---------------------------------------------------------- measurement */
 
 /* C[M, N] = A[M, K] B[N, K]^T with the same MFMA tile engine as the path

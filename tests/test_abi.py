@@ -200,3 +200,20 @@ def test_attention_argument_checks_before_launch():
     # empty problems launch nothing, so NULL pointers are fine
     assert lib.lce_attention_forward(None, None, None, 1, 2, 0, 128, 1, 0.0, None, None, None) == 0
     assert lib.lce_attention_forward(None, None, None, 0, 2, 64, 64, 0, 0.0, None, None, None) == 0
+
+
+def test_attention_backward_argument_checks_before_launch():
+    lib = _lib.load()
+    f = ctypes.c_void_p(0x1000)
+
+    def call(B=1, H=2, S=100, D=128, causal=1, scale=0.0, dq=f, delta=f):
+        return lib.lce_attention_backward(f, f, f, f, f, f, B, H, S, D, causal, scale, dq, f, f,
+                                          delta, None)
+
+    assert call(D=80) == _lib.LCE_ERR_UNSUPPORTED
+    assert call(S=-3) == _lib.LCE_ERR_INVALID_ARG
+    assert call(causal=-1) == _lib.LCE_ERR_INVALID_ARG
+    assert call(scale=-1.0) == _lib.LCE_ERR_INVALID_ARG
+    assert call(dq=None) == _lib.LCE_ERR_INVALID_ARG
+    assert call(delta=None) == _lib.LCE_ERR_INVALID_ARG
+    assert call(S=0, dq=None, delta=None) == 0

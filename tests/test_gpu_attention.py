@@ -128,3 +128,79 @@ def test_attention_full_size_sampled_rows():
     r1 = torch_api.attention_forward(t[0], t[1], ones, causal=wl.causal)
     torch.cuda.synchronize()
     assert float((r1.O - 1.0).abs().max()) <= 1e-5
+
+
+# ------------------------------------------------------------------ backward
+#
+# dQ, dK, dV against the fp64 oracle's exact gradient for the same bf16
+# inputs and an upstream dO rounded to bf16.  Tolerance 1e-2 relative L2 per
+# gradient (derived like the loss path's dH / dW: the probabilities and dS
+# enter the products rounded to bf16, <= 2^-9 relative each, and every
+# gradient is a sum of many such products).  The forward's O and lse feed
+# the backward as they would in training.
+
+def _run_bwd(Q, K, V, dO, causal, scale=None):
+    import torch
+    from vocab_cross_entropy_valid_amd import torch_api
+    dev = torch.device("cuda:0")
+    t = [torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (Q, K, V, dO)]
+    fwd = torch_api.attention_forward(*t[:3], causal=causal, scale=scale)
+    g = torch_api.attention_backward(*t[:3], fwd, t[3], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return g.dQ.cpu().numpy(), g.dK.cpu().numpy(), g.dV.cpu().numpy()
+
+
+BWD_CASES = [
+    # B, H, S, D, causal, seed
+    (1, 2, 200, 64, False, 621),
+    (2, 2, 257, 128, True, 622),     # ragged query, key and 32-query blocks
+    (1, 1, 1, 128, True, 623),
+    (1, 2, 130, 128, False, 624),
+    (1, 3, 512, 128, True, 625),     # several key groups of 128, diagonal skips
+]
+
+
+@pytest.mark.parametrize("B,H,S,D,causal,seed", BWD_CASES)
+def test_attention_backward_matches_oracle(B, H, S, D, causal, seed):
+    announce(f"attention backward B{B} H{H} S{S} D{D} causal={causal}")
+    Q, K, V = workloads.attention_inputs(B, H, S, D, seed)
+    dO = workloads.attention_inputs(B, H, S, D, seed + 1000)[0]
+    dQ, dK, dV = _run_bwd(Q, K, V, dO, causal)
+    ref = oracle.attention_backward(Q, K, V, dO, causal=causal)
+    for name, got, exp in (("dQ", dQ, ref.dQ), ("dK", dK, ref.dK), ("dV", dV, ref.dV)):
+        assert np.all(np.isfinite(got)), name
+        assert rel_l2(got, exp) <= 1e-2, (name, rel_l2(got, exp))
+
+
+def test_attention_backward_explicit_scale_and_determinism():
+    announce("attention backward explicit scale, determinism")
+    Q, K, V = workloads.attention_inputs(1, 2, 190, 128, 626, std=2.0)
+    dO = workloads.attention_inputs(1, 2, 190, 128, 627)[0]
+    a = _run_bwd(Q, K, V, dO, True, scale=0.2)
+    ref = oracle.attention_backward(Q, K, V, dO, causal=True, scale=0.2)
+    for got, exp in zip(a, (ref.dQ, ref.dK, ref.dV)):
+        assert rel_l2(got, exp) <= 1e-2
+    b = _run_bwd(Q, K, V, dO, True, scale=0.2)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.slow
+def test_attention_backward_full_size_sampled_heads():
+    """The benchmarked shape; the oracle recomputes whole sampled heads."""
+    import torch
+    from vocab_cross_entropy_valid_amd import torch_api
+    wl = workloads.ATTENTION
+    announce("attention backward full size: inputs")
+    Q, K, V = workloads.attention_inputs(wl.B, wl.H, wl.S, wl.D, wl.seed)
+    dO = workloads.attention_inputs(wl.B, wl.H, wl.S, wl.D, wl.seed + 1)[0]
+    dev = torch.device("cuda:0")
+    t = [torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (Q, K, V, dO)]
+    announce("attention backward full size: GPU")
+    fwd = torch_api.attention_forward(*t[:3], causal=wl.causal)
+    g = torch_api.attention_backward(*t[:3], fwd, t[3], causal=wl.causal)
+    torch.cuda.synchronize()
+    for b, hh in ((0, 0), (wl.B - 1, wl.H - 1), (3, 17)):
+        ref = oracle.attention_backward(Q[b, hh], K[b, hh], V[b, hh], dO[b, hh], causal=wl.causal)
+        for name, got, exp in (("dQ", g.dQ, ref.dQ), ("dK", g.dK, ref.dK), ("dV", g.dV, ref.dV)):
+            r = rel_l2(got[b, hh].cpu().numpy(), exp)
+            assert r <= 1e-2, (name, b, hh, r)

@@ -62,6 +62,8 @@ SIGNATURES = {
     "lce_embed_backward": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
     "lce_attention_forward": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, ctypes.c_float,
                                      _P, _P, _P]),
+    "lce_attention_backward": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT,
+                                      ctypes.c_float, _P, _P, _P, _P, _P]),
     "lce_check_error": (_INT, [_P, _P]),
     "lce_status_string": (ctypes.c_char_p, [_INT]),
     "lce_last_error": (ctypes.c_char_p, []),
@@ -187,6 +189,12 @@ def lce_embed_backward(dX, input_ids, valid_idx, valid_count, N, d, V, dW, accum
 def lce_attention_forward(Q, K, V, B, H, S, D, causal, scale, O, lse, stream) -> None:
     _check(load().lce_attention_forward(Q, K, V, B, H, S, D, causal, scale, O, lse, stream),
            "lce_attention_forward")
+
+
+def lce_attention_backward(Q, K, V, O, lse, dO, B, H, S, D, causal, scale, dQ, dK, dV, delta,
+                           stream) -> None:
+    _check(load().lce_attention_backward(Q, K, V, O, lse, dO, B, H, S, D, causal, scale, dQ, dK,
+                                         dV, delta, stream), "lce_attention_backward")
 
 
 def lce_check_error(err_flag, stream) -> None:

@@ -659,6 +659,47 @@ lce_status lce_attention_forward(const void* Q, const void* K, const void* V, in
   return LCE_OK;
 }
 
+lce_status lce_attention_backward(const void* Q, const void* K, const void* V, const float* O,
+                                  const float* lse, const void* dO, int64_t B, int64_t H,
+                                  int64_t S, int64_t D, int causal, float scale, float* dQ,
+                                  float* dK, float* dV, float* delta, void* stream) {
+  g_err.clear();
+  if (B < 0 || H < 0 || S < 0) return fail(LCE_ERR_INVALID_ARG, "B, H and S must be >= 0");
+  if (D != 64 && D != 128) return fail(LCE_ERR_UNSUPPORTED, "head dimension D must be 64 or 128");
+  if (causal != 0 && causal != 1) return fail(LCE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(LCE_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1 / sqrt(D))");
+  const int64_t BH = B * H;
+  if (BH == 0 || S == 0) return LCE_OK;
+  const int64_t lim = (int64_t)1 << 31;
+  if (S >= lim || BH >= lim || ((S + 127) / 128) * BH >= lim)
+    return fail(LCE_ERR_UNSUPPORTED, "B * H * ceil(S / 128) and S must be below 2^31");
+  if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV || !delta)
+    return fail(LCE_ERR_INVALID_ARG,
+                "Q, K, V, O, lse, dO, dQ, dK, dV and delta must not be NULL");
+  lce::AttnBwdArgs a{};
+  a.Q = (const uint16_t*)Q;
+  a.K = (const uint16_t*)K;
+  a.V = (const uint16_t*)V;
+  a.dO = (const uint16_t*)dO;
+  a.O = O;
+  a.lse = lse;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.delta = delta;
+  a.BH = BH;
+  a.S = (int)S;
+  a.causal = causal;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
+  a.scale = (float)sc;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = run(LCE_K_ATTN, s, [&] { return lce::launch_attn_bwd(a, (int)D, s); });
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return LCE_OK;
+}
+
 lce_status lce_check_error(const int32_t* err_flag, void* stream) {
   g_err.clear();
   if (!err_flag) return fail(LCE_ERR_INVALID_ARG, "err_flag is NULL");

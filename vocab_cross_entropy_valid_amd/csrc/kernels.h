@@ -145,4 +145,26 @@ struct AttnArgs {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s);
 
+
+// Online-softmax attention backward (two passes; see kernels_attn.hip).
+struct AttnBwdArgs {
+  const uint16_t* Q;   // bf16 [B*H, S, D]
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* dO;  // bf16 [B*H, S, D]
+  const float* O;      // f32 [B*H, S, D], the forward output
+  const float* lse;    // f32 [B*H, S], natural log
+  float* dQ;           // f32 [B*H, S, D]
+  float* dK;
+  float* dV;
+  float* delta;        // f32 [B*H, S] scratch: rowsum(dO * O)
+  int64_t BH;
+  int S;
+  int causal;
+  float scale;
+  float scale_log2;    // scale * log2(e)
+};
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, int D, hipStream_t s);
+
 }  // namespace lce

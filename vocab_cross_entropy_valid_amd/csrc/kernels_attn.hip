@@ -338,4 +338,356 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ backward
+//
+// dV = P^T dO, dP = dO V^T, dS = P (dP - D), D = rowsum(dO O),
+// dQ = scale dS K, dK = scale dS^T Q, with P = exp(scale Q K^T - lse)
+// recomputed tile by tile from the forward's logsumexp: the [S, S]
+// probabilities are never stored in the backward pass either.  Two passes,
+// no atomics (results are deterministic):
+//
+//  * dQ pass: a workgroup takes 128 queries (lane = query, as in the
+//    forward) and streams the keys in blocks of 64: S^T = K Q^T and
+//    dP^T = V dO^T on the MFMA (Q and dO fragments stay in registers),
+//    dS^T formed in the lane, dQ^T += K^T dS^T with K^T laid out in LDS in
+//    the paired-chunk order of the forward's V^T.  It also writes D.
+//  * dK / dV pass: a workgroup takes 128 keys (lane = key) and streams the
+//    queries in blocks of 32: S = Q K^T and dP = dO V^T (lse and D of the
+//    block's queries from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T
+//    with dO^T and Q^T in the paired-chunk layout.
+//
+// Tiles are staged through registers into LDS, single buffered: a first,
+// plain version of this pass.
+
+namespace {
+
+// transposed tile of T keys (or queries) per row: 16-byte chunks pairing
+// units u0 and u0 + 2 of 4 entries, XOR-swizzled by (row / 2) % (T / 8)
+template <int T>
+__device__ __forceinline__ int tt_chunk_offset(int row, int c) {
+  return row * (T * 2) + ((c ^ ((row >> 1) & (T / 8 - 1))) << 4);
+}
+
+template <int T>
+__device__ __forceinline__ int tt_unit_offset(int row, int u) {
+  const int u0 = u & ~2;
+  return tt_chunk_offset<T>(row, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
+}
+
+// rows [row0, row0 + R) of a [S, D] bf16 head into a row-major swizzled tile
+// (rows past S are zeros)
+template <int D, int R, int NT>
+__device__ __forceinline__ void stage_rows(char* dst, const bf16_t* src, int row0, int S, int tid) {
+  constexpr int C = D / 8;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int it = 0; it < (R * C + NT - 1) / NT; ++it) {
+    const int idx = it * NT + tid;
+    if (idx >= R * C) break;
+    const int row = idx / C, c = idx % C;
+    const int r = row0 + row;
+    const u32x4 v = r < S ? *(const u32x4*)(src + (int64_t)r * D + 8 * c) : z;
+    *(u32x4*)(dst + k_offset(row, c, C)) = v;
+  }
+}
+
+// the same rows transposed: row = dimension, entries = the R rows, in the
+// paired-chunk layout of tt_unit_offset<R>
+template <int D, int R, int NT>
+__device__ __forceinline__ void stage_rows_t(char* dst, const bf16_t* src, int row0, int S, int tid) {
+  constexpr int kUnits = (D / 8) * (R / 4);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int it = 0; it < (kUnits + NT - 1) / NT; ++it) {
+    const int unit = it * NT + tid;
+    if (unit >= kUnits) break;
+    const int kg = unit % (R / 4);  // entries 4 kg .. 4 kg + 3
+    const int dg = unit / (R / 4);  // dims 8 dg .. 8 dg + 7
+    u32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = row0 + 4 * kg + q;
+      v[q] = r < S ? *(const u32x4*)(src + (int64_t)r * D + 8 * dg) : z;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 u;
+      u[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+      u[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+      *(u32x2*)(dst + tt_unit_offset<R>(8 * dg + e, kg)) = u;
+    }
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace
+
+// dQ pass (and D = rowsum(dO O))
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int C = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int kTile = kKBlock * D * 2;  // 64 rows x D (= D rows x 64 entries)
+  __shared__ __attribute__((aligned(16))) char lds[3 * kTile];
+  char* lk = lds;               // K rows, row-major
+  char* lkt = lds + kTile;      // K^T, paired chunks
+  char* lv = lds + 2 * kTile;   // V rows, row-major
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int S = a.S;
+  const int nqb = (S + kQBlock - 1) / kQBlock;
+  const int qb = nqb - 1 - (int)(blockIdx.x / a.BH);
+  const int64_t bh = blockIdx.x % a.BH;
+  const int64_t head = bh * (int64_t)S * D;
+  const int q0 = qb * kQBlock + 32 * wave;
+  const int q = q0 + j;
+  const int qc = q < S ? q : S - 1;
+
+  // Q and dO fragments (B operands), and D = rowsum(dO O) of this lane's query
+  u32x4 qf[KS], df[KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int64_t off = head + (int64_t)qc * D + 16 * s + 8 * h;
+    qf[s] = *(const u32x4*)(a.Q + off);
+    df[s] = *(const u32x4*)(a.dO + off);
+    const f32x4 o0 = *(const f32x4*)(a.O + off);
+    const f32x4 o1 = *(const f32x4*)(a.O + off + 4);
+    dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
+             bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
+             bf16_lo(df[s][3]) * o1[2] + bf16_hi(df[s][3]) * o1[3];
+  }
+  const float Dq = dpart + __shfl_xor(dpart, 32);
+  const float lse2 = a.lse[bh * S + qc] * kLog2e;
+  if (h == 0 && q < S) a.delta[bh * S + q] = Dq;
+  const float c = a.scale_log2;
+
+  f32x16 dq[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[m][i] = 0.f;
+
+  const int kend = a.causal ? min(S, (qb + 1) * kQBlock) : S;
+  const int nkb = (kend + kKBlock - 1) / kKBlock;
+  const bf16_t* Kh = a.K + head;
+  const bf16_t* Vh = a.V + head;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * kKBlock;
+    __syncthreads();  // the previous block's reads are done
+    stage_rows<D, kKBlock, kAttnThreads>(lk, Kh, k0, S, tid);
+    stage_rows_t<D, kKBlock, kAttnThreads>(lkt, Kh, k0, S, tid);
+    stage_rows<D, kKBlock, kAttnThreads>(lv, Vh, k0, S, tid);
+    __syncthreads();
+    if (a.causal && k0 > q0 + 31) continue;
+
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[mt][i] = 0.f;
+        dp[mt][i] = 0.f;
+      }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int off = k_offset(32 * mt + j, 2 * s + h, C);
+        Mma<bf16_t>::run(sc[mt], *(const u32x4*)(lk + off), qf[s]);
+        Mma<bf16_t>::run(dp[mt], *(const u32x4*)(lv + off), df[s]);
+      }
+    const bool need_mask = k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0);
+    const int lim = a.causal ? min(q, S - 1) : S - 1;
+    u32x4 dsf[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float ds[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 8 * g + 2 * w + e;
+            float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
+            if (need_mask && k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) p = 0.f;
+            ds[e] = p * (dp[mt][i] - Dq);
+          }
+          dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
+        }
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const u32x4 af = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(32 * m + j, 4 * mt + 2 * g + h));
+          Mma<bf16_t>::run(dq[m], af, dsf[mt][g]);
+        }
+  }
+  if (q >= S) return;
+  float* dQq = a.dQ + head + (int64_t)q * D;
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v = {dq[m][4 * r4] * a.scale, dq[m][4 * r4 + 1] * a.scale,
+                 dq[m][4 * r4 + 2] * a.scale, dq[m][4 * r4 + 3] * a.scale};
+      *(f32x4*)(dQq + 32 * m + 8 * r4 + 4 * h) = v;
+    }
+}
+
+// dK / dV pass
+constexpr int kKvKeys = 128;  // keys per workgroup (32 per wave)
+constexpr int kKvQ = 32;      // queries per block
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
+  constexpr int C = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
+  constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
+  __shared__ __attribute__((aligned(16))) char lds[2 * kKV + 4 * kQT + 2 * kKvQ * 4];
+  char* lk = lds;
+  char* lv = lds + kKV;
+  char* lq = lds + 2 * kKV;             // Q rows
+  char* ldo = lq + kQT;                 // dO rows
+  char* lqt = ldo + kQT;                // Q^T
+  char* ldot = lqt + kQT;               // dO^T
+  float* llse = (float*)(ldot + kQT);   // lse * log2(e) of the block's queries (+inf past S)
+  float* ldel = llse + kKvQ;            // D of the block's queries
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int S = a.S;
+  const int nkb = (S + kKvKeys - 1) / kKvKeys;
+  const int kblk = (int)(blockIdx.x / a.BH);
+  const int64_t bh = blockIdx.x % a.BH;
+  const int64_t head = bh * (int64_t)S * D;
+  const int kbase = kblk * kKvKeys;
+  const int k0w = kbase + 32 * wave;  // first key of this wave
+  const int kk = k0w + j;             // this lane's key
+  const float c = a.scale_log2;
+  (void)nkb;
+
+  stage_rows<D, kKvKeys, kAttnThreads>(lk, a.K + head, kbase, S, tid);
+  stage_rows<D, kKvKeys, kAttnThreads>(lv, a.V + head, kbase, S, tid);
+
+  f32x16 dk[MD], dv[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[m][i] = 0.f;
+      dv[m][i] = 0.f;
+    }
+
+  const int nq = (S + kKvQ - 1) / kKvQ;
+  const int qstart = a.causal ? kbase / kKvQ : 0;
+  for (int qbk = qstart; qbk < nq; ++qbk) {
+    const int qb0 = qbk * kKvQ;
+    __syncthreads();  // the previous block's reads are done (and K / V staged)
+    stage_rows<D, kKvQ, kAttnThreads>(lq, a.Q + head, qb0, S, tid);
+    stage_rows<D, kKvQ, kAttnThreads>(ldo, a.dO + head, qb0, S, tid);
+    stage_rows_t<D, kKvQ, kAttnThreads>(lqt, a.Q + head, qb0, S, tid);
+    stage_rows_t<D, kKvQ, kAttnThreads>(ldot, a.dO + head, qb0, S, tid);
+    if (tid < kKvQ) {
+      const int qq = qb0 + tid;
+      llse[tid] = qq < S ? a.lse[bh * S + qq] * kLog2e : INFINITY;
+      ldel[tid] = qq < S ? a.delta[bh * S + qq] : 0.f;
+    }
+    __syncthreads();
+    if (a.causal && qb0 + kKvQ - 1 < k0w) continue;  // every query before the wave's keys
+
+    // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4
+    f32x16 sc, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = 0.f;
+      dp[i] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int qo = k_offset(j, 2 * s + h, C);
+      const int ko = k_offset(32 * wave + j, 2 * s + h, C);
+      Mma<bf16_t>::run(sc, *(const u32x4*)(lq + qo), *(const u32x4*)(lk + ko));
+      Mma<bf16_t>::run(dp, *(const u32x4*)(ldo + qo), *(const u32x4*)(lv + ko));
+    }
+    const bool diag = a.causal && qb0 < k0w + 32;
+    u32x4 pp[2], ps[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = *(const f32x4*)(llse + 8 * r4 + 4 * h);
+      const f32x4 d4 = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * r4 + e;
+        float pv = fast_exp2(fmaf(sc[i], c, -l4[e]));  // 0 past S (lse = +inf)
+        if (diag && qb0 + 8 * r4 + 4 * h + e < kk) pv = 0.f;
+        p[e] = pv;
+        ds[e] = pv * (dp[i] - d4[e]);
+      }
+      // values i = 8 g .. 8 g + 7 form operand g: r4 = 2 g, 2 g + 1
+      const int g = r4 >> 1, w0 = (r4 & 1) * 2;
+      pp[g][w0] = cvt_pk_bf16(p[0], p[1]);
+      pp[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
+      ps[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
+      ps[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
+        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
+        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
+      }
+  }
+  if (kk >= S) return;
+  float* dKk = a.dK + head + (int64_t)kk * D;
+  float* dVk = a.dV + head + (int64_t)kk * D;
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * m + 8 * r4 + 4 * h;
+      f32x4 vk = {dk[m][4 * r4] * a.scale, dk[m][4 * r4 + 1] * a.scale,
+                  dk[m][4 * r4 + 2] * a.scale, dk[m][4 * r4 + 3] * a.scale};
+      f32x4 vv = {dv[m][4 * r4], dv[m][4 * r4 + 1], dv[m][4 * r4 + 2], dv[m][4 * r4 + 3]};
+      *(f32x4*)(dKk + d0) = vk;
+      *(f32x4*)(dVk + d0) = vv;
+    }
+}
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, int D, hipStream_t s) {
+  if (a.S <= 0 || a.BH <= 0) return hipSuccess;
+  const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
+  const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
+  if (D == 128) {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3((unsigned)(nqb * a.BH)), dim3(kAttnThreads), 0,
+                       s, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads),
+                       0, s, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3((unsigned)(nqb * a.BH)), dim3(kAttnThreads), 0,
+                       s, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads),
+                       0, s, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace lce

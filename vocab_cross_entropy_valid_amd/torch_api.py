@@ -389,3 +389,35 @@ def attention_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal:
                                0.0 if scale is None else float(scale), _ptr(out.O), _ptr(out.lse),
                                _stream(dev))
     return out
+
+
+@dataclasses.dataclass
+class AttentionGrads:
+    dQ: torch.Tensor  # f32 [B, H, S, D]
+    dK: torch.Tensor
+    dV: torch.Tensor
+
+
+def attention_backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, fwd: AttentionOut,
+                       dO: torch.Tensor, causal: bool = True, scale: Optional[float] = None,
+                       out: Optional[AttentionGrads] = None,
+                       delta: Optional[torch.Tensor] = None) -> AttentionGrads:
+    """lce_attention_backward: dQ, dK, dV for an upstream bf16 dO."""
+    for t in (Q, K, V, dO):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("Q, K, V and dO must be contiguous bf16 [B, H, S, D] GPU tensors")
+    if Q.shape != K.shape or Q.shape != V.shape or Q.shape != dO.shape:
+        raise ValueError("Q, K, V and dO must have the same shape")
+    B, H, S, D = Q.shape
+    dev = Q.device
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = AttentionGrads(dQ=torch.empty(B, H, S, D, **f32), dK=torch.empty(B, H, S, D, **f32),
+                             dV=torch.empty(B, H, S, D, **f32))
+    if delta is None:
+        delta = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+    _lib.lce_attention_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(fwd.O), _ptr(fwd.lse), _ptr(dO),
+                                B, H, S, D, 1 if causal else 0,
+                                0.0 if scale is None else float(scale), _ptr(out.dQ),
+                                _ptr(out.dK), _ptr(out.dV), _ptr(delta), _stream(dev))
+    return out
