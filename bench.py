@@ -42,7 +42,8 @@ KERNEL_FILE = {"compact": "kernels_fwd.hip", "fwd": "kernels_fwd.hip", "merge": 
                "reduce": "kernels_fwd.hip", "zero": "kernels_bwd.hip",
                "transpose": "kernels_bwd.hip", "bwd_g": "kernels_bwd.hip", "dh": "kernels_bwd.hip",
                "dw": "kernels_bwd.hip", "gemm": "kernels_bwd.hip", "embed": "kernels_embed.hip",
-               "attn": "kernels_attn.hip"}
+               "attn": "kernels_attn.hip", "attn_dq": "kernels_attn.hip",
+               "attn_dkv": "kernels_attn.hip"}
 
 
 def _log(msg):
@@ -131,7 +132,7 @@ def cpu_baseline(H, W, y, target_s: float):
                       f"backward, {t:.1f} s; host cores available: {cores}"}
 
 
-ATTN_METRIC = "online-softmax attention forward TFLOP/s and % bf16 MFMA peak, causal, B=8 H=32 S=2048 D=128"
+ATTN_METRIC = "online-softmax attention forward+backward TFLOP/s and % bf16 MFMA peak, causal, B=8 H=32 S=2048 D=128"
 
 
 def attention_pairs(S: int, causal: bool) -> int:
@@ -139,16 +140,17 @@ def attention_pairs(S: int, causal: bool) -> int:
     return S * (S + 1) // 2 if causal else S * S
 
 
-def cpu_baseline_attention(wl, Q, K, V, target_s: float):
-    """The fp64 attention oracle on whole heads of the same workload, timed."""
+def cpu_baseline_attention(wl, Q, K, V, dO, target_s: float):
+    """The fp64 attention oracle (forward + backward) on whole heads of the same workload."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    flops_head = 4.0 * wl.D * attention_pairs(wl.S, wl.causal)
+    flops_head = ATTN_FLOPS_PER_PAIR * wl.D * attention_pairs(wl.S, wl.causal)
     t0 = time.perf_counter()
     heads = 0
     while heads < wl.B * wl.H:
         b, h = divmod(heads, wl.H)
         oracle.attention_forward(Q[b, h], K[b, h], V[b, h], causal=wl.causal)
+        oracle.attention_backward(Q[b, h], K[b, h], V[b, h], dO[b, h], causal=wl.causal)
         heads += 1
         if time.perf_counter() - t0 >= target_s:
             break
@@ -156,11 +158,21 @@ def cpu_baseline_attention(wl, Q, K, V, target_s: float):
     return {"value": heads * flops_head / t / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{heads} of the {wl.B * wl.H} heads (S {wl.S}, D {wl.D}, causal), fp64 "
-                      f"full-score softmax, {t:.1f} s; host cores available: {cores}"}
+                      f"full-score softmax forward + backward, {t:.1f} s; host cores "
+                      f"available: {cores}"}
+
+
+# FLOPs per unmasked (query, key) pair, in units of D: forward S = Q K^T and
+# O = P V (2 + 2); backward S recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K,
+# dK = dS^T Q (2 each).  The backward's two passes execute S and dP twice:
+# the dQ pass runs S, dP, dQ (6) and the dK / dV pass S, dP, dV, dK (8).
+ATTN_FLOPS_PER_PAIR = 14
+ATTN_KERNEL_FLOPS_PER_PAIR = {"attn": 4, "attn_dq": 6, "attn_dkv": 8}
 
 
 def bench_attention(args) -> None:
-    """Times lce_attention_forward on the Llama-3-8B-shaped attention batch."""
+    """Times lce_attention_forward + lce_attention_backward on the Llama-3-8B-shaped
+    attention batch (one step = forward, then backward for a fixed upstream dO)."""
     import torch
 
     import workloads
@@ -169,56 +181,78 @@ def bench_attention(args) -> None:
     wl = workloads.ATTENTION
     _log(f"[bench] generating {wl.name}: B={wl.B} H={wl.H} S={wl.S} D={wl.D} causal={wl.causal}")
     Q, K, V = workloads.attention_inputs(wl.B, wl.H, wl.S, wl.D, wl.seed)
+    dO = workloads.attention_inputs(wl.B, wl.H, wl.S, wl.D, wl.seed + 1000)[0]
     dev = torch.device("cuda:0")
     t = [torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (Q, K, V)]
-    out = torch_api.AttentionOut(
-        O=torch.empty(wl.B, wl.H, wl.S, wl.D, dtype=torch.float32, device=dev),
-        lse=torch.empty(wl.B, wl.H, wl.S, dtype=torch.float32, device=dev))
-    torch.cuda.synchronize()
-    # one launch takes ~0.5 ms: the clock needs tens of launches to settle, so
-    # the attention leg warms up with at least 30 (reported as "warmup")
-    warmup = max(args.warmup, 30)
-    for _ in range(warmup):
+    dOt = torch.from_numpy(dO).to(dev).to(torch.bfloat16).contiguous()
+    f32 = dict(dtype=torch.float32, device=dev)
+    shape = (wl.B, wl.H, wl.S, wl.D)
+    out = torch_api.AttentionOut(O=torch.empty(*shape, **f32),
+                                 lse=torch.empty(wl.B, wl.H, wl.S, **f32))
+    grads = torch_api.AttentionGrads(dQ=torch.empty(*shape, **f32), dK=torch.empty(*shape, **f32),
+                                     dV=torch.empty(*shape, **f32))
+    delta = torch.empty(wl.B, wl.H, wl.S, **f32)
+
+    def step():
         torch_api.attention_forward(*t, causal=wl.causal, out=out)
+        torch_api.attention_backward(*t, out, dOt, causal=wl.causal, out=grads, delta=delta)
+
+    torch.cuda.synchronize()
+    # one step takes a few ms: the clock needs tens of launches to settle, so
+    # the attention leg warms up with at least 20 steps (reported as "warmup")
+    warmup = max(args.warmup, 20)
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     _lib.lce_timing_reset()
     _lib.lce_timing_enable(True)
-    _log(f"[bench] timing {args.steps} attention launches")
+    _log(f"[bench] timing {args.steps} attention steps (forward + backward)")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        torch_api.attention_forward(*t, causal=wl.causal, out=out)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     _lib.lce_timing_enable(False)
-    ms, n = _lib.lce_timing_query(_lib.KERNEL_CLASSES.index("attn"))
+    pairs = attention_pairs(wl.S, wl.causal) * wl.B * wl.H
+    kernels = {}
+    for name, per_pair in ATTN_KERNEL_FLOPS_PER_PAIR.items():
+        ms, n = _lib.lce_timing_query(_lib.KERNEL_CLASSES.index(name))
+        avg_us = 1e3 * ms / max(n, 1)
+        fl = per_pair * wl.D * pairs
+        kernels[name] = {"ms_per_step": round(ms / args.steps, 4), "launches_per_step": n / args.steps,
+                         "avg_launch_us": round(avg_us, 2), "flops_per_launch": fl,
+                         "tflops": round(fl / (avg_us * 1e-6) / 1e12, 2)}
     _lib.lce_timing_reset()
-    assert bool(torch.isfinite(out.O).all())
+    for x in (out.O, grads.dQ, grads.dK, grads.dV):
+        assert bool(torch.isfinite(x).all())
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, dev)
-    flops = 4.0 * wl.D * attention_pairs(wl.S, wl.causal) * wl.B * wl.H
+    flops = ATTN_FLOPS_PER_PAIR * wl.D * pairs
     ms_step = 1e3 * elapsed / args.steps
     tflops = flops / (ms_step * 1e-3) / 1e12
-    avg_us = 1e3 * ms / n
-    ach = flops / (avg_us * 1e-6) / 1e12
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
     res = {
         "metric": ATTN_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic: seeded N(0, 1) Q, K, V rounded to bf16 (no dataset)",
+        "data": "synthetic: seeded N(0, 1) Q, K, V and dO rounded to bf16 (no dataset)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "D": wl.D,
                    "causal": wl.causal},
         "pct_peak_bf16": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "positions_per_s": round(wl.B * wl.S / (ms_step * 1e-3), 1),
         "score_matrix_bytes_avoided": 4 * wl.B * wl.H * wl.S * wl.S,
-        "roofline": {"kernel": "attn", "bound": "mfma", "achieved": round(ach, 2),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": kd["tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counter_traffic("attn", wl.name), "flops_per_launch": flops,
-                     "avg_launch_us": round(avg_us, 2)},
+                     "frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counter_traffic(dom, wl.name),
+                     "flops_per_launch": kd["flops_per_launch"],
+                     "avg_launch_us": kd["avg_launch_us"]},
+        "kernels": kernels,
     }
     if args.cpu_seconds > 0:
         _log("[bench] timing the CPU attention oracle on whole heads")
-        res["cpu_baseline"] = cpu_baseline_attention(wl, Q, K, V, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_attention(wl, Q, K, V, dO, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -320,7 +320,9 @@ typedef enum {
   LCE_K_GEMM = 9,      /* lce_gemm_nt                                    */
   LCE_K_EMBED = 10,    /* embedding gather / gradient scatter-sum        */
   LCE_K_ATTN = 11,     /* online-softmax attention forward               */
-  LCE_K_COUNT = 12
+  LCE_K_ATTN_DQ = 12,  /* attention backward, dQ pass (and rowsum(dO O)) */
+  LCE_K_ATTN_DKV = 13, /* attention backward, dK / dV pass               */
+  LCE_K_COUNT = 14
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -30,7 +30,7 @@ LCE_MEAN = 0
 LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
-                  "bwd_g", "dh", "dw", "gemm", "embed", "attn")
+                  "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""

@@ -695,8 +695,10 @@ lce_status lce_attention_backward(const void* Q, const void* K, const void* V, c
   a.scale = (float)sc;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = run(LCE_K_ATTN, s, [&] { return lce::launch_attn_bwd(a, (int)D, s); });
-  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  hipError_t e = run(LCE_K_ATTN_DQ, s, [&] { return lce::launch_attn_bwd_dq(a, (int)D, s); });
+  if (e != hipSuccess) return hip_fail(e, "attention backward (dQ pass) launch");
+  e = run(LCE_K_ATTN_DKV, s, [&] { return lce::launch_attn_bwd_dkv(a, (int)D, s); });
+  if (e != hipSuccess) return hip_fail(e, "attention backward (dK/dV pass) launch");
   return LCE_OK;
 }
 

@@ -165,6 +165,9 @@ struct AttnBwdArgs {
   float scale_log2;    // scale * log2(e)
 };
 
-hipError_t launch_attn_bwd(const AttnBwdArgs& a, int D, hipStream_t s);
+// The two passes launch separately: dQ (which also writes delta) first, then
+// dK / dV, which reads delta.
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s);
+hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s);
 
 }  // namespace lce

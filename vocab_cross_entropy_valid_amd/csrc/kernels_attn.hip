@@ -356,8 +356,10 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 //    block's queries from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T
 //    with dO^T and Q^T in the paired-chunk layout.
 //
-// Tiles are staged through registers into LDS, single buffered: a first,
-// plain version of this pass.
+// Tiles are staged through registers into LDS, single buffered.  The dK / dV
+// pass loads the next query block into registers while the current one
+// computes; each thread's load unit (4 rows x 8 dims) feeds both the
+// row-major and the transposed copy.
 
 namespace {
 
@@ -423,6 +425,47 @@ __device__ __forceinline__ void stage_rows_t(char* dst, const bf16_t* src, int r
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// A load unit: rows 4 kg .. 4 kg + 3 and dims 8 dg .. 8 dg + 7 of an R-row
+// tile of a [S, D] head, unit = dg * (R / 4) + kg.  The rows are clamped to
+// S - 1 at load time (always in bounds) and zeroed at store time.
+template <int D, int R>
+__device__ __forceinline__ void load_unit(u32x4 (&v)[4], const bf16_t* src, int row0, int S,
+                                          int unit) {
+  const int kg = unit % (R / 4);
+  const int dg = unit / (R / 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = min(row0 + 4 * kg + q, S - 1);
+    v[q] = *(const u32x4*)(src + (int64_t)r * D + 8 * dg);
+  }
+}
+
+// The unit into the row-major swizzled tile rm and, transposed, into the
+// paired-chunk tile tt (the layouts of stage_rows and stage_rows_t).
+template <int D, int R>
+__device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char* tt, int row0,
+                                           int S, int unit) {
+  constexpr int C = D / 8;
+  const int kg = unit % (R / 4);
+  const int dg = unit / (R / 4);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = row0 + 4 * kg + q < S ? vin[q] : z;
+    *(u32x4*)(rm + k_offset(4 * kg + q, dg, C)) = v[q];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    u32x2 u;
+    u[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+    u[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+    *(u32x2*)(tt + tt_unit_offset<R>(8 * dg + e, kg)) = u;
+  }
+}
 
 }  // namespace
 
@@ -557,22 +600,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   constexpr int MD = D / 32;
   constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
   constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  __shared__ __attribute__((aligned(16))) char lds[2 * kKV + 4 * kQT + 2 * kKvQ * 4];
+  // two query-block slots: Q, dO, Q^T, dO^T, lse and D of one block each
+  constexpr int kSlot = 4 * kQT + 2 * kKvQ * 4;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kKV + 2 * kSlot];
   char* lk = lds;
   char* lv = lds + kKV;
-  char* lq = lds + 2 * kKV;             // Q rows
-  char* ldo = lq + kQT;                 // dO rows
-  char* lqt = ldo + kQT;                // Q^T
-  char* ldot = lqt + kQT;               // dO^T
-  float* llse = (float*)(ldot + kQT);   // lse * log2(e) of the block's queries (+inf past S)
-  float* ldel = llse + kKvQ;            // D of the block's queries
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31;
   const int h = lane >> 5;
   const int S = a.S;
-  const int nkb = (S + kKvKeys - 1) / kKvKeys;
   const int kblk = (int)(blockIdx.x / a.BH);
   const int64_t bh = blockIdx.x % a.BH;
   const int64_t head = bh * (int64_t)S * D;
@@ -580,10 +618,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   const int k0w = kbase + 32 * wave;  // first key of this wave
   const int kk = k0w + j;             // this lane's key
   const float c = a.scale_log2;
-  (void)nkb;
 
   stage_rows<D, kKvKeys, kAttnThreads>(lk, a.K + head, kbase, S, tid);
   stage_rows<D, kKvKeys, kAttnThreads>(lv, a.V + head, kbase, S, tid);
+
+  __syncthreads();
+  // this lane's K and V fragments (B operands of S and dP) for the whole pass
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ko = k_offset(32 * wave + j, 2 * s + h, C);
+    kf[s] = *(const u32x4*)(lk + ko);
+    vf[s] = *(const u32x4*)(lv + ko);
+  }
 
   f32x16 dk[MD], dv[MD];
 #pragma unroll
@@ -596,21 +643,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
 
   const int nq = (S + kKvQ - 1) / kKvQ;
   const int qstart = a.causal ? kbase / kKvQ : 0;
-  for (int qbk = qstart; qbk < nq; ++qbk) {
+  // a query block in registers: load unit u of Q (u < kUnits) or of dO, and
+  // the lse (threads 0-31) or D (threads 32-63) of one query
+  constexpr int kUnits = (D / 8) * (kKvQ / 4);
+  const bool unit_on = tid < 2 * kUnits;
+  const bool unit_q = tid < kUnits;
+  const int unit = unit_q ? tid : tid - kUnits;
+  const bf16_t* usrc = (unit_q ? a.Q : a.dO) + head;
+  const float* vsrc = (tid < kKvQ ? a.lse : a.delta) + bh * S;
+  auto prefetch = [&](u32x4 (&pre)[4], float& pv, int qbk) {
     const int qb0 = qbk * kKvQ;
-    __syncthreads();  // the previous block's reads are done (and K / V staged)
-    stage_rows<D, kKvQ, kAttnThreads>(lq, a.Q + head, qb0, S, tid);
-    stage_rows<D, kKvQ, kAttnThreads>(ldo, a.dO + head, qb0, S, tid);
-    stage_rows_t<D, kKvQ, kAttnThreads>(lqt, a.Q + head, qb0, S, tid);
-    stage_rows_t<D, kKvQ, kAttnThreads>(ldot, a.dO + head, qb0, S, tid);
-    if (tid < kKvQ) {
-      const int qq = qb0 + tid;
-      llse[tid] = qq < S ? a.lse[bh * S + qq] * kLog2e : INFINITY;
-      ldel[tid] = qq < S ? a.delta[bh * S + qq] : 0.f;
+    if (unit_on) load_unit<D, kKvQ>(pre, usrc, qb0, S, unit);
+    if (tid < 2 * kKvQ) pv = vsrc[min(qb0 + (tid & (kKvQ - 1)), S - 1)];
+  };
+  auto stage = [&](const u32x4 (&pre)[4], float pv, int qbk, int slot) {
+    const int qb0 = qbk * kKvQ;
+    char* sl = lds + 2 * kKV + slot * kSlot;
+    if (unit_on)
+      store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S, unit);
+    if (tid < 2 * kKvQ) {
+      float* lv4 = (float*)(sl + 4 * kQT);
+      const bool in = qb0 + (tid & (kKvQ - 1)) < S;
+      lv4[tid] = tid < kKvQ ? (in ? pv * kLog2e : INFINITY) : (in ? pv : 0.f);
     }
-    __syncthreads();
-    if (a.causal && qb0 + kKvQ - 1 < k0w) continue;  // every query before the wave's keys
-
+  };
+  auto compute = [&](int qbk, int slot) {
+    const int qb0 = qbk * kKvQ;
+    if (a.causal && qb0 + kKvQ - 1 < k0w) return;  // every query before the wave's keys
+    const char* sl = lds + 2 * kKV + slot * kSlot;
+    const char* lq = sl;                               // Q rows
+    const char* ldo = sl + kQT;                        // dO rows
+    const char* lqt = sl + 2 * kQT;                    // Q^T
+    const char* ldot = sl + 3 * kQT;                   // dO^T
+    const float* llse = (const float*)(sl + 4 * kQT);  // lse log2(e) (+inf past S)
+    const float* ldel = llse + kKvQ;                   // D
     // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4
     f32x16 sc, dp;
 #pragma unroll
@@ -621,9 +687,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int qo = k_offset(j, 2 * s + h, C);
-      const int ko = k_offset(32 * wave + j, 2 * s + h, C);
-      Mma<bf16_t>::run(sc, *(const u32x4*)(lq + qo), *(const u32x4*)(lk + ko));
-      Mma<bf16_t>::run(dp, *(const u32x4*)(ldo + qo), *(const u32x4*)(lv + ko));
+      Mma<bf16_t>::run(sc, *(const u32x4*)(lq + qo), kf[s]);
+      Mma<bf16_t>::run(dp, *(const u32x4*)(ldo + qo), vf[s]);
     }
     const bool diag = a.causal && qb0 < k0w + 32;
     u32x4 pp[2], ps[2];
@@ -655,6 +720,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
         Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
         Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
       }
+  };
+
+  // Pipeline: block k computes from slot k % 2 while block k + 1, loaded
+  // into registers two blocks earlier, is written to the other slot and
+  // block k + 2 is requested; one barrier per block.  Register set A holds
+  // even blocks (relative to qstart), set B odd ones.
+  u32x4 preA[4], preB[4];
+  float pvA = 0.f, pvB = 0.f;
+  prefetch(preA, pvA, qstart);
+  if (qstart + 1 < nq) prefetch(preB, pvB, qstart + 1);
+  stage(preA, pvA, qstart, 0);
+  if (qstart + 2 < nq) prefetch(preA, pvA, qstart + 2);
+  __syncthreads();
+  for (int qbk = qstart; qbk < nq; qbk += 2) {
+    compute(qbk, 0);
+    if (qbk + 1 < nq) {
+      stage(preB, pvB, qbk + 1, 1);
+      if (qbk + 3 < nq) prefetch(preB, pvB, qbk + 3);
+    }
+    __syncthreads();
+    if (qbk + 1 >= nq) break;
+    compute(qbk + 1, 1);
+    if (qbk + 2 < nq) {
+      stage(preA, pvA, qbk + 2, 0);
+      if (qbk + 4 < nq) prefetch(preA, pvA, qbk + 4);
+    }
+    __syncthreads();
   }
   if (kk >= S) return;
   float* dKk = a.dK + head + (int64_t)kk * D;
@@ -672,21 +764,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     }
 }
 
-hipError_t launch_attn_bwd(const AttnBwdArgs& a, int D, hipStream_t s) {
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
   if (a.S <= 0 || a.BH <= 0) return hipSuccess;
   const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
+  const dim3 grid((unsigned)(nqb * a.BH));
+  if (D == 128)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s) {
+  if (a.S <= 0 || a.BH <= 0) return hipSuccess;
   const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
-  if (D == 128) {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3((unsigned)(nqb * a.BH)), dim3(kAttnThreads), 0,
-                       s, a);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads),
-                       0, s, a);
-  } else {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3((unsigned)(nqb * a.BH)), dim3(kAttnThreads), 0,
-                       s, a);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads),
-                       0, s, a);
-  }
+  const dim3 grid((unsigned)(nkb * a.BH));
+  if (D == 128)
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, grid, dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
