@@ -443,6 +443,30 @@ def main():
         roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": None, "traffic": None}
 
+    # HBM / latency passes: algorithmic bytes per step and the rate they reach
+    esz = 2 if wl.dtype == "bf16" else 4
+    n_vt = -(-wl.V // 256)
+    tpc = max(1, -(-n_vt // 64))
+    J = -(-n_vt // tpc)  # vocabulary chunks of the forward (as the library plans them)
+    pass_bytes = {
+        # labels read; index, count and flag written; loss and lse zeroed on ignored rows
+        "compact": 8 * wl.N + 4 * n_valid + 8 + 8 * (wl.N - n_valid),
+        # (max, sum, target) partials of every chunk read, index and label read,
+        # lse, loss and the compact loss written
+        "merge": 12 * J * n_valid + 12 * n_valid + 12 * n_valid,
+        "reduce": 4 * n_valid + 16,
+        # fp32 dH rows of ignored tokens zeroed, labels read
+        "zero": 4 * (wl.N - n_valid) * wl.d + 8 * wl.N,
+        # H^T of the valid rows and W^T of every vocabulary block, read and written
+        "transpose": 2 * esz * wl.d * (n_valid + wl.V),
+    }
+    hbm_passes = {}
+    for name, nbytes in pass_bytes.items():
+        if name in kernels:
+            gbs = nbytes / (kernels[name]["ms_per_step"] * 1e-3) / 1e9
+            hbm_passes[name] = {"bytes_per_step": int(nbytes), "GB/s": round(gbs, 1),
+                                "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
     if tied is not None and "embed" in kernels:
         k = kernels["embed"]
         tied["embed_ms_per_step"] = round(k["ms_per_step"], 4)
@@ -503,6 +527,7 @@ def main():
         "workspace_bytes": int(ws.numel()),
         "logits_table_bytes_avoided": wl.N * wl.V * 4,
         "roofline": roofline,
+        "hbm_passes": hbm_passes,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "gemm_engine_reference": gemm,
         "tied_input": tied,

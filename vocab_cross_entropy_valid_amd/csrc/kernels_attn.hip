@@ -442,8 +442,9 @@ __device__ __forceinline__ void load_unit(u32x4 (&v)[4], const bf16_t* src, int 
 }
 
 // The unit into the row-major swizzled tile rm and, transposed, into the
-// paired-chunk tile tt (the layouts of stage_rows and stage_rows_t).
-template <int D, int R>
+// paired-chunk tile tt (the layouts of stage_rows and stage_rows_t); with
+// kT false the row-major copy only.
+template <int D, int R, bool kT = true>
 __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char* tt, int row0,
                                            int S, int unit) {
   constexpr int C = D / 8;
@@ -456,6 +457,7 @@ __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char
     v[q] = row0 + 4 * kg + q < S ? vin[q] : z;
     *(u32x4*)(rm + k_offset(4 * kg + q, dg, C)) = v[q];
   }
+  if (!kT) return;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int w = e >> 1;
@@ -469,17 +471,19 @@ __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char
 
 }  // namespace
 
-// dQ pass (and D = rowsum(dO O))
+// dQ pass (and D = rowsum(dO O)).  One wave per SIMD: the next key block is
+// loaded into registers while the current one computes (one load unit feeds
+// K row-major and K^T; V row-major), two LDS slots, one barrier per block;
+// the fragment reads of each phase are issued together into their own
+// registers.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int C = D / 8;
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int kTile = kKBlock * D * 2;  // 64 rows x D (= D rows x 64 entries)
-  __shared__ __attribute__((aligned(16))) char lds[3 * kTile];
-  char* lk = lds;               // K rows, row-major
-  char* lkt = lds + kTile;      // K^T, paired chunks
-  char* lv = lds + 2 * kTile;   // V rows, row-major
+  constexpr int kSlot = 3 * kTile;        // K rows, K^T (paired chunks), V rows
+  __shared__ __attribute__((aligned(16))) char lds[2 * kSlot];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -523,59 +527,116 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   const int nkb = (kend + kKBlock - 1) / kKBlock;
   const bf16_t* Kh = a.K + head;
   const bf16_t* Vh = a.V + head;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * kKBlock;
-    __syncthreads();  // the previous block's reads are done
-    stage_rows<D, kKBlock, kAttnThreads>(lk, Kh, k0, S, tid);
-    stage_rows_t<D, kKBlock, kAttnThreads>(lkt, Kh, k0, S, tid);
-    stage_rows<D, kKBlock, kAttnThreads>(lv, Vh, k0, S, tid);
-    __syncthreads();
-    if (a.causal && k0 > q0 + 31) continue;
 
+  // a key block in registers: units it * 256 + tid, of K below kKU, else of V
+  constexpr int kKU = (D / 8) * (kKBlock / 4);
+  constexpr int kIt = (2 * kKU + kAttnThreads - 1) / kAttnThreads;
+  u32x4 pre[kIt][4];
+  auto prefetch = [&](int kb) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int u = it * kAttnThreads + tid;
+      if (u < 2 * kKU)
+        load_unit<D, kKBlock>(pre[it], u < kKU ? Kh : Vh, kb * kKBlock, S, u < kKU ? u : u - kKU);
+    }
+  };
+  auto stage = [&](int kb, int slot) {
+    char* sl = lds + slot * kSlot;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int u = it * kAttnThreads + tid;
+      if (u < kKU)
+        store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
+      else if (u < 2 * kKU)
+        store_unit<D, kKBlock, false>(pre[it], sl + 2 * kTile, nullptr, kb * kKBlock, S, u - kKU);
+    }
+  };
+  auto compute = [&](int kb, int slot) {
+    const int k0 = kb * kKBlock;
+    if (a.causal && k0 > q0 + 31) return;  // every key after the wave's queries
+    const char* lk = lds + slot * kSlot;
+    const char* lkt = lk + kTile;
+    const char* lv = lk + 2 * kTile;
+    // S^T = K Q^T and dP^T = V dO^T, one 32-key half (mt) at a time
     f32x16 sc[2], dp[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      u32x4 fk[KS], fv[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int off = k_offset(32 * mt + j, 2 * s + h, C);
+        fk[s] = *(const u32x4*)(lk + off);
+        fv[s] = *(const u32x4*)(lv + off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sc[mt][i] = 0.f;
         dp[mt][i] = 0.f;
       }
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int off = k_offset(32 * mt + j, 2 * s + h, C);
-        Mma<bf16_t>::run(sc[mt], *(const u32x4*)(lk + off), qf[s]);
-        Mma<bf16_t>::run(dp[mt], *(const u32x4*)(lv + off), df[s]);
+      for (int s = 0; s < KS; ++s) {
+        Mma<bf16_t>::run(sc[mt], fk[s], qf[s]);
+        Mma<bf16_t>::run(dp[mt], fv[s], df[s]);
       }
-    const bool need_mask = k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0);
-    const int lim = a.causal ? min(q, S - 1) : S - 1;
-    u32x4 dsf[2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float ds[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int i = 8 * g + 2 * w + e;
-            float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
-            if (need_mask && k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) p = 0.f;
-            ds[e] = p * (dp[mt][i] - Dq);
-          }
-          dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
-        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // K^T fragments of dQ^T += K^T dS^T: independent of the softmax
+    u32x4 ft[MD][2][2];
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const u32x4 af = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(32 * m + j, 4 * mt + 2 * g + h));
-          Mma<bf16_t>::run(dq[m], af, dsf[mt][g]);
-        }
+        for (int g = 0; g < 2; ++g)
+          ft[m][mt][g] = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(32 * m + j, 4 * mt + 2 * g + h));
+    __builtin_amdgcn_sched_barrier(0);
+    // dS^T = P^T (dP^T - D); masks (sequence end, causal diagonal) only on
+    // the blocks that need them
+    const int lim = a.causal ? min(q, S - 1) : S - 1;
+    u32x4 dsf[2][2];
+    auto softmax = [&](const bool masked) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float ds[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int i = 8 * g + 2 * w + e;
+              float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
+              if (masked && k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) p = 0.f;
+              ds[e] = p * (dp[mt][i] - Dq);
+            }
+            dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
+          }
+    };
+    if (k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0))
+      softmax(true);
+    else
+      softmax(false);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) Mma<bf16_t>::run(dq[m], ft[m][mt][g], dsf[mt][g]);
+  };
+
+  prefetch(0);
+  stage(0, 0);
+  if (nkb > 1) prefetch(1);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    compute(kb, kb & 1);
+    if (kb + 1 < nkb) {
+      stage(kb + 1, (kb + 1) & 1);  // the slot block kb - 1 used: free since the last barrier
+      if (kb + 2 < nkb) prefetch(kb + 2);
+    }
+    __syncthreads();
   }
   if (q >= S) return;
   float* dQq = a.dQ + head + (int64_t)q * D;
@@ -677,7 +738,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     const char* ldot = sl + 3 * kQT;                   // dO^T
     const float* llse = (const float*)(sl + 4 * kQT);  // lse log2(e) (+inf past S)
     const float* ldel = llse + kKvQ;                   // D
-    // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4
+    // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4.
+    // The block runs in three phases, fenced so that the compiler keeps every
+    // LDS fragment in its own registers: left alone it funnels each read
+    // through one register quad and waits on it right before its MFMA.
+    u32x4 fq[KS], fdo[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int qo = k_offset(j, 2 * s + h, C);
+      fq[s] = *(const u32x4*)(lq + qo);
+      fdo[s] = *(const u32x4*)(ldo + qo);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 sc, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -686,39 +758,63 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int qo = k_offset(j, 2 * s + h, C);
-      Mma<bf16_t>::run(sc, *(const u32x4*)(lq + qo), kf[s]);
-      Mma<bf16_t>::run(dp, *(const u32x4*)(ldo + qo), vf[s]);
+      Mma<bf16_t>::run(sc, fq[s], kf[s]);
+      Mma<bf16_t>::run(dp, fdo[s], vf[s]);
     }
-    const bool diag = a.causal && qb0 < k0w + 32;
-    u32x4 pp[2], ps[2];
+    __builtin_amdgcn_sched_barrier(0);
+    // lse / D of the block's queries and the dO^T / Q^T fragments of the
+    // second products: none depends on the softmax, so their latency hides
+    // under it
+    f32x4 l4[4], d4[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 l4 = *(const f32x4*)(llse + 8 * r4 + 4 * h);
-      const f32x4 d4 = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * r4 + e;
-        float pv = fast_exp2(fmaf(sc[i], c, -l4[e]));  // 0 past S (lse = +inf)
-        if (diag && qb0 + 8 * r4 + 4 * h + e < kk) pv = 0.f;
-        p[e] = pv;
-        ds[e] = pv * (dp[i] - d4[e]);
-      }
-      // values i = 8 g .. 8 g + 7 form operand g: r4 = 2 g, 2 g + 1
-      const int g = r4 >> 1, w0 = (r4 & 1) * 2;
-      pp[g][w0] = cvt_pk_bf16(p[0], p[1]);
-      pp[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
-      ps[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
-      ps[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
+      l4[r4] = *(const f32x4*)(llse + 8 * r4 + 4 * h);
+      d4[r4] = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
     }
+    u32x4 fo[MD][2], fqt[MD][2];
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
-        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
-        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
+        fo[m][g] = *(const u32x4*)(ldot + off);
+        fqt[m][g] = *(const u32x4*)(lqt + off);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // the causal mask only on the diagonal block of the wave (a wave-uniform
+    // branch: the other blocks skip its compare and select per score)
+    u32x4 pp[2], ps[2];
+    auto softmax = [&](const bool masked) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r4 + e;
+          float pv = fast_exp2(fmaf(sc[i], c, -l4[r4][e]));  // 0 past S (lse = +inf)
+          if (masked && qb0 + 8 * r4 + 4 * h + e < kk) pv = 0.f;
+          p[e] = pv;
+          ds[e] = pv * (dp[i] - d4[r4][e]);
+        }
+        // values i = 8 g .. 8 g + 7 form operand g: r4 = 2 g, 2 g + 1
+        const int g = r4 >> 1, w0 = (r4 & 1) * 2;
+        pp[g][w0] = cvt_pk_bf16(p[0], p[1]);
+        pp[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
+        ps[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
+        ps[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
+      }
+    };
+    if (a.causal && qb0 < k0w + 32)
+      softmax(true);
+    else
+      softmax(false);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        Mma<bf16_t>::run(dv[m], fo[m][g], pp[g]);
+        Mma<bf16_t>::run(dk[m], fqt[m][g], ps[g]);
       }
   };
 
