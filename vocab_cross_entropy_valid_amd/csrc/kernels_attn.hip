@@ -654,6 +654,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
 constexpr int kKvKeys = 128;  // keys per workgroup (32 per wave)
 constexpr int kKvQ = 32;      // queries per block
 
+// One wave per SIMD.  Block b of 32 queries runs the S / dP products A(b),
+// then its softmax, and the accumulation C(b) (dV^T += dO^T P^T, dK^T +=
+// Q^T dS^T) is deferred to the next block, where its MFMAs issue under the
+// softmax of b + 1: the wave then keeps the matrix core busy while the VALU
+// works.  Block b lives in LDS slot b % 3 (Q, dO, Q^T, dO^T, lse, D) from its
+// staging two blocks ahead until C(b) has run; the K / V rows are staged
+// through the same LDS once, at the start, into registers.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int C = D / 8;
@@ -661,11 +668,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   constexpr int MD = D / 32;
   constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
   constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  // two query-block slots: Q, dO, Q^T, dO^T, lse and D of one block each
   constexpr int kSlot = 4 * kQT + 2 * kKvQ * 4;
-  __shared__ __attribute__((aligned(16))) char lds[2 * kKV + 2 * kSlot];
-  char* lk = lds;
-  char* lv = lds + kKV;
+  constexpr int kLds = 2 * kKV > 3 * kSlot ? 2 * kKV : 3 * kSlot;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -680,17 +685,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   const int kk = k0w + j;             // this lane's key
   const float c = a.scale_log2;
 
-  stage_rows<D, kKvKeys, kAttnThreads>(lk, a.K + head, kbase, S, tid);
-  stage_rows<D, kKvKeys, kAttnThreads>(lv, a.V + head, kbase, S, tid);
-
-  __syncthreads();
   // this lane's K and V fragments (B operands of S and dP) for the whole pass
   u32x4 kf[KS], vf[KS];
+  {
+    char* lk = lds;
+    char* lv = lds + kKV;
+    stage_rows<D, kKvKeys, kAttnThreads>(lk, a.K + head, kbase, S, tid);
+    stage_rows<D, kKvKeys, kAttnThreads>(lv, a.V + head, kbase, S, tid);
+    __syncthreads();
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int ko = k_offset(32 * wave + j, 2 * s + h, C);
-    kf[s] = *(const u32x4*)(lk + ko);
-    vf[s] = *(const u32x4*)(lv + ko);
+    for (int s = 0; s < KS; ++s) {
+      const int ko = k_offset(32 * wave + j, 2 * s + h, C);
+      kf[s] = *(const u32x4*)(lk + ko);
+      vf[s] = *(const u32x4*)(lv + ko);
+    }
+    __syncthreads();  // the query slots below reuse this LDS
   }
 
   f32x16 dk[MD], dv[MD];
@@ -712,35 +721,55 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   const int unit = unit_q ? tid : tid - kUnits;
   const bf16_t* usrc = (unit_q ? a.Q : a.dO) + head;
   const float* vsrc = (tid < kKvQ ? a.lse : a.delta) + bh * S;
-  auto prefetch = [&](u32x4 (&pre)[4], float& pv, int qbk) {
+  u32x4 pre[4];
+  float pre_v = 0.f;
+  auto slot_of = [&](int qbk) { return lds + (qbk % 3) * kSlot; };
+  auto prefetch = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
     if (unit_on) load_unit<D, kKvQ>(pre, usrc, qb0, S, unit);
-    if (tid < 2 * kKvQ) pv = vsrc[min(qb0 + (tid & (kKvQ - 1)), S - 1)];
+    if (tid < 2 * kKvQ) pre_v = vsrc[min(qb0 + (tid & (kKvQ - 1)), S - 1)];
   };
-  auto stage = [&](const u32x4 (&pre)[4], float pv, int qbk, int slot) {
+  auto stage = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
-    char* sl = lds + 2 * kKV + slot * kSlot;
+    char* sl = slot_of(qbk);
     if (unit_on)
       store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S, unit);
     if (tid < 2 * kKvQ) {
       float* lv4 = (float*)(sl + 4 * kQT);
       const bool in = qb0 + (tid & (kKvQ - 1)) < S;
-      lv4[tid] = tid < kKvQ ? (in ? pv * kLog2e : INFINITY) : (in ? pv : 0.f);
+      lv4[tid] = tid < kKvQ ? (in ? pre_v * kLog2e : INFINITY) : (in ? pre_v : 0.f);
     }
   };
-  auto compute = [&](int qbk, int slot) {
+
+  // P and dS of the previous block (B operands of its deferred accumulation)
+  u32x4 pp[2], ps[2];
+  bool pending = false;  // C of the previous block still to run
+  // C(qbk): dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot qbk
+  auto accumulate = [&](int qbk) {
+    const char* sl = slot_of(qbk);
+    const char* lqt = sl + 2 * kQT;   // Q^T
+    const char* ldot = sl + 3 * kQT;  // dO^T
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
+        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
+        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
+      }
+  };
+
+  // block qbk: A(qbk), then its softmax with C(qbk - 1) issued alongside
+  auto compute = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
-    if (a.causal && qb0 + kKvQ - 1 < k0w) return;  // every query before the wave's keys
-    const char* sl = lds + 2 * kKV + slot * kSlot;
+    const char* sl = slot_of(qbk);
     const char* lq = sl;                               // Q rows
     const char* ldo = sl + kQT;                        // dO rows
-    const char* lqt = sl + 2 * kQT;                    // Q^T
-    const char* ldot = sl + 3 * kQT;                   // dO^T
     const float* llse = (const float*)(sl + 4 * kQT);  // lse log2(e) (+inf past S)
     const float* ldel = llse + kKvQ;                   // D
     // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4.
-    // The block runs in three phases, fenced so that the compiler keeps every
-    // LDS fragment in its own registers: left alone it funnels each read
+    // Each phase's LDS fragments are read together into their own registers
+    // (sched_barrier fences): left alone, the compiler funnels each read
     // through one register quad and waits on it right before its MFMA.
     u32x4 fq[KS], fdo[KS];
 #pragma unroll
@@ -762,29 +791,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
       Mma<bf16_t>::run(dp, fdo[s], vf[s]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // lse / D of the block's queries and the dO^T / Q^T fragments of the
-    // second products: none depends on the softmax, so their latency hides
-    // under it
     f32x4 l4[4], d4[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       l4[r4] = *(const f32x4*)(llse + 8 * r4 + 4 * h);
       d4[r4] = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
     }
-    u32x4 fo[MD][2], fqt[MD][2];
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
-        fo[m][g] = *(const u32x4*)(ldot + off);
-        fqt[m][g] = *(const u32x4*)(lqt + off);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // the causal mask only on the diagonal block of the wave (a wave-uniform
-    // branch: the other blocks skip its compare and select per score)
-    u32x4 pp[2], ps[2];
-    auto softmax = [&](const bool masked) {
+    // softmax of this block; the causal mask only on the wave's diagonal
+    // block (a wave-uniform branch), and the previous block's accumulation
+    // in the same region, so that its MFMAs interleave with the VALU work
+    auto softmax = [&](const bool masked, const bool prev) {
+      if (prev) accumulate(qbk - 1);
+      u32x4 np[2], ns[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         float p[4], ds[4];
@@ -798,52 +816,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
         }
         // values i = 8 g .. 8 g + 7 form operand g: r4 = 2 g, 2 g + 1
         const int g = r4 >> 1, w0 = (r4 & 1) * 2;
-        pp[g][w0] = cvt_pk_bf16(p[0], p[1]);
-        pp[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
-        ps[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
-        ps[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
+        np[g][w0] = cvt_pk_bf16(p[0], p[1]);
+        np[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
+        ns[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
+        ns[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
       }
-    };
-    if (a.causal && qb0 < k0w + 32)
-      softmax(true);
-    else
-      softmax(false);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        Mma<bf16_t>::run(dv[m], fo[m][g], pp[g]);
-        Mma<bf16_t>::run(dk[m], fqt[m][g], ps[g]);
+        pp[g] = np[g];
+        ps[g] = ns[g];
       }
+    };
+    const bool diag = a.causal && qb0 < k0w + 32;
+    if (pending) {
+      if (diag) softmax(true, true);
+      else softmax(false, true);
+    } else {
+      if (diag) softmax(true, false);
+      else softmax(false, false);
+    }
+    pending = true;
   };
 
-  // Pipeline: block k computes from slot k % 2 while block k + 1, loaded
-  // into registers two blocks earlier, is written to the other slot and
-  // block k + 2 is requested; one barrier per block.  Register set A holds
-  // even blocks (relative to qstart), set B odd ones.
-  u32x4 preA[4], preB[4];
-  float pvA = 0.f, pvB = 0.f;
-  prefetch(preA, pvA, qstart);
-  if (qstart + 1 < nq) prefetch(preB, pvB, qstart + 1);
-  stage(preA, pvA, qstart, 0);
-  if (qstart + 2 < nq) prefetch(preA, pvA, qstart + 2);
-  __syncthreads();
-  for (int qbk = qstart; qbk < nq; qbk += 2) {
-    compute(qbk, 0);
-    if (qbk + 1 < nq) {
-      stage(preB, pvB, qbk + 1, 1);
-      if (qbk + 3 < nq) prefetch(preB, pvB, qbk + 3);
-    }
-    __syncthreads();
-    if (qbk + 1 >= nq) break;
-    compute(qbk + 1, 1);
-    if (qbk + 2 < nq) {
-      stage(preA, pvA, qbk + 2, 0);
-      if (qbk + 4 < nq) prefetch(preA, pvA, qbk + 4);
-    }
-    __syncthreads();
+  // Prologue: blocks qstart and qstart + 1 staged, qstart + 2 in registers.
+  prefetch(qstart);
+  stage(qstart);
+  if (qstart + 1 < nq) {
+    prefetch(qstart + 1);
+    stage(qstart + 1);
   }
+  if (qstart + 2 < nq) prefetch(qstart + 2);
+  __syncthreads();
+  for (int qbk = qstart; qbk < nq; ++qbk) {
+    // every query before the wave's keys: nothing to do (only blocks before
+    // the wave's first active one are skipped, so nothing is pending then)
+    if (!(a.causal && qbk * kKvQ + kKvQ - 1 < k0w)) compute(qbk);
+    __syncthreads();  // slot (qbk + 2) % 3 = slot of qbk - 1: its C has run
+    if (qbk + 2 < nq) {
+      stage(qbk + 2);
+      if (qbk + 3 < nq) prefetch(qbk + 3);
+    }
+  }
+  if (pending) accumulate(nq - 1);
+
   if (kk >= S) return;
   float* dKk = a.dK + head + (int64_t)kk * D;
   float* dVk = a.dV + head + (int64_t)kk * D;
