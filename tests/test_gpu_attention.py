@@ -157,6 +157,8 @@ BWD_CASES = [
     (1, 1, 1, 128, True, 623),
     (1, 2, 130, 128, False, 624),
     (1, 3, 512, 128, True, 625),     # several key groups of 128, diagonal skips
+    (1, 2, 40, 64, False, 628),      # two query blocks: the pipeline's shortest loop
+    (2, 1, 96, 128, True, 629),      # three query blocks (every LDS slot used once)
 ]
 
 
