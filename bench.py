@@ -497,6 +497,21 @@ def main():
         gemm = {"shape": [n_valid, wl.V, wl.d], "ms": round(gms, 3),
                 "tflops": round(2.0 * n_valid * wl.V * wl.d / (gms * 1e-3) / 1e12, 1)}
         del C
+        # the vendor library's bare GEMM at the same shape (torch's Linear path,
+        # bf16 in and out, fp32 accumulation): context for the fused kernels'
+        # rate, outside the timed steps
+        F = torch.nn.functional
+        for _ in range(2):
+            Cv = F.linear(A, Wt)
+        e0.record()
+        for _ in range(reps):
+            Cv = F.linear(A, Wt)
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / reps
+        gemm["vendor_linear_ms"] = round(vms, 3)
+        gemm["vendor_linear_tflops"] = round(2.0 * n_valid * wl.V * wl.d / (vms * 1e-3) / 1e12, 1)
+        del Cv
 
     cpu = None
     if args.cpu_seconds > 0:
