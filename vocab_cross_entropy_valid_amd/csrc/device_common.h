@@ -382,10 +382,20 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two fp32 values -> packed bf16, round to nearest even: one vector
+// conversion, which the backend emits as a single v_cvt_pk_bf16_f32 (the
+// same rounding as bf16_bits for finite values, at one instruction per pair
+// instead of four per value).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 template <typename T> struct Store2;
 template <> struct Store2<bf16_t> {
   __device__ __forceinline__ static void run(void* p, float a, float b) {
-    *(uint32_t*)p = bf16_bits(a) | (bf16_bits(b) << 16);
+    *(uint32_t*)p = pack_bf16x2(a, b);
   }
 };
 template <> struct Store2<float> {
@@ -399,8 +409,8 @@ template <typename T> struct Store4;
 template <> struct Store4<bf16_t> {
   __device__ __forceinline__ static void run(void* p, float a, float b, float c, float d) {
     u32x2 v;
-    v[0] = bf16_bits(a) | (bf16_bits(b) << 16);
-    v[1] = bf16_bits(c) | (bf16_bits(d) << 16);
+    v[0] = pack_bf16x2(a, b);
+    v[1] = pack_bf16x2(c, d);
     *(u32x2*)p = v;
   }
 };

@@ -159,10 +159,23 @@ __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* ld
   const int vl0 = tm * kTile + wa * kHalf;  // first local vocab entry of this wave
   // entry (mt, i) sits at c + 4 h past vl0, c = 32 mt + 8 (i / 4) + i % 4 a
   // compile-time constant; bounds are shifted instead of the positions
-  const int nv_h = (int)nv - vl0 - 4 * h;             // c < nv_h: inside V
   int y_h[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) y_h[nt] = (int)(y[nt] - a.v0) - vl0 - 4 * h;  // label at c
+  // G = (exp(z - lse) - [c == label]) w, one code path for every tile:
+  //   G = sgn(w) exp2(z log2(e) + cw) - [c == label] w,  cw = log2|w| - lse log2(e),
+  // i.e. one fma and one exp per entry, then a compare, a select and an fma.
+  // A token past the count has w = 0, so cw = -inf and its entries are
+  // exactly 0 (for finite z, without a product that could make NaN).
+  // Entries past V only need to be finite: dH multiplies them by the zeroed
+  // W^T columns past V, and dW never stores those rows.
+  float cw[kNT], wneg[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    cw[nt] = fast_log2(fabsf(w_t[nt])) - lse_t[nt] * kLog2e;
+    wneg[nt] = -w_t[nt];
+  }
+  const float sgn = w < 0.f ? -1.f : 1.f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -170,10 +183,8 @@ __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* ld
       const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        const float p = fast_exp2((acc[mt][nt][i] - lse_t[nt]) * kLog2e);
-        const float gv = (p - (c == y_h[nt] ? 1.f : 0.f)) * w_t[nt];
-        // selects (not products) so that a clamped row can never turn into NaN
-        acc[mt][nt][i] = (c < nv_h && w_t[nt] != 0.f) ? gv : 0.f;
+        const float e = fast_exp2(fmaf(acc[mt][nt][i], kLog2e, cw[nt]));
+        acc[mt][nt][i] = fmaf(e, sgn, c == y_h[nt] ? wneg[nt] : 0.f);
       }
     }
 

@@ -1,6 +1,8 @@
 // Forward kernels: valid-token compaction, fused projection + online
 // logsumexp over vocabulary tiles, merge of vocabulary chunks, and the
 // deterministic loss reduction.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -158,39 +160,51 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       // compile-time constant c = 32 mt + 8 (i / 4) + i % 4.  Comparing c with
       // per-lane bounds keeps the 64 positions out of registers.
       const int vlim_h = (int)min<int64_t>(a.V - vw0, (int64_t)kHalf) - 4 * h;  // c < vlim_h: < V
+      int rel_h[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) rel_h[nt] = y[nt] - vw0 - 4 * h;  // label at c == rel_h
       // per token: online (max, sum) update over each 32-entry slice (mt), so
-      // that only 16 accumulator values are live in VGPRs at a time
+      // that only 16 accumulator values are live in VGPRs at a time.  The
+      // bounds mask (entries at or beyond V drop out as -inf) runs only on a
+      // wave whose entries reach past V (a wave-uniform branch).
+      auto slices = [&](auto kMask, auto kLabel) {
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int rel_h = y[nt] - vw0 - 4 * h;  // label at c == rel_h
+        for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          float z[16];
+          for (int mt = 0; mt < 4; ++mt) {
+            float z[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
-            // entries at or beyond V (last tile only) drop out as -inf
-            z[i] = c < vlim_h ? acc[mt][nt][i] : -INFINITY;
-            // target logit, taken from the same fp32 accumulator as the sum
-            if (c == rel_h) zy[nt] = z[i];
-          }
-          float tmax = z[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[i]);
-          if (tmax != -INFINITY) {  // else every entry of this slice is past V
-            tmax *= kLog2e;
-            if (tmax > m[nt]) {
-              s[nt] *= fast_exp2(m[nt] - tmax);
-              m[nt] = tmax;
+            for (int i = 0; i < 16; ++i) {
+              const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
+              z[i] = (!decltype(kMask)::value || c < vlim_h) ? acc[mt][nt][i] : -INFINITY;
+              // target logit, taken from the same fp32 accumulator as the sum
+              if (decltype(kLabel)::value && c == rel_h[nt]) zy[nt] = z[i];
             }
-            const float mn = m[nt];
-            float sum = 0.f;
+            float tmax = z[0];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(z[i], kLog2e, -mn));
-            s[nt] += sum;
+            for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[i]);
+            if (!decltype(kMask)::value || tmax != -INFINITY) {  // else the slice is past V
+              tmax *= kLog2e;
+              if (tmax > m[nt]) {
+                s[nt] *= fast_exp2(m[nt] - tmax);
+                m[nt] = tmax;
+              }
+              const float mn = m[nt];
+              float sum = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(z[i], kLog2e, -mn));
+              s[nt] += sum;
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      typedef std::integral_constant<bool, true> kOn;
+      typedef std::integral_constant<bool, false> kOff;
+      if (vw0 + kHalf > a.V) {
+        slices(kOn(), kOn());
+      } else {
+        slices(kOff(), kOn());
       }
     }
 
