@@ -106,6 +106,19 @@ def test_reduction_sum_and_grad_scale():
     _check(out, H, W, y, "bf16", reduction="sum", grad=2.5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_negative_and_zero_upstream_grad(dtype):
+    """G = (softmax - onehot) w with w < 0 (the gradient of a maximised loss)
+    and with w = 0: the recompute folds |w| into the exponent and the sign
+    into a final fma, so both need their own check.  w = 0 gives exact zeros."""
+    announce(f"upstream grad -0.75 and 0 ({dtype})")
+    H, W, y = workloads.custom(333, 192, 1300, dtype=dtype, seed=23, ignore_frac=0.1)
+    out = run_path(H, W, y, dtype, grad=-0.75)
+    _check(out, H, W, y, dtype, grad=-0.75)
+    out = run_path(H, W, y, dtype, grad=0.0)
+    assert np.all(out["dH"] == 0) and np.all(out["dW"] == 0)
+
+
 def test_large_logits_stay_finite():
     announce("large logits")
     H, W, y = workloads.custom(300, 128, 1000, seed=22, w_std=0.5, h_std=2.0)
