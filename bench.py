@@ -30,7 +30,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 # FLOPs per step of each kernel class, as a multiple of N_valid * d * V
-CLASS_FLOPS = {"fwd": 2, "bwd_g": 2, "dh": 2, "dw": 2}
+CLASS_FLOPS = {"fwd": 2, "bwd_g": 2, "dh": 2, "dw": 2, "dh_dw": 4}
 
 
 _CSRC = "vocab_cross_entropy_valid_amd/csrc/"
@@ -43,7 +43,7 @@ KERNEL_FILE = {"compact": "kernels_fwd.hip", "fwd": "kernels_fwd.hip", "merge": 
                "transpose": "kernels_bwd.hip", "bwd_g": "kernels_bwd.hip", "dh": "kernels_bwd.hip",
                "dw": "kernels_bwd.hip", "gemm": "kernels_bwd.hip", "embed": "kernels_embed.hip",
                "attn": "kernels_attn.hip", "attn_dq": "kernels_attn.hip",
-               "attn_dkv": "kernels_attn.hip"}
+               "attn_dkv": "kernels_attn.hip", "dh_dw": "kernels_bwd.hip"}
 
 
 def _log(msg):

@@ -322,7 +322,8 @@ typedef enum {
   LCE_K_ATTN = 11,     /* online-softmax attention forward               */
   LCE_K_ATTN_DQ = 12,  /* attention backward, dQ pass (and rowsum(dO O)) */
   LCE_K_ATTN_DKV = 13, /* attention backward, dK / dV pass               */
-  LCE_K_COUNT = 14
+  LCE_K_DH_DW = 14,    /* dH and dW of one vocabulary block, one launch   */
+  LCE_K_COUNT = 15
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -30,7 +30,8 @@ LCE_MEAN = 0
 LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
-                  "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv")
+                  "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv",
+                  "dh_dw")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""

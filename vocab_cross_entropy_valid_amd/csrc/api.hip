@@ -459,12 +459,20 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       }
       // dH first: right after the recompute the G block is still largely in
       // the Infinity Cache (measured faster; dW's time does not depend on
-      // the order)
-      e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
-      if (e != hipSuccess) return hip_fail(e, "dH launch");
-      e = run(LCE_K_DW, s,
-              [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
-      if (e != hipSuccess) return hip_fail(e, "dW launch");
+      // the order).  When even the chunk's largest dH tile grid (C / 256
+      // token tiles x d / 256 hidden tiles) cannot give every CU a tile, dH
+      // and dW share one launch, so that the short dW tiles run on the CUs
+      // the long dH tiles leave idle.
+      if ((p.C / 256) * ((d + 255) / 256) < grid_persistent()) {
+        e = run(LCE_K_DH_DW, s, [&] { return lce::launch_dh_dw(ha, wa, dtype, s); });
+        if (e != hipSuccess) return hip_fail(e, "dH + dW launch");
+      } else {
+        e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
+        if (e != hipSuccess) return hip_fail(e, "dH launch");
+        e = run(LCE_K_DW, s,
+                [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
+        if (e != hipSuccess) return hip_fail(e, "dW launch");
+      }
     }
   }
   return LCE_OK;

@@ -110,6 +110,10 @@ hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
 // grid: persistent workgroups (a multiple of 8; each walks slots grid apart)
 hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s);
+// dH and dW of one vocabulary block in a single launch: the dH tiles first
+// (long K), then one workgroup per dW tile, dispatched onto the CUs the dH
+// tiles leave free.  For chunks whose dH tile grid cannot fill the GPU.
+hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s);
 // Workspace layout of the embedding backward (byte offsets, 256-aligned).
 struct EmbedPlan {
   int end_bit;  // sort key bits: 2^end_bit > V (V itself is the padding sentinel)

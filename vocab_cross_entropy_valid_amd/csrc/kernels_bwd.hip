@@ -275,8 +275,10 @@ hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s) {
 // (B = W^T rows); K runs over the vocabulary block.  Rows are scattered to the
 // tokens' original positions through valid_idx.  beta = 0 on the first
 // vocabulary block, 1 afterwards.
+// (ga, gb): the block of tiles the 32 slots of one XCD take (ga * gb = 32)
 template <typename T>
-__device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds) {
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, int ga = 4,
+                                        int gb = 8) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -291,7 +293,7 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds) {
   const int TM = (int)((n_act + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
   int tm, tn;
-  if (!xcd_tile(slot, TM, TN, 4, 8, tm, tn)) return;
+  if (!xcd_tile(slot, TM, TN, ga, gb, tm, tn)) return;
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int nstages = (int)((nv + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
 
@@ -493,6 +495,21 @@ __global__ __launch_bounds__(kThreads, 1) void dw_step_kernel(DwArgs a) {
   }
 }
 
+// dH tiles in slots [0, n_dh), dW tiles after them (n_dh is a multiple of
+// 256, so every slot keeps its XCD: slot % 8).  The dH tiles take 2 x 16
+// blocks per XCD instead of 4 x 8, so that a grid of few token tiles still
+// spreads over all 8 XCDs and leaves free CUs on each for the dW tiles
+// (slots go to the XCDs round-robin, dW's included).
+template <typename T, int kOpt>
+__global__ __launch_bounds__(kThreads, 1) void dh_dw_kernel(DhArgs ha, DwArgs wa, int n_dh) {
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  const int b = (int)blockIdx.x;
+  if (b < n_dh)
+    dh_tile<T>(ha, b, lds, 2, 16);
+  else
+    dw_tile<T, kOpt>(wa, b - n_dh, lds);
+}
+
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
   const int TM = (int)(a.C / kTile), TN = (int)((a.d + kTile - 1) / kTile);
   const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
@@ -521,6 +538,30 @@ hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s) {
     hipLaunchKernelGGL(dw_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(dw_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s) {
+  const int TMh = (int)(ha.C / kTile), TNh = (int)((ha.d + kTile - 1) / kTile);
+  const int n_dh = 256 * ((((TMh + 1) / 2) * ((TNh + 15) / 16) + 7) / 8);
+  const int TMw = (int)(wa.Vs / kTile), TNw = (int)((wa.d + kTile - 1) / kTile);
+  wa.nslots = 256 * ((((TMw + 3) / 4) * ((TNw + 7) / 8) + 7) / 8);
+  const dim3 grid((unsigned)(n_dh + wa.nslots));
+  if (dtype == 1) {
+    if (wa.opt_kind == 1)
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 1>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+    else if (wa.opt_kind == 2)
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 2>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+    else
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 0>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+  } else {
+    if (wa.opt_kind == 1)
+      hipLaunchKernelGGL((dh_dw_kernel<float, 1>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+    else if (wa.opt_kind == 2)
+      hipLaunchKernelGGL((dh_dw_kernel<float, 2>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+    else
+      hipLaunchKernelGGL((dh_dw_kernel<float, 0>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
   }
   return hipGetLastError();
 }
