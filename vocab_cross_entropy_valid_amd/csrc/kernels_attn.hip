@@ -356,10 +356,11 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 //    block's queries from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T
 //    with dO^T and Q^T in the paired-chunk layout.
 //
-// Tiles are staged through registers into LDS, single buffered.  The dK / dV
-// pass loads the next query block into registers while the current one
-// computes; each thread's load unit (4 rows x 8 dims) feeds both the
-// row-major and the transposed copy.
+// Both passes run one wave per SIMD and stage their streamed tiles through
+// registers: the next block is loaded while the current one computes, and
+// each thread's load unit (4 rows x 8 dims) feeds both the row-major and the
+// transposed LDS copy.  The dQ pass keeps two LDS slots, the dK / dV pass
+// three (its accumulation runs one block late); one barrier per block.
 
 namespace {
 
@@ -393,36 +394,6 @@ __device__ __forceinline__ void stage_rows(char* dst, const bf16_t* src, int row
   }
 }
 
-// the same rows transposed: row = dimension, entries = the R rows, in the
-// paired-chunk layout of tt_unit_offset<R>
-template <int D, int R, int NT>
-__device__ __forceinline__ void stage_rows_t(char* dst, const bf16_t* src, int row0, int S, int tid) {
-  constexpr int kUnits = (D / 8) * (R / 4);
-  const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int it = 0; it < (kUnits + NT - 1) / NT; ++it) {
-    const int unit = it * NT + tid;
-    if (unit >= kUnits) break;
-    const int kg = unit % (R / 4);  // entries 4 kg .. 4 kg + 3
-    const int dg = unit / (R / 4);  // dims 8 dg .. 8 dg + 7
-    u32x4 v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = row0 + 4 * kg + q;
-      v[q] = r < S ? *(const u32x4*)(src + (int64_t)r * D + 8 * dg) : z;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 u;
-      u[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
-      u[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
-      *(u32x2*)(dst + tt_unit_offset<R>(8 * dg + e, kg)) = u;
-    }
-  }
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -441,9 +412,10 @@ __device__ __forceinline__ void load_unit(u32x4 (&v)[4], const bf16_t* src, int 
   }
 }
 
-// The unit into the row-major swizzled tile rm and, transposed, into the
-// paired-chunk tile tt (the layouts of stage_rows and stage_rows_t); with
-// kT false the row-major copy only.
+// The unit into the row-major swizzled tile rm (the layout of stage_rows)
+// and, transposed (row = dimension, entries = the tile's R rows), into the
+// paired-chunk tile tt of tt_unit_offset<R>; with kT false the row-major
+// copy only.
 template <int D, int R, bool kT = true>
 __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char* tt, int row0,
                                            int S, int unit) {
