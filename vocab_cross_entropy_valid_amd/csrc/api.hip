@@ -373,6 +373,9 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     th.active_c0 = c0;
     e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(th, dtype, s); });
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    // bf16 without an optimizer step: dH reads the W block directly (K-major,
+    // transposing LDS reads), so the W^T copy is not built
+    const bool w_direct = dtype == LCE_BF16 && step == nullptr;
     for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
       lce::TransposeArgs tw{};
       tw.src = W;
@@ -387,8 +390,10 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       tw.K = d;
       tw.active_count = c0 > 0 ? valid_count : nullptr;
       tw.active_c0 = c0;
-      e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
-      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      if (!w_direct) {
+        e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
+        if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      }
 
       lce::BwdGArgs ga{};
       ga.H = H;
@@ -417,6 +422,7 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       lce::DhArgs ha{};
       ha.G = G;
       ha.WT = WT;
+      ha.W = w_direct ? W : nullptr;
       ha.ldG = p.ldG;
       ha.ldWT = p.ldWT;
       ha.C = p.C;

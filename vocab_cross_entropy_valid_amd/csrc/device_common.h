@@ -137,6 +137,7 @@ constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer, gfx9 family
 struct RowPtrs {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t off[4];
+  uint32_t stride;  // bytes the source advances per stage
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
@@ -172,6 +173,33 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
     const int64_t rel = s.gather ? (int64_t)s.gather[r] : r - s.row0;
     rp.off[i] = (uint32_t)(rel * s.ld) + chunk * 16;
   }
+  rp.stride = kRowBytes;
+  return rp;
+}
+
+// K-major B operand: the source is row-major [K][n] (each K row holds the
+// tile's 256 operand rows contiguously, e.g. W [vocabulary][hidden] when K
+// runs over the vocabulary), so a stage is 64 K rows x 256 operand rows of
+// bf16, 512 bytes per K row.  LDS row v (0..63) holds K row k0 + 64 s + v;
+// its sixteen-byte chunk c sits at position c ^ (4 (v % 4)), so that the
+// transposing fragment reads below (8 K rows x 64 bytes per instruction)
+// hit each bank group exactly twice.  Load i of wave w fills LDS rows
+// 2 (8 i + w) and 2 (8 i + w) + 1, lane L the chunk at position L % 32 of
+// row 2 (8 i + w) + L / 32.  The resource covers K rows [k0, k0 + krows):
+// rows past it read as zeros.
+__device__ __forceinline__ RowPtrs make_kmajor_ptrs(const char* base, int64_t ld, int64_t k0,
+                                                    int64_t krows, int64_t n0, int tid) {
+  RowPtrs rp;
+  const int w = tid >> 6;
+  const int L = tid & 63;
+  rp.rsrc = make_rsrc(base + k0 * ld, (krows > 0 ? krows : 0) * ld);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = 2 * (8 * i + w) + (L >> 5);
+    const int c = (L & 31) ^ (4 * (v & 3));
+    rp.off[i] = (uint32_t)(v * ld + (n0 + 8 * c) * 2);
+  }
+  rp.stride = (uint32_t)(64 * ld);
   return rp;
 }
 
@@ -205,6 +233,50 @@ __device__ __forceinline__ void load_frags_ab(u32x4 (&fa)[4], u32x4 (&fb)[kNT], 
   fa[3] = *(const u32x4*)(ca + oa + 12288);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// One B fragment (32 operand rows x 16 K) from a K-major stage with the
+// gfx950 transposing LDS read ds_read_b64_tr_b16: within each group of 16
+// lanes, lane i receives, as element e of its result, element i % 4 of the
+// 8 bytes lane 4 e + i / 4 addressed.  Lane l addresses K row kb + 8 (l / 32)
+// + (l % 16) / 4 (+ 4 for the second read) at operand row nb + 16 ((l / 16)
+// % 2) + 4 (l % 4), so that it receives operand row nb + l % 32 at K rows
+// kb + 8 (l / 32) + 0..7: the layout of a row-major fragment.  bt_base is
+// that lane's byte address of K row kb = 0 (swizzle included).
+__device__ __forceinline__ u32x4 load_frag_bt(const char* cb, int bt_base, int s) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const char* p = cb + bt_base + s * (16 * 512);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)LCE_LDS_PTR(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)LCE_LDS_PTR(p + 4 * 512));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo);
+  const u32x2 b = __builtin_bit_cast(u32x2, hi);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// Byte address of lane l's first transposed read for 32-row block nt of the
+// wave's 64 operand rows (see load_frag_bt).
+__device__ __forceinline__ int bt_lane_base(int wb, int nt, int lane) {
+  const int v = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int n = wb * kWaveN + 32 * nt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int pos = (n >> 3) ^ (4 * (v & 3));
+  return v * 512 + pos * 16 + (n & 7) * 2;
+}
+
+// Fragment reads of MFMA step s with a K-major B (two transposing reads per
+// B fragment, eight reads per step), in the order the MFMAs consume them.
+__device__ __forceinline__ void load_frags_abt(u32x4 (&fa)[4], u32x4 (&fb)[kNT], const char* ca,
+                                               const char* cb, int a_base, int bt0, int bt1,
+                                               int s) {
+  const int ea = a_base ^ (32 * s), oa = a_base ^ ((32 * s) ^ 64);
+  fa[0] = *(const u32x4*)(ca + ea);
+  fb[0] = load_frag_bt(cb, bt0, s);
+  fb[1] = load_frag_bt(cb, bt1, s);
+  fa[1] = *(const u32x4*)(ca + oa + 4096);
+  fa[2] = *(const u32x4*)(ca + ea + 8192);
+  fa[3] = *(const u32x4*)(ca + oa + 12288);
+}
+
 typedef f32x16 Acc[4][kNT];
 
 template <typename T>
@@ -231,9 +303,9 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 // 0 go first; the previous stage's step-3 MFMAs (kPrev) cover their latency
 // and carry the nl direct-to-LDS loads of this stage; then each step's 8
 // MFMAs alternate with the 6 fragment reads of the following step.
-template <bool kPrev, int nl>
+template <bool kPrev, int nl, int kReads = 6>
 __device__ __forceinline__ void schedule_body() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
   if (kPrev) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -246,11 +318,11 @@ __device__ __forceinline__ void schedule_body() {
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
+    for (int q = 0; q < kReads; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (kReads < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - kReads, 0);
   }
 }
 
@@ -276,24 +348,109 @@ __device__ __forceinline__ void stage_barrier() {
 // reads.  Reads A buffer sa and B buffer k & 1.  Loads B(k + 1) (kLB) into
 // the B buffer read by stage k - 1, then A(k + 2) (kLA) into A buffer sa2,
 // also last read by stage k - 1: both were free at the previous barrier.
+// kBT: B is K-major (make_kmajor_ptrs) and its fragments come from the
+// transposing reads; b_base then holds the lane's base for block nt = 0 and
+// b_base1 the one for nt = 1.
+template <bool kBT>
+__device__ __forceinline__ void load_frags(u32x4 (&fa)[4], u32x4 (&fb)[kNT], const char* ca,
+                                           const char* cb, int a_base, int b_base, int b_base1,
+                                           int s) {
+  if constexpr (kBT)
+    load_frags_abt(fa, fb, ca, cb, a_base, b_base, b_base1, s);
+  else
+    load_frags_ab(fa, fb, ca, cb, a_base, b_base, s);
+}
+
+// Stage body with a K-major B (kBT).  The compiler puts a full vmcnt(0) in
+// front of any transposing LDS read that follows a direct-to-LDS load still
+// in flight (it does not for ordinary LDS reads), so all 16 transposing reads
+// of the stage (4 steps x 2 blocks x 2 halves) are issued before the stage's
+// loads; the wait then falls on the next stage's first read, by which time
+// only A(k + 2), issued a stage earlier, can still be outstanding.
 template <typename T, bool kPrev, bool kLB, bool kLA>
-__device__ __forceinline__ void stage_body(Acc& acc, char* lds, int k, int sa, int sa2, int a_base,
-                                           int b_base, const RowPtrs& pa, const RowPtrs& pb,
-                                           int wave_u, u32x4 (&f3a)[4], u32x4 (&f3b)[kNT]) {
+__device__ __forceinline__ void stage_body_bt(Acc& acc, char* lds, int k, int sa, int sa2,
+                                              int a_base, int b_base, int b_base1,
+                                              const RowPtrs& pa, const RowPtrs& pb, int wave_u,
+                                              u32x4 (&f3a)[4], u32x4 (&f3b)[kNT]) {
   const char* ca = lds + kLdsA + sa * kOpBytes;
   const char* cb = lds + kLdsB + (k & 1) * kOpBytes;
   u32x4 fa[3][4], fb[3][kNT];
-  load_frags_ab(fa[0], fb[0], ca, cb, a_base, b_base, 0);
-  if (kLB) load_op(lds + kLdsB + ((k + 1) & 1) * kOpBytes, pb, (uint32_t)((k + 1) * kRowBytes), wave_u);
+  auto a_frags = [&](u32x4 (&f)[4], int s) {
+    const int ea = a_base ^ (32 * s), oa = a_base ^ ((32 * s) ^ 64);
+    f[0] = *(const u32x4*)(ca + ea);
+    f[1] = *(const u32x4*)(ca + oa + 4096);
+    f[2] = *(const u32x4*)(ca + ea + 8192);
+    f[3] = *(const u32x4*)(ca + oa + 12288);
+  };
+  a_frags(fa[0], 0);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    fb[s][0] = load_frag_bt(cb, b_base, s);
+    fb[s][1] = load_frag_bt(cb, b_base1, s);
+  }
+  u32x4 nb0 = load_frag_bt(cb, b_base, 3), nb1 = load_frag_bt(cb, b_base1, 3);
+  if (kLB) load_op(lds + kLdsB + ((k + 1) & 1) * kOpBytes, pb, (uint32_t)(k + 1) * pb.stride, wave_u);
   if (kLA) load_op(lds + kLdsA + sa2 * kOpBytes, pa, (uint32_t)((k + 2) * kRowBytes), wave_u);
   if (kPrev) mma_step<T>(acc, f3a, f3b);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
-    if (s < 2) load_frags_ab(fa[s + 1], fb[s + 1], ca, cb, a_base, b_base, s + 1);
-    else load_frags_ab(f3a, f3b, ca, cb, a_base, b_base, 3);
+    if (s < 2) a_frags(fa[s + 1], s + 1);
+    else a_frags(f3a, 3);
     mma_step<T>(acc, fa[s], fb[s]);
   }
-  if constexpr (sizeof(T) == 2) schedule_body<kPrev, (kLB ? 4 : 0) + (kLA ? 4 : 0)>();
+  f3b[0] = nb0;
+  f3b[1] = nb1;
+  // reads: the 4 A fragments of step 0 and the 16 transposing reads first;
+  // then the previous stage's step-3 MFMAs carry the loads; then each step's
+  // 8 MFMAs alternate with the following step's 4 A reads
+  __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);
+  if (kPrev) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < (kLB ? 4 : 0) + (kLA ? 4 : 0)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  } else if (kLB || kLA) {
+    __builtin_amdgcn_sched_group_barrier(0x020, (kLB ? 4 : 0) + (kLA ? 4 : 0), 0);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  if (kLB) stage_barrier<kLA ? 4 : 0>();
+}
+
+template <typename T, bool kPrev, bool kLB, bool kLA, bool kBT = false>
+__device__ __forceinline__ void stage_body(Acc& acc, char* lds, int k, int sa, int sa2, int a_base,
+                                           int b_base, int b_base1, const RowPtrs& pa,
+                                           const RowPtrs& pb, int wave_u, u32x4 (&f3a)[4],
+                                           u32x4 (&f3b)[kNT]) {
+  if constexpr (kBT) {
+    stage_body_bt<T, kPrev, kLB, kLA>(acc, lds, k, sa, sa2, a_base, b_base, b_base1, pa, pb,
+                                      wave_u, f3a, f3b);
+    return;
+  }
+  const char* ca = lds + kLdsA + sa * kOpBytes;
+  const char* cb = lds + kLdsB + (k & 1) * kOpBytes;
+  const uint32_t bstride = kBT ? pb.stride : (uint32_t)kRowBytes;
+  u32x4 fa[3][4], fb[3][kNT];
+  load_frags<kBT>(fa[0], fb[0], ca, cb, a_base, b_base, b_base1, 0);
+  if (kLB) load_op(lds + kLdsB + ((k + 1) & 1) * kOpBytes, pb, (uint32_t)(k + 1) * bstride, wave_u);
+  if (kLA) load_op(lds + kLdsA + sa2 * kOpBytes, pa, (uint32_t)((k + 2) * kRowBytes), wave_u);
+  if (kPrev) mma_step<T>(acc, f3a, f3b);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s < 2) load_frags<kBT>(fa[s + 1], fb[s + 1], ca, cb, a_base, b_base, b_base1, s + 1);
+    else load_frags<kBT>(f3a, f3b, ca, cb, a_base, b_base, b_base1, 3);
+    mma_step<T>(acc, fa[s], fb[s]);
+  }
+  if constexpr (sizeof(T) == 2)
+    schedule_body<kPrev, (kLB ? 4 : 0) + (kLA ? 4 : 0), kBT ? 8 : 6>();
   // B(k + 1) and A(k + 1) must have landed; A(k + 2), issued last, may not
   if (kLB) stage_barrier<kLA ? 4 : 0>();
 }
@@ -303,9 +460,12 @@ __device__ __forceinline__ int next3(int b) { return b == 2 ? 0 : b + 1; }
 // acc += A_tile(256 x K) * B_tile(256 x K)^T over nstages stages of 128 bytes.
 // Ends with a barrier, so the caller may reuse LDS afterwards.  Stage j of A
 // lives in A buffer j % 3, stage j of B in B buffer j % 2.
-template <typename T>
+// kBT: B is a K-major operand (make_kmajor_ptrs), read with the transposing
+// fragment reads (bf16 only).
+template <typename T, bool kBT = false>
 __device__ __forceinline__ void tile_mainloop(Acc& acc, char* lds, const RowPtrs& pa,
                                               const RowPtrs& pb, int nstages, int tid) {
+  static_assert(!kBT || sizeof(T) == 2, "the transposing B path is bf16 only");
   if (nstages <= 0) return;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -315,7 +475,8 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, char* lds, const RowPtrs
   const int r = lane & 31;
   const int x = ((lane >> 5) ^ (r & 7) ^ (r >> 3)) << 4;
   const int a_base = (wa * kHalf + r) * kRowBytes + x;
-  const int b_base = (wb * kWaveN + r) * kRowBytes + x;
+  const int b_base = kBT ? bt_lane_base(wb, 0, lane) : (wb * kWaveN + r) * kRowBytes + x;
+  const int b_base1 = kBT ? bt_lane_base(wb, 1, lane) : 0;
   // prologue: A(0), B(0), A(1); stage 0 needs the first two
   load_op(lds + kLdsA, pa, 0, wave_u);
   load_op(lds + kLdsB, pb, 0, wave_u);
@@ -327,22 +488,28 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, char* lds, const RowPtrs
   }
   u32x4 f3a[4], f3b[kNT];
   if (nstages == 1) {
-    stage_body<T, false, false, false>(acc, lds, 0, 0, 2, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+    stage_body<T, false, false, false, kBT>(acc, lds, 0, 0, 2, a_base, b_base, b_base1, pa, pb,
+                                            wave_u, f3a, f3b);
   } else if (nstages == 2) {
-    stage_body<T, false, true, false>(acc, lds, 0, 0, 2, a_base, b_base, pa, pb, wave_u, f3a, f3b);
-    stage_body<T, true, false, false>(acc, lds, 1, 1, 0, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+    stage_body<T, false, true, false, kBT>(acc, lds, 0, 0, 2, a_base, b_base, b_base1, pa, pb,
+                                           wave_u, f3a, f3b);
+    stage_body<T, true, false, false, kBT>(acc, lds, 1, 1, 0, a_base, b_base, b_base1, pa, pb,
+                                           wave_u, f3a, f3b);
   } else {
-    stage_body<T, false, true, true>(acc, lds, 0, 0, 2, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+    stage_body<T, false, true, true, kBT>(acc, lds, 0, 0, 2, a_base, b_base, b_base1, pa, pb,
+                                          wave_u, f3a, f3b);
     int sa = 1, sa2 = 0;  // k % 3 and (k + 2) % 3
     int k = 1;
     for (; k + 2 < nstages; ++k) {
-      stage_body<T, true, true, true>(acc, lds, k, sa, sa2, a_base, b_base, pa, pb, wave_u, f3a, f3b);
+      stage_body<T, true, true, true, kBT>(acc, lds, k, sa, sa2, a_base, b_base, b_base1, pa, pb,
+                                           wave_u, f3a, f3b);
       sa = next3(sa);
       sa2 = next3(sa2);
     }
-    stage_body<T, true, true, false>(acc, lds, k, sa, sa2, a_base, b_base, pa, pb, wave_u, f3a, f3b);
-    stage_body<T, true, false, false>(acc, lds, k + 1, next3(sa), sa2, a_base, b_base, pa, pb,
-                                      wave_u, f3a, f3b);
+    stage_body<T, true, true, false, kBT>(acc, lds, k, sa, sa2, a_base, b_base, b_base1, pa, pb,
+                                          wave_u, f3a, f3b);
+    stage_body<T, true, false, false, kBT>(acc, lds, k + 1, next3(sa), sa2, a_base, b_base,
+                                           b_base1, pa, pb, wave_u, f3a, f3b);
   }
   mma_step<T>(acc, f3a, f3b);
   __syncthreads();

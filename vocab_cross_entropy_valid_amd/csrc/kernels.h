@@ -44,7 +44,8 @@ struct BwdGArgs {
 
 struct DhArgs {
   const void* G;   // [C][ldG]
-  const void* WT;  // [d][ldWT]
+  const void* WT;  // [d][ldWT] (when W is null)
+  const void* W;   // [V][d] bf16 read directly (K-major B operand), or null
   int64_t C, Vs, d;
   int64_t ldG, ldWT;
   const int32_t* valid_idx;

@@ -271,12 +271,14 @@ hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s) {
 
 // ----------------------------------------------------------- dH += G W
 //
-// C tile rows = tokens of the chunk (A = G rows), columns = hidden units
-// (B = W^T rows); K runs over the vocabulary block.  Rows are scattered to the
-// tokens' original positions through valid_idx.  beta = 0 on the first
-// vocabulary block, 1 afterwards.
+// C tile rows = tokens of the chunk (A = G rows), columns = hidden units;
+// K runs over the vocabulary block.  B is either W itself, read K-major with
+// the transposing LDS reads (kBT: bf16, W not updated during the launch), or
+// the W^T rows of the transposed block.  Rows are scattered to the tokens'
+// original positions through valid_idx.  beta = 0 on the first vocabulary
+// block, 1 afterwards.
 // (ga, gb): the block of tiles the 32 slots of one XCD take (ga * gb = 32)
-template <typename T>
+template <typename T, bool kBT = false>
 __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, int ga = 4,
                                         int gb = 8) {
   const int tid = threadIdx.x;
@@ -300,12 +302,19 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
   // rows past the valid count clamp to the last valid row (cache hits)
   // instead of streaming the block's unused rows
   RowSource as{(const char*)a.G, a.ldG * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, n_act, 0};
-  RowSource bs{(const char*)a.WT, a.ldWT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
   const RowPtrs pa = make_row_ptrs<false>(as, tid);
-  const RowPtrs pb = make_row_ptrs<false>(bs, tid);
+  RowPtrs pb;
+  if constexpr (kBT) {
+    // W rows v0 .. v0 + nv of the block (rows past V read as zeros)
+    pb = make_kmajor_ptrs((const char*)a.W, a.d * Elem<T>::kSize, a.v0, nv, (int64_t)tn * kTile,
+                          tid);
+  } else {
+    RowSource bs{(const char*)a.WT, a.ldWT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
+    pb = make_row_ptrs<false>(bs, tid);
+  }
   Acc acc;
   zero_acc(acc);
-  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: LDS is free
+  tile_mainloop<T, kBT>(acc, lds, pa, pb, nstages, tid);  // ends with a barrier: LDS is free
 
   // destination rows of the tile's tokens, in the (now free) stage buffers
   int* rows = (int*)lds;
@@ -465,13 +474,13 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 
 // ------------------------------------------------------------ launches
 
-template <typename T>
+template <typename T, bool kBT>
 __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   // One LDS object only: with a second __shared__ array the compiler can no
   // longer tell the direct-to-LDS loads of the next stage from the fragment
   // reads of the current one and waits for every load right after issuing it.
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  dh_tile<T>(a, blockIdx.x, lds);
+  dh_tile<T, kBT>(a, blockIdx.x, lds);
 }
 
 template <typename T>
@@ -500,12 +509,12 @@ __global__ __launch_bounds__(kThreads, 1) void dw_step_kernel(DwArgs a) {
 // blocks per XCD instead of 4 x 8, so that a grid of few token tiles still
 // spreads over all 8 XCDs and leaves free CUs on each for the dW tiles
 // (slots go to the XCDs round-robin, dW's included).
-template <typename T, int kOpt>
+template <typename T, int kOpt, bool kBT>
 __global__ __launch_bounds__(kThreads, 1) void dh_dw_kernel(DhArgs ha, DwArgs wa, int n_dh) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   const int b = (int)blockIdx.x;
   if (b < n_dh)
-    dh_tile<T>(ha, b, lds, 2, 16);
+    dh_tile<T, kBT>(ha, b, lds, 2, 16);
   else
     dw_tile<T, kOpt>(wa, b - n_dh, lds);
 }
@@ -513,10 +522,12 @@ __global__ __launch_bounds__(kThreads, 1) void dh_dw_kernel(DhArgs ha, DwArgs wa
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
   const int TM = (int)(a.C / kTile), TN = (int)((a.d + kTile - 1) / kTile);
   const int grid = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
-  if (dtype == 1)
-    hipLaunchKernelGGL(dh_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, a);
+  if (dtype == 1 && a.W)
+    hipLaunchKernelGGL((dh_kernel<bf16_t, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((dh_kernel<bf16_t, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((dh_kernel<float, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -548,20 +559,24 @@ hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s) {
   const int TMw = (int)(wa.Vs / kTile), TNw = (int)((wa.d + kTile - 1) / kTile);
   wa.nslots = 256 * ((((TMw + 3) / 4) * ((TNw + 7) / 8) + 7) / 8);
   const dim3 grid((unsigned)(n_dh + wa.nslots));
+  // the optimizer epilogues rewrite W's rows while dH tiles run: they keep
+  // dH on the transposed copy (ha.W null)
   if (dtype == 1) {
     if (wa.opt_kind == 1)
-      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 1>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 1, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
     else if (wa.opt_kind == 2)
-      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 2>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 2, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+    else if (ha.W)
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 0, true>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
     else
-      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 0>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<bf16_t, 0, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
   } else {
     if (wa.opt_kind == 1)
-      hipLaunchKernelGGL((dh_dw_kernel<float, 1>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<float, 1, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
     else if (wa.opt_kind == 2)
-      hipLaunchKernelGGL((dh_dw_kernel<float, 2>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<float, 2, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
     else
-      hipLaunchKernelGGL((dh_dw_kernel<float, 0>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
+      hipLaunchKernelGGL((dh_dw_kernel<float, 0, false>), grid, dim3(kThreads), 0, s, ha, wa, n_dh);
   }
   return hipGetLastError();
 }
