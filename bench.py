@@ -466,8 +466,10 @@ def main():
         "reduce": 4 * n_valid + 16,
         # fp32 dH rows of ignored tokens zeroed, labels read
         "zero": 4 * (wl.N - n_valid) * wl.d + 8 * wl.N,
-        # H^T of the valid rows and W^T of every vocabulary block, read and written
-        "transpose": 2 * esz * wl.d * (n_valid + wl.V),
+        # H^T of the valid rows, read and written; W^T of every vocabulary
+        # block too where dH cannot read W directly (fp32, fused optimizer)
+        "transpose": 2 * esz * wl.d * (n_valid + (0 if wl.dtype == "bf16" and not args.fused_opt
+                                                  else wl.V)),
     }
     hbm_passes = {}
     for name, nbytes in pass_bytes.items():
