@@ -441,6 +441,51 @@ __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char
   }
 }
 
+// Row-major 32-row x 128-dim bf16 tile (16 sixteen-byte chunks per 256-byte
+// row) that is also read transposed: chunk c of row r sits at position
+// c ^ trs(r), trs(r) = (r % 16) ^ 4 (r % 4).  trs is a bijection on any 16
+// consecutive rows, so 16 lanes reading one chunk of consecutive rows hit
+// distinct banks; a transposing read of 8 consecutive rows x 4 chunks puts
+// two rows' chunks on each group of four banks, i.e. each bank twice (the
+// minimum for 512 bytes); the staging writes spread evenly as well.
+__device__ __forceinline__ int trs_offset(int row, int chunk) {
+  return row * 256 + ((chunk ^ ((row & 15) ^ ((row & 3) << 2))) << 4);
+}
+
+// A fragment of the transposed tile, straight from such a row-major tile
+// with two ds_read_b64_tr_b16: operand row = tile column dim0 + lane % 32, K =
+// tile rows r0 + 4 (lane / 32) + {0..3} and the same + 8, the paired order
+// in which the accumulator-derived B operands hold the queries.  Within a
+// group of 16 lanes, lane i receives as element e the element i % 4 of the
+// 8 bytes lane 4 e + i / 4 addressed, so lane l addresses row r0 + 4 (l / 32)
+// + (l % 16) / 4 at column dim0 + 16 ((l / 16) % 2) + 4 (l % 4).
+__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int dim0, int lane) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int dim = dim0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const char* p1 = tile + trs_offset(row, dim >> 3) + (dim & 7) * 2;
+  const char* p2 = tile + trs_offset(row + 8, dim >> 3) + (dim & 7) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p1));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p2));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo);
+  const u32x2 b = __builtin_bit_cast(u32x2, hi);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// A load unit (see load_unit) into such a tile, rows past S zeroed.
+__device__ __forceinline__ void store_unit_trs(const u32x4 (&vin)[4], char* tile, int row0, int S,
+                                               int unit) {
+  constexpr int R = 32;
+  const int kg = unit % (R / 4);
+  const int dg = unit / (R / 4);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(u32x4*)(tile + trs_offset(4 * kg + q, dg)) = row0 + 4 * kg + q < S ? vin[q] : z;
+}
+
 }  // namespace
 
 // dQ pass (and D = rowsum(dO O)).  One wave per SIMD: the next key block is
@@ -640,7 +685,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   constexpr int MD = D / 32;
   constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
   constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  constexpr int kSlot = 4 * kQT + 2 * kKvQ * 4;
+  // D = 128: the accumulation reads Q^T and dO^T straight from the row-major
+  // tiles (transposing LDS reads), so a slot holds Q, dO, lse and D only;
+  // D = 64 keeps transposed copies in the paired-chunk layout
+  constexpr bool kTr = D == 128;
+  constexpr int kTiles = kTr ? 2 : 4;
+  constexpr int kSlot = kTiles * kQT + 2 * kKvQ * 4;
   constexpr int kLds = 2 * kKV > 3 * kSlot ? 2 * kKV : 3 * kSlot;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int tid = threadIdx.x;
@@ -704,10 +754,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   auto stage = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
     char* sl = slot_of(qbk);
-    if (unit_on)
-      store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S, unit);
+    if (unit_on) {
+      if constexpr (kTr)
+        store_unit_trs(pre, sl + (unit_q ? 0 : kQT), qb0, S, unit);
+      else
+        store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S,
+                            unit);
+    }
     if (tid < 2 * kKvQ) {
-      float* lv4 = (float*)(sl + 4 * kQT);
+      float* lv4 = (float*)(sl + kTiles * kQT);
       const bool in = qb0 + (tid & (kKvQ - 1)) < S;
       lv4[tid] = tid < kKvQ ? (in ? pre_v * kLog2e : INFINITY) : (in ? pre_v : 0.f);
     }
@@ -719,25 +774,37 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   // C(qbk): dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot qbk
   auto accumulate = [&](int qbk) {
     const char* sl = slot_of(qbk);
-    const char* lqt = sl + 2 * kQT;   // Q^T
-    const char* ldot = sl + 3 * kQT;  // dO^T
+    if constexpr (kTr) {
+      const char* lq = sl;         // Q rows, read transposed
+      const char* ldo = sl + kQT;  // dO rows, read transposed
 #pragma unroll
-    for (int m = 0; m < MD; ++m)
+      for (int m = 0; m < MD; ++m)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
-        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
-        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
-      }
+        for (int g = 0; g < 2; ++g) {
+          Mma<bf16_t>::run(dv[m], tr_frag(ldo, 16 * g, 32 * m, lane), pp[g]);
+          Mma<bf16_t>::run(dk[m], tr_frag(lq, 16 * g, 32 * m, lane), ps[g]);
+        }
+    } else {
+      const char* lqt = sl + 2 * kQT;   // Q^T
+      const char* ldot = sl + 3 * kQT;  // dO^T
+#pragma unroll
+      for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
+          Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
+          Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
+        }
+    }
   };
 
   // block qbk: A(qbk), then its softmax with C(qbk - 1) issued alongside
   auto compute = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
     const char* sl = slot_of(qbk);
-    const char* lq = sl;                               // Q rows
-    const char* ldo = sl + kQT;                        // dO rows
-    const float* llse = (const float*)(sl + 4 * kQT);  // lse log2(e) (+inf past S)
+    const char* lq = sl;                                    // Q rows
+    const char* ldo = sl + kQT;                             // dO rows
+    const float* llse = (const float*)(sl + kTiles * kQT);  // lse log2(e) (+inf past S)
     const float* ldel = llse + kKvQ;                   // D
     // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4.
     // Each phase's LDS fragments are read together into their own registers
@@ -746,7 +813,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     u32x4 fq[KS], fdo[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int qo = k_offset(j, 2 * s + h, C);
+      const int qo = kTr ? trs_offset(j, 2 * s + h) : k_offset(j, 2 * s + h, C);
       fq[s] = *(const u32x4*)(lq + qo);
       fdo[s] = *(const u32x4*)(ldo + qo);
     }
