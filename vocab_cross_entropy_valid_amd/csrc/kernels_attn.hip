@@ -474,10 +474,11 @@ __device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int dim0, int
   return r;
 }
 
-// A load unit (see load_unit) into such a tile, rows past S zeroed.
+// A load unit (see load_unit) of an R-row tile into such a layout, rows past
+// S zeroed.
+template <int R>
 __device__ __forceinline__ void store_unit_trs(const u32x4 (&vin)[4], char* tile, int row0, int S,
                                                int unit) {
-  constexpr int R = 32;
   const int kg = unit % (R / 4);
   const int dg = unit / (R / 4);
   const u32x4 z = {0u, 0u, 0u, 0u};
@@ -499,7 +500,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int kTile = kKBlock * D * 2;  // 64 rows x D (= D rows x 64 entries)
-  constexpr int kSlot = 3 * kTile;        // K rows, K^T (paired chunks), V rows
+  // D = 128: K^T for the dQ product is read straight from the K rows
+  // (transposing LDS reads), so a slot holds K and V; D = 64 keeps a
+  // transposed copy of K in the paired-chunk layout
+  constexpr bool kTr = D == 128;
+  constexpr int kSlot = (kTr ? 2 : 3) * kTile;  // K rows, [K^T,] V rows
   __shared__ __attribute__((aligned(16))) char lds[2 * kSlot];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -562,18 +567,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int u = it * kAttnThreads + tid;
-      if (u < kKU)
-        store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
-      else if (u < 2 * kKU)
-        store_unit<D, kKBlock, false>(pre[it], sl + 2 * kTile, nullptr, kb * kKBlock, S, u - kKU);
+      if (u < kKU) {
+        if constexpr (kTr)
+          store_unit_trs<kKBlock>(pre[it], sl, kb * kKBlock, S, u);
+        else
+          store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
+      } else if (u < 2 * kKU) {
+        store_unit<D, kKBlock, false>(pre[it], sl + (kTr ? 1 : 2) * kTile, nullptr, kb * kKBlock,
+                                      S, u - kKU);
+      }
     }
   };
   auto compute = [&](int kb, int slot) {
     const int k0 = kb * kKBlock;
     if (a.causal && k0 > q0 + 31) return;  // every key after the wave's queries
     const char* lk = lds + slot * kSlot;
-    const char* lkt = lk + kTile;
-    const char* lv = lk + 2 * kTile;
+    const char* lkt = lk + kTile;  // D = 64 only
+    const char* lv = lk + (kTr ? 1 : 2) * kTile;
     // S^T = K Q^T and dP^T = V dO^T, one 32-key half (mt) at a time
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int off = k_offset(32 * mt + j, 2 * s + h, C);
-        fk[s] = *(const u32x4*)(lk + off);
+        fk[s] = *(const u32x4*)(lk + (kTr ? trs_offset(32 * mt + j, 2 * s + h) : off));
         fv[s] = *(const u32x4*)(lv + off);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -606,7 +616,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          ft[m][mt][g] = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(32 * m + j, 4 * mt + 2 * g + h));
+          ft[m][mt][g] = kTr ? tr_frag(lk, 32 * mt + 16 * g, 32 * m, lane)
+                             : *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(
+                                   32 * m + j, 4 * mt + 2 * g + h));
     __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); masks (sequence end, causal diagonal) only on
     // the blocks that need them
@@ -756,7 +768,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     char* sl = slot_of(qbk);
     if (unit_on) {
       if constexpr (kTr)
-        store_unit_trs(pre, sl + (unit_q ? 0 : kQT), qb0, S, unit);
+        store_unit_trs<kKvQ>(pre, sl + (unit_q ? 0 : kQT), qb0, S, unit);
       else
         store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S,
                             unit);
