@@ -92,6 +92,52 @@ __device__ __forceinline__ int vt_unit_offset(int dv, int u) {
   return vt_chunk_offset(dv, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
 }
 
+// Row-major bf16 tile of 128-dim rows (16 sixteen-byte chunks per 256-byte
+// row) that is also read transposed: chunk c of row r sits at position
+// c ^ trs(r), trs(r) = (r % 16) ^ 4 (r % 4).  trs is a bijection on any 16
+// consecutive rows, so 16 lanes reading one chunk of consecutive rows hit
+// distinct banks; a transposing read of 8 consecutive rows x 4 chunks puts
+// two rows' chunks on each group of four banks, i.e. each bank twice (the
+// minimum for 512 bytes); the staging writes spread evenly as well.
+__device__ __forceinline__ int trs_offset(int row, int chunk) {
+  return row * 256 + ((chunk ^ ((row & 15) ^ ((row & 3) << 2))) << 4);
+}
+
+// A fragment of the transposed tile, straight from such a row-major tile
+// with two ds_read_b64_tr_b16: operand row = tile column dim0 + lane % 32, K =
+// tile rows r0 + 4 (lane / 32) + {0..3} and the same + 8, the paired order
+// in which the accumulator-derived B operands hold the queries.  Within a
+// group of 16 lanes, lane i receives as element e the element i % 4 of the
+// 8 bytes lane 4 e + i / 4 addressed, so lane l addresses row r0 + 4 (l / 32)
+// + (l % 16) / 4 at column dim0 + 16 ((l / 16) % 2) + 4 (l % 4).
+__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int dim0, int lane) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int dim = dim0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const char* p1 = tile + trs_offset(row, dim >> 3) + (dim & 7) * 2;
+  const char* p2 = tile + trs_offset(row + 8, dim >> 3) + (dim & 7) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p1));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p2));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo);
+  const u32x2 b = __builtin_bit_cast(u32x2, hi);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// A load unit (see load_unit) of an R-row tile into such a layout, rows past
+// S zeroed.
+template <int R>
+__device__ __forceinline__ void store_unit_trs(const u32x4 (&vin)[4], char* tile, int row0, int S,
+                                               int unit) {
+  const int kg = unit % (R / 4);
+  const int dg = unit / (R / 4);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(u32x4*)(tile + trs_offset(4 * kg + q, dg)) = row0 + 4 * kg + q < S ? vin[q] : z;
+}
+
 template <int D>
 struct BlockRegs {
   static constexpr int kKLoads = kKBlock * D / 8 / kAttnThreads;              // 16-B K loads
@@ -439,52 +485,6 @@ __device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char
     u[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
     *(u32x2*)(tt + tt_unit_offset<R>(8 * dg + e, kg)) = u;
   }
-}
-
-// Row-major 32-row x 128-dim bf16 tile (16 sixteen-byte chunks per 256-byte
-// row) that is also read transposed: chunk c of row r sits at position
-// c ^ trs(r), trs(r) = (r % 16) ^ 4 (r % 4).  trs is a bijection on any 16
-// consecutive rows, so 16 lanes reading one chunk of consecutive rows hit
-// distinct banks; a transposing read of 8 consecutive rows x 4 chunks puts
-// two rows' chunks on each group of four banks, i.e. each bank twice (the
-// minimum for 512 bytes); the staging writes spread evenly as well.
-__device__ __forceinline__ int trs_offset(int row, int chunk) {
-  return row * 256 + ((chunk ^ ((row & 15) ^ ((row & 3) << 2))) << 4);
-}
-
-// A fragment of the transposed tile, straight from such a row-major tile
-// with two ds_read_b64_tr_b16: operand row = tile column dim0 + lane % 32, K =
-// tile rows r0 + 4 (lane / 32) + {0..3} and the same + 8, the paired order
-// in which the accumulator-derived B operands hold the queries.  Within a
-// group of 16 lanes, lane i receives as element e the element i % 4 of the
-// 8 bytes lane 4 e + i / 4 addressed, so lane l addresses row r0 + 4 (l / 32)
-// + (l % 16) / 4 at column dim0 + 16 ((l / 16) % 2) + 4 (l % 4).
-__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int dim0, int lane) {
-  typedef short i16x4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int dim = dim0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const char* p1 = tile + trs_offset(row, dim >> 3) + (dim & 7) * 2;
-  const char* p2 = tile + trs_offset(row + 8, dim >> 3) + (dim & 7) * 2;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p1));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p2));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo);
-  const u32x2 b = __builtin_bit_cast(u32x2, hi);
-  u32x4 r = {a[0], a[1], b[0], b[1]};
-  return r;
-}
-
-// A load unit (see load_unit) of an R-row tile into such a layout, rows past
-// S zeroed.
-template <int R>
-__device__ __forceinline__ void store_unit_trs(const u32x4 (&vin)[4], char* tile, int row0, int S,
-                                               int unit) {
-  const int kg = unit % (R / 4);
-  const int dg = unit / (R / 4);
-  const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *(u32x4*)(tile + trs_offset(4 * kg + q, dg)) = row0 + 4 * kg + q < S ? vin[q] : z;
 }
 
 }  // namespace
