@@ -357,6 +357,11 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     if (e != hipSuccess) return hip_fail(e, "zero-rows launch");
   }
 
+  // bf16 without an optimizer step: dH reads each W block directly (K-major,
+  // transposing LDS reads), so no W^T copy is built.  The optimizer step
+  // rewrites W's rows in its dW epilogue while dH may still run (the merged
+  // dH + dW launch), so it keeps dH on the copy; fp32 has no transposing read.
+  const bool w_direct = dtype == LCE_BF16 && step == nullptr;
   // At least one chunk, so that dW is written even when N == 0.
   for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
     lce::TransposeArgs th{};
@@ -373,24 +378,21 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     th.active_c0 = c0;
     e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(th, dtype, s); });
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
-    // bf16 without an optimizer step: dH reads the W block directly (K-major,
-    // transposing LDS reads), so the W^T copy is not built
-    const bool w_direct = dtype == LCE_BF16 && step == nullptr;
     for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
-      lce::TransposeArgs tw{};
-      tw.src = W;
-      tw.ld_src = d;
-      tw.gather = nullptr;
-      tw.row0 = v0;
-      tw.count = nullptr;
-      tw.nrows_static = V;
-      tw.dst = WT;
-      tw.ncols = p.Vs;
-      tw.ld_dst = p.ldWT;
-      tw.K = d;
-      tw.active_count = c0 > 0 ? valid_count : nullptr;
-      tw.active_c0 = c0;
       if (!w_direct) {
+        lce::TransposeArgs tw{};
+        tw.src = W;
+        tw.ld_src = d;
+        tw.gather = nullptr;
+        tw.row0 = v0;
+        tw.count = nullptr;
+        tw.nrows_static = V;
+        tw.dst = WT;
+        tw.ncols = p.Vs;
+        tw.ld_dst = p.ldWT;
+        tw.K = d;
+        tw.active_count = c0 > 0 ? valid_count : nullptr;
+        tw.active_c0 = c0;
         e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
         if (e != hipSuccess) return hip_fail(e, "transpose launch");
       }
