@@ -92,6 +92,9 @@ def test_config1_tiny_fp32():
     (333, 64, 1500, "f32", 0.2, 14),       # fp32, ragged everywhere
     (257, 192, 257, "bf16", 0.0, 15),      # one past a tile in N and V
     (9000, 64, 700, "bf16", 0.05, 16),     # several backward token chunks
+    # three vocabulary blocks, the last 233 entries (not a multiple of 64),
+    # and two hidden tiles with d = 320: dH reads W directly (K-major)
+    (500, 320, 33001, "bf16", 0.1, 17),
 ])
 def test_parity_small(N, d, V, dtype, ign, seed):
     announce(f"parity N={N} d={d} V={V} {dtype} ignore={ign} seed={seed}")
