@@ -163,6 +163,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       int rel_h[kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) rel_h[nt] = y[nt] - vw0 - 4 * h;  // label at c == rel_h
+      // Target logit, taken from the same fp32 accumulator as the sum (a
+      // label is always below V, so never a masked entry).  Only a wave in
+      // which some lane's label falls in its 128 entries runs the compare.
+      bool lab = false;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) lab |= (unsigned)(y[nt] - vw0) < (unsigned)kHalf;
+      if (__ballot(lab)) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (32 * mt + 8 * (i >> 2) + (i & 3) == rel_h[nt]) zy[nt] = acc[mt][nt][i];
+      }
       // per token: online (max, sum) update over each 32-entry slice (mt), so
       // that only 16 accumulator values are live in VGPRs at a time.  The
       // bounds mask (entries at or beyond V drop out as -inf) runs only on a
@@ -177,8 +192,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) {
               const int c = 32 * mt + 8 * (i >> 2) + (i & 3);
               z[i] = (!decltype(kMask)::value || c < vlim_h) ? acc[mt][nt][i] : -INFINITY;
-              // target logit, taken from the same fp32 accumulator as the sum
-              if (decltype(kLabel)::value && c == rel_h[nt]) zy[nt] = z[i];
             }
             float tmax = z[0];
 #pragma unroll
@@ -202,9 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       typedef std::integral_constant<bool, true> kOn;
       typedef std::integral_constant<bool, false> kOff;
       if (vw0 + kHalf > a.V) {
-        slices(kOn(), kOn());
+        slices(kOn(), kOff());
       } else {
-        slices(kOff(), kOn());
+        slices(kOff(), kOff());
       }
     }
 
