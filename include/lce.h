@@ -102,7 +102,9 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
  *                 same H, W, labels and ignore_index.
  *  dH             fully written: rows of ignored tokens are 0.
  *  dW             overwritten when accumulate_dW == 0, added to otherwise
- *                 (for a weight that also receives other gradients).
+ *                 (for a weight that also receives other gradients);
+ *                 16-byte aligned (stored as 4-float vectors), else
+ *                 LCE_ERR_INVALID_ARG before any launch.
  * The logits are recomputed chunk by chunk; nothing of size N * V is stored.
  * No floating-point atomics are used: results are bitwise reproducible.
  */
@@ -194,7 +196,7 @@ lce_status lce_lse_merge(const float* part_max, const float* part_sum, const flo
                          float* lse, double* loss_sum, float* loss_mean, void* stream);
 
 /* Backward of one shard, given the merged lse.  dW_shard [V_shard, d] f32 as
- * dW in lce_backward.  dH receives this shard's share: overwritten (ignored
+ * dW in lce_backward (16-byte aligned).  dH receives this shard's share: overwritten (ignored
  * rows set to 0) when accumulate_dH == 0, added to otherwise; summing the
  * shares of every shard gives lce_backward's dH.
  */

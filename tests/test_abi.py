@@ -106,6 +106,8 @@ def test_backward_rejects_bad_reduction_and_nulls():
     args[16] = fake
     args[17] = 16
     assert lib.lce_backward(*args) == _lib.LCE_ERR_WORKSPACE
+    args[14] = ctypes.c_void_p(0x1004)  # dW is stored as 16-byte vectors
+    assert lib.lce_backward(*args) == _lib.LCE_ERR_INVALID_ARG
 
 
 def test_gemm_and_timing_argument_checks():
@@ -148,6 +150,9 @@ def test_shard_workspace_and_merge_argument_checks():
     r = lib.lce_forward_shard(fake, fake, fake, -100, 10, 64, 100, 40, 30, 1, fake, fake, fake,
                               fake, fake, fake, fake, need - 1, None)
     assert r == _lib.LCE_ERR_WORKSPACE
+    r = lib.lce_backward_shard(fake, fake, fake, -100, fake, fake, fake, 10, 64, 100, 40, 30, 1,
+                               fake, 0, fake, 0, ctypes.c_void_p(0x1008), 0, fake, 1 << 40, None)
+    assert r == _lib.LCE_ERR_INVALID_ARG  # misaligned dW_shard
     # no shards, a stride shorter than N, missing outputs
     assert lib.lce_lse_merge(fake, fake, fake, 0, 10, 10, fake, fake, fake, fake, fake, None,
                              None) == _lib.LCE_ERR_INVALID_ARG

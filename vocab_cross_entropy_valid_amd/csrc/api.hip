@@ -502,6 +502,8 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
     return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
   if (!W || !valid_count || !grad_out || !dW)
     return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and dW must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(dW) & 15) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "dW must be 16-byte aligned");
   if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
     return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
   return backward_impl(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, 0, V,
@@ -578,6 +580,8 @@ lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t*
     return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_MEAN (0) or LCE_SUM (1)");
   if (!W_shard || !valid_count || !grad_out || !dW_shard)
     return fail(LCE_ERR_INVALID_ARG, "W_shard, valid_count, grad_out and dW_shard must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(dW_shard) & 15) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "dW_shard must be 16-byte aligned");
   if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
     return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
   return backward_impl(H, W_shard, labels, ignore_index, lse, valid_idx, valid_count, N, d, V_total,

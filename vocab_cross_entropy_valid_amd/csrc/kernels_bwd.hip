@@ -97,6 +97,17 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Two values as one non-temporal global store, for data that a later kernel
+// reads once (the recomputed G^T blocks).
+template <typename T> __device__ __forceinline__ void stream2(void* p, float a, float b);
+template <> __device__ __forceinline__ void stream2<bf16_t>(void* p, float a, float b) {
+  __builtin_nontemporal_store(pack_bf16x2(a, b), (uint32_t*)p);
+}
+template <> __device__ __forceinline__ void stream2<float>(void* p, float a, float b) {
+  const f32x2 v = {a, b};
+  __builtin_nontemporal_store(v, (f32x2*)p);
+}
+
 // --------------------------------------------------- recompute + G tile
 //
 // Same MFMA tile as the forward (A = W rows, B = gathered H rows, so each lane
@@ -189,7 +200,9 @@ __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* ld
     }
 
   // G^T[vocab][token]: the lane's 2 consecutive tokens per store; for a fixed
-  // accumulator register the 32 lanes of a half-wave cover 128 contiguous bytes
+  // accumulator register the 32 lanes of a half-wave cover 128 contiguous
+  // bytes.  Non-temporal stores: 1% faster than ordinary ones on the Llama-3
+  // head (dW reads the block once, after the whole recompute).
   const int il0 = tn * kTile + wb * kWaveN + 2 * j;  // local token of nt = 0
   char* GT = (char*)a.GT;
 #pragma unroll
@@ -197,7 +210,7 @@ __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* ld
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      Store2<T>::run(GT + (vl * a.ldGT + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
+      stream2<T>(GT + (vl * a.ldGT + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
     }
 
   char* G = (char*)a.G;
@@ -356,10 +369,13 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
 
 // ---------------------------------------------------------- dW += G^T H
 //
-// C tile rows = vocabulary entries of the block (A = G^T rows), columns =
-// hidden units (B = H^T rows); K runs over the chunk's valid tokens only
-// (the count is read on the device).  Each workgroup owns its dW tile, so
-// no atomics are needed and the result is deterministic.
+// K runs over the chunk's valid tokens only (the count is read on the
+// device).  Each workgroup owns its dW tile, so no atomics are needed and
+// the result is deterministic.  The plain store computes the tile as dW^T
+// (rows = hidden units from H^T, columns = vocabulary entries from G^T): a
+// lane then holds four consecutive hidden units of one dW row and writes
+// them as one 16-byte vector (2% faster than four 4-byte stores on the
+// Llama-3 head).  The optimizer epilogues keep rows = vocabulary entries.
 template <typename T, int kStep>  // 0: store dW; 1: SGD; 2: AdamW
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
@@ -372,8 +388,9 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   const int64_t nv = min(a.Vs, a.V - a.v0);
   const int TM = (int)((nv + kTile - 1) / kTile);
   const int TN = (int)((a.d + kTile - 1) / kTile);
-  int tm, tn;
-  if (!xcd_tile(slot, TM, TN, 4, 8, tm, tn)) return;
+  int tm, tn;  // vocabulary and hidden tile
+  if (kStep == 0 ? !xcd_tile(slot, TN, TM, 4, 8, tn, tm) : !xcd_tile(slot, TM, TN, 4, 8, tm, tn))
+    return;
   const int count = *a.valid_count;
   int64_t kact = (int64_t)count - a.c0;
   if (kact < 0) kact = 0;
@@ -383,15 +400,48 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 
   RowSource as{(const char*)a.GT, a.ldGT * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.Vs, 0};
   RowSource bs{(const char*)a.HT, a.ldHT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
-  const RowPtrs pa = make_row_ptrs<false>(as, tid);
-  const RowPtrs pb = make_row_ptrs<false>(bs, tid);
   Acc acc;
   zero_acc(acc);
-  tile_mainloop<T>(acc, lds, pa, pb, nstages, tid);
-
-  const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
-  const int m_base = tm * kTile + wa * kHalf + 4 * h;
-  if constexpr (kStep > 0) {
+  if constexpr (kStep == 0) {
+    tile_mainloop<T>(acc, lds, make_row_ptrs<false>(bs, tid), make_row_ptrs<false>(as, tid),
+                     nstages, tid);
+    // acc[mt][nt][4 g + e] is dW[v_base + 32 nt][k_base + 32 mt + 8 g + e]
+    float* out0 = a.dW + a.v0 * a.d;
+    const int v_base = tm * kTile + wb * kWaveN + (lane & 31);
+    const int k_base = tn * kTile + wa * kHalf + 4 * h;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // read-modify-write (accumulate) in two batches of 64 values
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int v = v_base + 32 * nt;
+      f32x4 old[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int k = k_base + 32 * mt + 8 * g;
+          old[mt][g] = (a.accumulate && v < nv && k < a.d)
+                           ? *(const f32x4*)(out0 + (int64_t)v * a.d + k) : zero;
+        }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int k = k_base + 32 * mt + 8 * g;  // d is a multiple of 64: all four in range
+          if (v < nv && k < a.d) {
+            f32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = old[mt][g][e] + acc[mt][nt][4 * g + e];
+            *(f32x4*)(out0 + (int64_t)v * a.d + k) = r;
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    tile_mainloop<T>(acc, lds, make_row_ptrs<false>(as, tid), make_row_ptrs<false>(bs, tid),
+                     nstages, tid);
+    const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
+    const int m_base = tm * kTile + wa * kHalf + 4 * h;
     // The gradient tile goes straight into the optimizer (no dW table; OjasX
     // page, core technology: no persistent .grad buffers).  PyTorch's
     // formulas: SGD p -= lr (g + wd p); AdamW p *= 1 - lr wd, m = b1 m +
@@ -442,33 +492,6 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-    return;
-  }
-  float* out0 = a.dW + a.v0 * a.d;
-  // read-modify-write (accumulate) in four batches of 32 values, as for dH
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    float old[16][kNT];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int n = n_base + 32 * nt;
-        old[i][nt] = (a.accumulate && ml < nv && n < a.d) ? out0[(int64_t)ml * a.d + n] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-      if (ml >= nv) continue;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int n = n_base + 32 * nt;
-        if (n < a.d) out0[(int64_t)ml * a.d + n] = old[i][nt] + acc[mt][nt][i];
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -531,9 +554,17 @@ hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Slots for the dW tiles of one vocabulary block: 4 x 8 blocks of tiles per
+// XCD, over (hidden, vocabulary) tiles for the plain store and over
+// (vocabulary, hidden) tiles for the optimizer epilogues (as dw_tile maps them).
+int dw_slots(const DwArgs& a) {
+  const int TV = (int)((a.Vs + kTile - 1) / kTile), TD = (int)((a.d + kTile - 1) / kTile);
+  const int TM = a.opt_kind == 0 ? TD : TV, TN = a.opt_kind == 0 ? TV : TD;
+  return 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
+}
+
 hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s) {
-  const int TM = (int)(a.Vs / kTile), TN = (int)((a.d + kTile - 1) / kTile);
-  a.nslots = 256 * ((((TM + 3) / 4) * ((TN + 7) / 8) + 7) / 8);
+  a.nslots = dw_slots(a);
   grid = std::min(grid, a.nslots);
   if (a.opt_kind == 1) {
     if (dtype == 1)
@@ -556,8 +587,7 @@ hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s) {
 hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s) {
   const int TMh = (int)(ha.C / kTile), TNh = (int)((ha.d + kTile - 1) / kTile);
   const int n_dh = 256 * ((((TMh + 1) / 2) * ((TNh + 15) / 16) + 7) / 8);
-  const int TMw = (int)(wa.Vs / kTile), TNw = (int)((wa.d + kTile - 1) / kTile);
-  wa.nslots = 256 * ((((TMw + 3) / 4) * ((TNw + 7) / 8) + 7) / 8);
+  wa.nslots = dw_slots(wa);
   const dim3 grid((unsigned)(n_dh + wa.nslots));
   // the optimizer epilogues rewrite W's rows while dH tiles run: they keep
   // dH on the transposed copy (ha.W null)
