@@ -281,12 +281,31 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __rest
   const int count = *a.valid_count;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
+  // Chunks in batches of 16 loads issued together: one memory round trip per
+  // batch instead of one per chunk (the kernel is latency-bound).  The sum
+  // still runs over the chunks in order.
+  constexpr int kB = 16;
   float M = -INFINITY;
-  for (int c = 0; c < a.J; ++c) M = fmaxf(M, a.pm[(int64_t)c * a.Nb + i]);
+  for (int c0 = 0; c0 < a.J; c0 += kB) {
+    float pm[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      pm[b] = (c0 + b < a.J) ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) M = fmaxf(M, pm[b]);
+  }
   float S = 0.f;
-  for (int c = 0; c < a.J; ++c) {
-    const int64_t o = (int64_t)c * a.Nb + i;
-    S += a.ps[o] * fast_exp2(a.pm[o] - M);
+  for (int c0 = 0; c0 < a.J; c0 += kB) {
+    float pm[kB], ps[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const bool in = c0 + b < a.J;
+      pm[b] = in ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
+      ps[b] = in ? a.ps[(int64_t)(c0 + b) * a.Nb + i] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (c0 + b < a.J) S += ps[b] * fast_exp2(pm[b] - M);
   }
   const int r = a.valid_idx[i];
   const int64_t yv = a.labels[r];
@@ -322,12 +341,31 @@ __global__ __launch_bounds__(256) void fwd_part_kernel(FwdArgs a, float* __restr
   const int count = *a.valid_count;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
+  // Chunks in batches of 16 loads issued together: one memory round trip per
+  // batch instead of one per chunk (the kernel is latency-bound).  The sum
+  // still runs over the chunks in order.
+  constexpr int kB = 16;
   float M = -INFINITY;
-  for (int c = 0; c < a.J; ++c) M = fmaxf(M, a.pm[(int64_t)c * a.Nb + i]);
+  for (int c0 = 0; c0 < a.J; c0 += kB) {
+    float pm[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      pm[b] = (c0 + b < a.J) ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) M = fmaxf(M, pm[b]);
+  }
   float S = 0.f;
-  for (int c = 0; c < a.J; ++c) {
-    const int64_t o = (int64_t)c * a.Nb + i;
-    S += a.ps[o] * fast_exp2(a.pm[o] - M);
+  for (int c0 = 0; c0 < a.J; c0 += kB) {
+    float pm[kB], ps[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const bool in = c0 + b < a.J;
+      pm[b] = in ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
+      ps[b] = in ? a.ps[(int64_t)(c0 + b) * a.Nb + i] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (c0 + b < a.J) S += ps[b] * fast_exp2(pm[b] - M);
   }
   const int r = a.valid_idx[i];
   const int64_t yl = a.labels[r] - a.y_off;
