@@ -44,10 +44,16 @@ hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_
 // dst[k][i] = src[row(row0 + i)][k] for i < rows available, 0 for the rest of
 // the ncols columns.  64 x 64 element tiles through LDS; HBM-bound.  Reads
 // and writes are 16-byte vectors (8 bf16 or 4 fp32 per access).
+//
+// bf16: a thread reads 8 consecutive columns k of two adjacent rows (2p,
+// 2p + 1) and pairs them into 32-bit words {src[2p][k], src[2p + 1][k]},
+// which is already the layout of dst row k at columns 2p, 2p + 1.  The words
+// go to LDS as 64 rows (k) of 32 words (p) with a 33-word stride, so that
+// the 64 lanes of a write (8 column vectors x 8 row pairs) hit distinct
+// banks; each output vector is then 4 word reads instead of 8 two-byte ones.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   constexpr int kV = 16 / sizeof(T);  // elements per 16-byte vector
-  __shared__ T tile[64][64 + kV];
   const int tid = threadIdx.x;
   const int64_t i0 = (int64_t)blockIdx.x * 64;
   const int64_t k0 = (int64_t)blockIdx.y * 64;
@@ -55,6 +61,43 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   int64_t avail = a.count ? (int64_t)(*a.count) - a.row0 : a.nrows_static - a.row0;
   if (avail < 0) avail = 0;
   if (avail > a.ncols) avail = a.ncols;
+  if constexpr (sizeof(T) == 2) {
+    __shared__ uint32_t tw[64 * 33];
+    const int kv = tid & 7;  // column vector: columns k0 + 8 kv .. + 7
+    const int p = tid >> 3;  // row pair: rows i0 + 2p, i0 + 2p + 1
+    u32x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t i = i0 + 2 * p + h;
+      v[h] = u32x4{0u, 0u, 0u, 0u};
+      if (i < avail) {
+        const int64_t r = a.row0 + i;
+        const int64_t phys = a.gather ? (int64_t)a.gather[r] : r;
+        v[h] = *(const u32x4*)((const T*)a.src + phys * a.ld_src + k0 + 8 * kv);
+      }
+    }
+    // word q of a row holds columns 2q (low half) and 2q + 1 (high half)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = v[0][q], y = v[1][q];
+      tw[(8 * kv + 2 * q) * 33 + p] = (x & 0xffffu) | (y << 16);
+      tw[(8 * kv + 2 * q + 1) * 33 + p] = (x >> 16) | (y & 0xffff0000u);
+    }
+    __syncthreads();
+    // dst row k, columns i0 + 8 g .. + 7 = words 4 g .. 4 g + 3 of LDS row k
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = it * 256 + tid;
+      const int k = idx >> 3;
+      const int g = idx & 7;
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = tw[k * 33 + 4 * g + j];
+      *(u32x4*)((T*)a.dst + (k0 + k) * a.ld_dst + i0 + 8 * g) = w;
+    }
+    return;
+  }
+  __shared__ T tile[64][64 + kV];
   // read: 64 rows x 64 elements = 64 * 64 / kV vectors; thread -> (row, vector)
   constexpr int kVecPerRow = 64 / kV;
 #pragma unroll
