@@ -329,7 +329,9 @@ typedef enum {
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the
- * launch stream (host-side registry, process-wide). */
+ * launch stream (host-side registry, process-wide).  The events are created
+ * with hipEventDisableSystemFence: they time the launches and order nothing
+ * (a caller synchronises its stream or device before reading results). */
 lce_status lce_timing_enable(int on);
 /* Clears the registry. */
 lce_status lce_timing_reset(void);

@@ -158,8 +158,11 @@ hipEvent_t take_event() {
       return e;
     }
   }
+  // Timing-only events: without the system-scope fence that a default event
+  // performs when it completes, recording one writes back and invalidates no
+  // cache, so the instrumented launches run as they would without it.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
