@@ -95,6 +95,10 @@ def test_config1_tiny_fp32():
     # three vocabulary blocks, the last 233 entries (not a multiple of 64),
     # and two hidden tiles with d = 320: dH reads W directly (K-major)
     (500, 320, 33001, "bf16", 0.1, 17),
+    # two token chunks (the second dW pass adds to the first) with a partial
+    # second hidden tile (d = 320), in bf16 and fp32
+    (8400, 320, 900, "bf16", 0.05, 18),
+    (8300, 128, 600, "f32", 0.1, 19),
 ])
 def test_parity_small(N, d, V, dtype, ign, seed):
     announce(f"parity N={N} d={d} V={V} {dtype} ignore={ign} seed={seed}")
