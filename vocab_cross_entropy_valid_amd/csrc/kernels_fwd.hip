@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       // that only 16 accumulator values are live in VGPRs at a time.  The
       // bounds mask (entries at or beyond V drop out as -inf) runs only on a
       // wave whose entries reach past V (a wave-uniform branch).
-      auto slices = [&](auto kMask, auto kLabel) {
+      auto slices = [&](auto kMask) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
@@ -215,9 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_lse_kernel(FwdArgs a) {
       typedef std::integral_constant<bool, true> kOn;
       typedef std::integral_constant<bool, false> kOff;
       if (vw0 + kHalf > a.V) {
-        slices(kOn(), kOff());
+        slices(kOn());
       } else {
-        slices(kOff(), kOff());
+        slices(kOff());
       }
     }
 
@@ -272,20 +272,14 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int grid, hipStream_t s) {
 
 // ---------------------------------------------------------------- merge
 //
-// Combines the J chunk partials of each compact row with the same
-// max-and-rescale step, then lse = (M + log2 S) ln 2 and
-// loss = lse - z_target, written at the row's original position.
-__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __restrict__ loss,
-                                                        float* __restrict__ lse,
-                                                        float* __restrict__ loss_c) {
-  const int count = *a.valid_count;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= count) return;
-  // Chunks in batches of 16 loads issued together: one memory round trip per
-  // batch instead of one per chunk (the kernel is latency-bound).  The sum
-  // still runs over the chunks in order.
+// (M, S) of compact row i over the J chunk partials: M = max of the chunk
+// maxima, S = sum of each chunk's sum rescaled to M (log2 units).  The loads
+// go out in batches of 16, one memory round trip per batch instead of one
+// per chunk (the merge is latency-bound); the sum runs over the chunks in
+// order.
+__device__ __forceinline__ void merge_chunks(const FwdArgs& a, int64_t i, float& M, float& S) {
   constexpr int kB = 16;
-  float M = -INFINITY;
+  M = -INFINITY;
   for (int c0 = 0; c0 < a.J; c0 += kB) {
     float pm[kB];
 #pragma unroll
@@ -294,7 +288,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __rest
 #pragma unroll
     for (int b = 0; b < kB; ++b) M = fmaxf(M, pm[b]);
   }
-  float S = 0.f;
+  S = 0.f;
   for (int c0 = 0; c0 < a.J; c0 += kB) {
     float pm[kB], ps[kB];
 #pragma unroll
@@ -307,6 +301,19 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __rest
     for (int b = 0; b < kB; ++b)
       if (c0 + b < a.J) S += ps[b] * fast_exp2(pm[b] - M);
   }
+}
+
+// Combines the J chunk partials of each compact row with the same
+// max-and-rescale step, then lse = (M + log2 S) ln 2 and
+// loss = lse - z_target, written at the row's original position.
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __restrict__ loss,
+                                                        float* __restrict__ lse,
+                                                        float* __restrict__ loss_c) {
+  const int count = *a.valid_count;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float M, S;
+  merge_chunks(a, i, M, S);
   const int r = a.valid_idx[i];
   const int64_t yv = a.labels[r];
   const int cy = (int)(yv / kVocabTile) / a.tpc;
@@ -341,32 +348,8 @@ __global__ __launch_bounds__(256) void fwd_part_kernel(FwdArgs a, float* __restr
   const int count = *a.valid_count;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
-  // Chunks in batches of 16 loads issued together: one memory round trip per
-  // batch instead of one per chunk (the kernel is latency-bound).  The sum
-  // still runs over the chunks in order.
-  constexpr int kB = 16;
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < a.J; c0 += kB) {
-    float pm[kB];
-#pragma unroll
-    for (int b = 0; b < kB; ++b)
-      pm[b] = (c0 + b < a.J) ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
-#pragma unroll
-    for (int b = 0; b < kB; ++b) M = fmaxf(M, pm[b]);
-  }
-  float S = 0.f;
-  for (int c0 = 0; c0 < a.J; c0 += kB) {
-    float pm[kB], ps[kB];
-#pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      const bool in = c0 + b < a.J;
-      pm[b] = in ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
-      ps[b] = in ? a.ps[(int64_t)(c0 + b) * a.Nb + i] : 0.f;
-    }
-#pragma unroll
-    for (int b = 0; b < kB; ++b)
-      if (c0 + b < a.J) S += ps[b] * fast_exp2(pm[b] - M);
-  }
+  float M, S;
+  merge_chunks(a, i, M, S);
   const int r = a.valid_idx[i];
   const int64_t yl = a.labels[r] - a.y_off;
   float zt = -INFINITY;
