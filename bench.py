@@ -285,8 +285,9 @@ def main():
                          "causal) instead of the loss path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with no communication in forward; see DESIGN.md)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(token rows would shard across GPUs, with no communication in the "
+              "forward; the vocabulary-shard entry points cover a split table)",
               file=sys.stderr)
         sys.exit(2)
 
