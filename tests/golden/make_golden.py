@@ -7,12 +7,14 @@ comes from the GPU path.  For each full-size configuration it stores:
                 regenerates the inputs and must see the same bytes
   n_valid       number of valid rows
   loss_sum      sum of the per-row losses (full fp64 forward)
+  loss_valid    per-row loss of every valid row, in valid-index order (fp64)
+  lse_valid     per-row logsumexp of every valid row, same order (fp64)
   vocab_ids     sampled vocabulary rows (frequent labels, the ragged last
                 tile, random ids)
   dW_rows       dW[vocab_ids] for the mean loss (needs the logsumexp of every
                 valid row, hence the full forward)
 
-Per-row loss / lse / dH are cheap and are recomputed live by the test.
+Per-row dH is cheap and is recomputed live by the test on sampled rows.
 
 Usage: python tests/golden/make_golden.py [config ...]   (default 2 3 4 5)
 """
@@ -50,6 +52,7 @@ def make(cid: int) -> None:
     out = os.path.join(HERE, f"full_config{cid}.npz")
     np.savez_compressed(out, checksum=np.array(cs), n_valid=np.array(f.valid_count),
                         loss_sum=np.array(f.loss_sum), vocab_ids=vid,
+                        loss_valid=f.loss[f.valid_idx], lse_valid=f.lse[f.valid_idx],
                         dW_rows=dW.astype(np.float32))
     print(f"config {cid}: n_valid {f.valid_count} mean loss {f.loss_mean:.6f} "
           f"(forward {t1 - t0:.0f} s, total {time.time() - t0:.0f} s) -> {out}", flush=True)

@@ -5,8 +5,10 @@ The fp64 oracle cannot redo a 62K x 128K x 4K forward in a test, so:
   * valid_count / valid_idx: bit-exact against the oracle's compaction;
   * mean loss: within 2e-3 of the stored oracle value (tests/golden, written
     by make_golden.py from the oracle only);
-  * per-row loss / lse (1e-4 absolute) and dH rows (1e-2 relative L2) on
-    sampled rows, recomputed live by the oracle row by row;
+  * per-row loss and lse of every valid row (1e-4 absolute) against the
+    stored oracle values;
+  * dH rows (1e-2 relative L2) on sampled rows, recomputed live by the
+    oracle row by row;
   * dW rows (1e-2 relative L2) on stored sampled vocabulary rows;
   * properties at any size: dH rows of ignored tokens are exactly 0, the
     columns of dW sum to ~0 (rows of softmax - onehot sum to 0), and
@@ -51,12 +53,15 @@ def test_full_size_config(cid):
     assert abs(float(fwd.loss_mean.item()) - mean_ref) <= 2e-3
     assert abs(float(fwd.loss_sum.item()) - float(g["loss_sum"])) <= 1e-5 * float(g["loss_sum"])
 
-    # sampled rows, recomputed live by the oracle
+    # every valid row's loss and lse against the stored oracle values
+    loss = fwd.loss.cpu().numpy()
+    lse = fwd.lse.cpu().numpy()
+    np.testing.assert_allclose(loss[idx], g["loss_valid"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(lse[idx], g["lse_valid"], rtol=0, atol=1e-4)
+    # sampled rows, recomputed live by the oracle (also checks the stored values)
     rng = np.random.default_rng(100 + cid)
     rows = np.unique(np.concatenate([idx[:2], idx[-2:], rng.choice(idx, 12, replace=False)]))
     lse_ref, loss_ref, _ = oracle.rows_forward(H, W, y, rows)
-    loss = fwd.loss.cpu().numpy()
-    lse = fwd.lse.cpu().numpy()
     np.testing.assert_allclose(loss[rows], loss_ref, rtol=0, atol=1e-4)
     np.testing.assert_allclose(lse[rows], lse_ref, rtol=0, atol=1e-4)
     dH_ref = oracle.rows_dH(H, W, y, rows, 1.0 / n_valid)

@@ -106,6 +106,40 @@ def test_parity_small(N, d, V, dtype, ign, seed):
     _check(run_path(H, W, y, dtype), H, W, y, dtype)
 
 
+# The launch configuration the benchmark times for d >= 1793: a full token
+# chunk (C = 8192 rows) gives (C / 256) * ceil(d / 256) >= 256 dH tiles, so
+# the host runs dH (W read K-major in bf16, W^T in fp32) and the persistent
+# dW kernel as two launches per vocabulary block instead of the merged one.
+# Each case asserts through the timing registry that it took that path.
+@pytest.mark.parametrize("N,d,V,dtype,ign,seed", [
+    # 64-wide last hidden tile (1856 = 7 * 256 + 64), ragged vocabulary
+    (8192, 1856, 3001, "bf16", 0.1, 41),
+    # half the rows ignored: fewer active token tiles than C / 256
+    (8192, 2048, 700, "bf16", 0.5, 42),
+    # three token chunks: the second and third dW passes add to the first
+    (16640, 2048, 1500, "bf16", 0.02, 43),
+    # fp32: dH from the transposed W block
+    (8192, 2048, 600, "f32", 0.1, 44),
+])
+def test_parity_separate_dh_dw_launches(N, d, V, dtype, ign, seed):
+    from vocab_cross_entropy_valid_amd import _lib
+    announce(f"separate dH/dW launches N={N} d={d} V={V} {dtype} ignore={ign} seed={seed}")
+    H, W, y = workloads.custom(N, d, V, dtype=dtype, seed=seed, ignore_frac=ign)
+    _lib.lce_timing_reset()
+    _lib.lce_timing_enable(True)
+    try:
+        out = run_path(H, W, y, dtype)
+    finally:
+        _lib.lce_timing_enable(False)
+    launches = {name: _lib.lce_timing_query(k)[1] for k, name in enumerate(_lib.KERNEL_CLASSES)}
+    _lib.lce_timing_reset()
+    chunks = -(-N // 8192)
+    blocks = -(-V // 16384)
+    assert launches["dh"] == chunks * blocks and launches["dw"] == chunks * blocks, launches
+    assert launches["dh_dw"] == 0, launches
+    _check(out, H, W, y, dtype)
+
+
 def test_reduction_sum_and_grad_scale():
     announce("reduction=sum grad=2.5")
     H, W, y = workloads.custom(400, 128, 2100, seed=21)
