@@ -67,7 +67,11 @@ typedef enum { LCE_MEAN = 0, LCE_SUM = 1 } lce_reduction;
 
 /* Bytes of device workspace that lce_forward and lce_backward need for these
  * sizes (the larger of the two; the calls may share one buffer).  Returns 0
- * for invalid sizes. */
+ * for invalid sizes.  Bounded by the token chunk (8192 rows), the vocabulary
+ * block (16384 entries) and d, plus O(N) per-token vectors: for bf16 the
+ * bounded G block and its transpose (bf16 [8192, 16384] each) and the
+ * chunk's transposed H rows (bf16 [d, 8192]); fp32 adds the transposed W
+ * block (fp32 [d, 16384]).  It never grows with N * V. */
 size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype);
 
 /* Forward pass.
@@ -114,6 +118,14 @@ lce_status lce_backward(const void* H, const void* W, const int64_t* labels, int
                         int reduction, float* dH, float* dW, int accumulate_dW, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* fp32 -> bf16 copy of n values (e.g. dH or dW for a bf16 parameter):
+ * dst[i] = src[i] rounded to the nearest bfloat16, ties to even; NaN stays
+ * NaN, values beyond the bf16 range become +-inf.  src (f32 [n]) and dst
+ * (bf16 bits [n]) are device memory, 16-byte aligned, not overlapping, else
+ * LCE_ERR_INVALID_ARG before any launch.  One HBM-bound kernel on `stream`
+ * (the optional output cast after the dH zero-fill of ignored rows). */
+lce_status lce_cast_bf16(const float* src, void* dst, int64_t n, void* stream);
+
 /* ------------------------------------------ fused optimizer update
  *
  * The backward pass with the optimizer applied to each dW tile as it is
@@ -141,11 +153,21 @@ typedef struct {
  * rounded to nearest even, and W_master is required; for fp32 W, W_master may
  * be NULL and W itself is updated.  exp_avg / exp_avg_sq: fp32 [V, d] AdamW
  * state, updated in place (NULL for SGD).  Every row of W is updated (g = 0
- * for rows no valid token touches).  Needs N <= 8192 (one token chunk, so
- * each dW tile is complete when it is applied): LCE_ERR_UNSUPPORTED
- * otherwise.  A W row is rewritten only after its last read in this pass;
- * dH uses the weights from before the update.
+ * for rows no valid token touches).  Any N: the vocabulary is walked block by
+ * block, and a block's dW, summed over the token chunks in an fp32
+ * accumulator inside the workspace, is applied by the last chunk that holds
+ * valid rows.  A W row is rewritten only after its last read in this pass;
+ * dH uses the weights from before the update.  Workspace: at least
+ * lce_step_workspace_bytes(N, d, V, dtype) bytes (also enough for
+ * lce_forward), 256-byte aligned, else LCE_ERR_WORKSPACE.
  */
+/* Bytes of device workspace lce_backward_step needs: lce_workspace_bytes plus
+ * the transposed W block (dH keeps reading the block's old weights while the
+ * update rewrites them) and, when N exceeds one token chunk (8192 rows), the
+ * fp32 dW block accumulator ([16384, d]).  Independent of N beyond that and
+ * of V.  Returns 0 for invalid sizes. */
+size_t lce_step_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype);
+
 lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int64_t ignore_index,
                              const float* lse, const int32_t* valid_idx, const int32_t* valid_count,
                              int64_t N, int64_t d, int64_t V, int dtype, const float* grad_out,
@@ -325,7 +347,8 @@ typedef enum {
   LCE_K_ATTN_DQ = 12,  /* attention backward, dQ pass (and rowsum(dO O)) */
   LCE_K_ATTN_DKV = 13, /* attention backward, dK / dV pass               */
   LCE_K_DH_DW = 14,    /* dH and dW of one vocabulary block, one launch   */
-  LCE_K_COUNT = 15
+  LCE_K_CAST = 15,     /* fp32 -> bf16 output cast                        */
+  LCE_K_COUNT = 16
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -382,6 +382,47 @@ def optimizer_step(p, g, kind: str, lr: float, weight_decay: float = 0.0, beta1:
 
 
 # --------------------------------------------------------------------------
+# output cast
+# --------------------------------------------------------------------------
+#
+# The gradients come out of the backward pass in float32; a bfloat16
+# parameter takes them rounded to the nearest bfloat16 value, a tie going to
+# the neighbour whose last mantissa bit is 0 (IEEE round to nearest, ties to
+# even).  A bfloat16 value is a float32 whose low 16 bits are zero (sign, 8
+# exponent bits, 7 mantissa bits).  Below, the two bfloat16 neighbours of x
+# are found from its bit pattern and the nearer one is picked by comparing
+# the two distances exactly in float64.
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """float32 array of x rounded to the nearest bfloat16 (ties to even).
+
+    NaN stays NaN; values that are already bfloat16 (0, inf included) are
+    unchanged; a magnitude at or past the midpoint between the largest
+    bfloat16 and 2^128 becomes inf."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    down = u & 0xFFFF0000                    # same sign, magnitude truncated
+    up = down + 0x10000                      # next bfloat16 away from zero
+    E = ((u >> 23) & 0xFF).astype(np.int64)  # exponent field of x
+    spacing = np.ldexp(1.0, np.maximum(E, 1) - 134)   # bfloat16 step at x
+    ax = np.abs(x.astype(np.float64))
+    lo = np.abs(down.astype(np.uint32).view(np.float32).astype(np.float64))
+    hi = lo + spacing
+    with np.errstate(invalid="ignore"):
+        d_lo = ax - lo
+        d_hi = hi - ax
+    odd = ((down >> 16) & 1) == 1
+    take_up = (d_hi < d_lo) | ((d_hi == d_lo) & odd)
+    out = np.where(take_up, up, down).astype(np.uint32)
+    exact = (u & 0xFFFF) == 0
+    out = np.where(exact, u.astype(np.uint32), out)
+    res = out.view(np.float32).copy()
+    res[np.isnan(x)] = np.nan
+    return res.reshape(x.shape)
+
+
+# --------------------------------------------------------------------------
 # attention through an online softmax
 # --------------------------------------------------------------------------
 #

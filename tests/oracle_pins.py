@@ -614,6 +614,62 @@ def pin_attn_backward_closed_forms(o):
         np.testing.assert_allclose(g.dK.sum(axis=-2), 0.0, atol=1e-12)
 
 
+# ------------------------------------------------------------- output cast
+
+def _bf16_sweep():
+    rng = np.random.default_rng(700)
+    x = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e-3).astype(np.float32),
+        np.ldexp(rng.random(500) + 1.0, rng.integers(-149, 128, 500)).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38,
+                  3.4028235e38, 1e-45, -1e-45, 1.1754944e-38], dtype=np.float32),
+    ])
+    # exact ties: a bfloat16 value plus half its step, for even and odd last bits
+    base = rng.integers(0x3F000000, 0x40000000, 300, dtype=np.uint64) & 0xFFFF0000
+    ties = (base + 0x8000).astype(np.uint32).view(np.float32)
+    # one bit either side of a tie
+    near = np.concatenate([(base + 0x7FFF).astype(np.uint32).view(np.float32),
+                           (base + 0x8001).astype(np.uint32).view(np.float32)])
+    return np.concatenate([x, ties, -ties, near])
+
+
+def pin_bf16_matches_torch(o):
+    """Round to nearest even against PyTorch's CPU float32 -> bfloat16
+    conversion (a library routine the oracle does not use), on random values,
+    subnormals, values near the overflow threshold, exact ties and values one
+    bit off a tie; NaN stays NaN."""
+    import torch
+    x = _bf16_sweep()
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = o.round_to_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(o.round_to_bf16(np.array([np.nan], np.float32)))[0]
+
+
+def pin_bf16_closed_forms(o):
+    """Values with the low 16 bits zero are unchanged; 1 + 2^-8 lies halfway
+    between 1 (even) and 1 + 2^-7 (odd) and goes to 1; 1 + 3 2^-8 lies halfway
+    between 1 + 2^-7 (odd) and 1 + 2^-6 (even) and goes up; the error never
+    exceeds half a bfloat16 step and the rounding is monotone."""
+    f = np.float32
+    assert o.round_to_bf16(np.array([1 + 2.0 ** -8], f))[0] == 1.0
+    assert o.round_to_bf16(np.array([1 + 3 * 2.0 ** -8], f))[0] == f(1 + 2.0 ** -6)
+    assert o.round_to_bf16(np.array([-(1 + 3 * 2.0 ** -8)], f))[0] == f(-(1 + 2.0 ** -6))
+    assert o.round_to_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -20], f))[0] == f(1 + 2.0 ** -7)
+    x = _bf16_sweep()
+    x = x[np.isfinite(x) & (np.abs(x) < 3.3e38)]
+    r = o.round_to_bf16(x)
+    assert np.all((r.view(np.uint32) & 0xFFFF) == 0)
+    ex = x[(x.view(np.uint32) & 0xFFFF) == 0]
+    assert np.array_equal(o.round_to_bf16(ex), ex)
+    e = np.frexp(np.abs(x.astype(np.float64)))[1]
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    assert np.all(np.abs(r.astype(np.float64) - x) <= step / 2)
+    srt = np.sort(x)
+    assert np.all(np.diff(o.round_to_bf16(srt).astype(np.float64)) >= 0)
+
+
 PINS = [
     pin_w_zero, pin_h_zero, pin_v_one, pin_two_class, pin_dw_colsum,
     pin_shift_invariance, pin_permutation, pin_ignored_rows,
@@ -625,7 +681,7 @@ PINS = [
     pin_attn_uniform, pin_attn_single_key, pin_attn_key_shift, pin_attn_permutation,
     pin_attn_rows_sum_to_one, pin_attn_causal_prefix, pin_attn_dominant_key,
     pin_attn_torch_sdpa, pin_attn_backward_finite_differences, pin_attn_backward_torch,
-    pin_attn_backward_closed_forms,
+    pin_attn_backward_closed_forms, pin_bf16_matches_torch, pin_bf16_closed_forms,
 ]
 
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "lce.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lce_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lce_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -46,10 +46,13 @@ def test_workspace_bounded_independent_of_n_times_v():
     assert w3 == w5
     # the backward block is bounded by constants (token chunk C <= 8192,
     # vocabulary block Vs <= 16384, padded strides) and d, never by N or V:
-    # G [C, Vs], G^T [Vs, C], H^T [d, C], W^T [d, Vs] in bf16
+    # G [C, Vs], G^T [Vs, C], H^T [d, C] in bf16 (dH reads W itself)
     C, Vs, pad, d = 8192, 16384, 64, 4096
-    bound = 2 * (C * (Vs + pad) + Vs * (C + pad) + d * (C + pad) + d * (Vs + pad)) + (1 << 20)
-    assert w5 <= bound
+    exact = 2 * (C * (Vs + pad) + Vs * (C + pad) + d * (C + pad))
+    assert w5 == exact
+    # fp32 adds the W^T block [d, Vs]
+    wf = _lib.lce_workspace_bytes(65536, d, 128256, _lib.LCE_F32)
+    assert wf == 2 * exact + 4 * d * (Vs + pad)
     # far below the [N, V] fp32 logits table it replaces
     assert w5 < 65536 * 128256 * 4 / 40
     # growing V past the vocabulary block does not grow the workspace
@@ -173,7 +176,6 @@ def test_backward_step_argument_checks_before_launch():
         return lib.lce_backward_step(fake, fake, fake, -100, fake, fake, fake, N, 64, 100, dtype,
                                      fake, 0, fake, master, m, v, ctypes.byref(o), fake, 1 << 40,
                                      None)
-    assert call(N=8193) == _lib.LCE_ERR_UNSUPPORTED        # more than one token chunk
     assert call(master=None) == _lib.LCE_ERR_INVALID_ARG   # bf16 without master weights
     assert call(kind=7) == _lib.LCE_ERR_INVALID_ARG
     assert call(step=0) == _lib.LCE_ERR_INVALID_ARG
@@ -181,7 +183,28 @@ def test_backward_step_argument_checks_before_launch():
     assert call(eps=0.0) == _lib.LCE_ERR_INVALID_ARG
     assert call(lr=-1.0) == _lib.LCE_ERR_INVALID_ARG
     assert call(m=None) == _lib.LCE_ERR_INVALID_ARG
-    assert call(kind=_lib.LCE_OPT_SGD, m=None, v=None, N=8193) == _lib.LCE_ERR_UNSUPPORTED
+    # any N: several token chunks need the larger step workspace
+    need = _lib.lce_step_workspace_bytes(20000, 64, 100, 1)
+    o = _lib.LceOptimizer(kind=_lib.LCE_OPT_SGD, lr=1e-3, weight_decay=0.0, beta1=0.9,
+                          beta2=0.999, eps=1e-8, step=1)
+    r = lib.lce_backward_step(fake, fake, fake, -100, fake, fake, fake, 20000, 64, 100, 1, fake,
+                              0, fake, fake, None, None, ctypes.byref(o), fake, need - 1, None)
+    assert r == _lib.LCE_ERR_WORKSPACE
+
+
+def test_step_workspace_is_bounded():
+    """The fused step adds the transposed W block and, beyond one token chunk,
+    the fp32 dW block accumulator: bounded by constants and d, not by N or V."""
+    bf = _lib.LCE_BF16
+    d, Vs, C, pad = 4096, 16384, 8192, 64
+    plain3 = _lib.lce_workspace_bytes(8192, d, 128256, bf)
+    step3 = _lib.lce_step_workspace_bytes(8192, d, 128256, bf)
+    assert step3 - plain3 == 2 * d * (Vs + pad)                # W^T block, one chunk
+    step4 = _lib.lce_step_workspace_bytes(16384, d, 260000, bf)
+    step5 = _lib.lce_step_workspace_bytes(65536, d, 128256, bf)
+    assert step4 == step5 == step3 + 4 * Vs * d                # + fp32 dW block accumulator
+    assert _lib.lce_step_workspace_bytes(1 << 20, d, 128256, bf) - step5 < (1 << 20) * 64 * 13
+    assert _lib.lce_step_workspace_bytes(10, 100, 10, bf) == 0
 
 
 def test_attention_argument_checks_before_launch():

@@ -236,7 +236,35 @@ def _attn_bwd_dv_untransposed(Q, K, V, dO, causal=False, scale=None):
     return O.AttentionGrads(dQ=g.dQ, dK=g.dK, dV=P @ np.asarray(dO, dtype=np.float64))
 
 
+def _bf16_truncate(x):
+    # rounds toward zero instead of to nearest
+    x = np.asarray(x, dtype=np.float32)
+    return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def _bf16_ties_away(x):
+    # a tie goes away from zero instead of to the even neighbour
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x8000) & 0xFFFF0000).astype(np.uint32).view(np.float32).copy()
+    r[np.isnan(x)] = np.nan
+    return r
+
+
+def _bf16_ties_odd(x):
+    # a tie goes to the odd neighbour
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    odd = (u >> 16) & 1
+    r = ((u + 0x8000 - odd) & 0xFFFF0000).astype(np.uint32).view(np.float32).copy()
+    r[np.isnan(x)] = np.nan
+    return r
+
+
 MUTATIONS = {
+    "bf16_truncates": ("round_to_bf16", _bf16_truncate),
+    "bf16_ties_away_from_zero": ("round_to_bf16", _bf16_ties_away),
+    "bf16_ties_to_odd": ("round_to_bf16", _bf16_ties_odd),
     "attn_bwd_without_row_dot": ("attention_row_dot", _attn_bwd_no_rowdot),
     "attn_bwd_dk_unscaled": ("attention_backward", _attn_bwd_dk_unscaled),
     "attn_bwd_dv_untransposed": ("attention_backward", _attn_bwd_dv_untransposed),

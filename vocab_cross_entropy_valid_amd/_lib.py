@@ -31,7 +31,7 @@ LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
                   "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv",
-                  "dh_dw")
+                  "dh_dw", "cast")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""
@@ -51,6 +51,8 @@ SIGNATURES = {
                            _P, _P, _SZ, _P]),
     "lce_backward": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
                             _P, _P, _INT, _P, _SZ, _P]),
+    "lce_cast_bf16": (_INT, [_P, _P, _I64, _P]),
+    "lce_step_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT]),
     "lce_backward_step": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
                                  _P, _P, _P, _P, ctypes.POINTER(LceOptimizer), _P, _SZ, _P]),
     "lce_forward_shard": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _INT, _P, _P, _P,
@@ -117,6 +119,14 @@ def _check(status: int, what: str) -> None:
 
 def lce_workspace_bytes(N: int, d: int, V: int, dtype: int) -> int:
     return int(load().lce_workspace_bytes(N, d, V, dtype))
+
+
+def lce_cast_bf16(src, dst, n, stream) -> None:
+    _check(load().lce_cast_bf16(src, dst, n, stream), "lce_cast_bf16")
+
+
+def lce_step_workspace_bytes(N: int, d: int, V: int, dtype: int) -> int:
+    return int(load().lce_step_workspace_bytes(N, d, V, dtype))
 
 
 def lce_forward(H, W, labels, ignore_index, N, d, V, dtype, loss, lse, valid_idx,

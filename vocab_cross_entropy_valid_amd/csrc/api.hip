@@ -51,11 +51,18 @@ struct Plan {
   // backward
   int64_t C, Vs;
   int64_t ldG, ldGT, ldHT, ldWT;  // padded row strides (elements)
-  size_t off_G, off_GT, off_HT, off_WT, bwd_bytes;
+  size_t off_G, off_GT, off_HT, off_WT, off_D, bwd_bytes;
+  bool has_wt;  // W^T block: fp32 (no transposing LDS read) and the fused step
+  bool has_d;   // fp32 dW block accumulator: fused step over several token chunks
   size_t total;
 };
 
-Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype) {
+// step: the plan of lce_backward_step, which keeps dH on a W^T copy of each
+// vocabulary block (the block's rows of W are rewritten by the update while
+// dH tiles may still read them) and, when the rows span several token
+// chunks, sums a block's dW over the chunks in an fp32 [Vs][d] accumulator
+// before the update consumes it.
+Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype, bool step = false) {
   Plan p{};
   p.N = N;
   p.d = d;
@@ -86,7 +93,12 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype) {
   p.off_G = o; o += align_up((size_t)p.C * (size_t)p.ldG * p.esz);
   p.off_GT = o; o += align_up((size_t)p.Vs * (size_t)p.ldGT * p.esz);
   p.off_HT = o; o += align_up((size_t)d * (size_t)p.ldHT * p.esz);
-  p.off_WT = o; o += align_up((size_t)d * (size_t)p.ldWT * p.esz);
+  p.has_wt = dtype != LCE_BF16 || step;
+  p.has_d = step && N > p.C;
+  p.off_WT = o;
+  if (p.has_wt) o += align_up((size_t)d * (size_t)p.ldWT * p.esz);
+  p.off_D = o;
+  if (p.has_d) o += align_up((size_t)p.Vs * (size_t)d * sizeof(float));
   p.bwd_bytes = o;
   p.total = std::max(p.fwd_bytes, p.bwd_bytes);
   return p;
@@ -188,6 +200,11 @@ extern "C" {
 size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype) {
   if (check_sizes(N, d, V, dtype) != LCE_OK) return 0;
   return make_plan(N, d, V, dtype).total;
+}
+
+size_t lce_step_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype) {
+  if (check_sizes(N, d, V, dtype) != LCE_OK) return 0;
+  return make_plan(N, d, V, dtype, true).total;
 }
 
 }  // extern "C"
@@ -343,14 +360,15 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
                          const float* grad_out, int reduction, float* dH, int accumulate_dH,
                          float* dW, int accumulate_dW, void* workspace, size_t workspace_bytes,
                          hipStream_t s, const lce::DwArgs* step = nullptr) {
-  const Plan p = make_plan(N, d, V, dtype);
+  const Plan p = make_plan(N, d, V, dtype, step != nullptr);
   lce_status st = check_workspace(p, workspace, workspace_bytes);
   if (st != LCE_OK) return st;
   char* ws = (char*)workspace;
   void* G = ws + p.off_G;
   void* GT = ws + p.off_GT;
   void* HT = ws + p.off_HT;
-  void* WT = ws + p.off_WT;
+  void* WT = p.has_wt ? ws + p.off_WT : nullptr;
+  float* Dacc = p.has_d ? (float*)(ws + p.off_D) : nullptr;
 
   hipError_t e = hipSuccess;
   if (!accumulate_dH) {
@@ -364,9 +382,11 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
   // transposing LDS reads), so no W^T copy is built.  The optimizer step
   // rewrites W's rows in its dW epilogue while dH may still run (the merged
   // dH + dW launch), so it keeps dH on the copy; fp32 has no transposing read.
-  const bool w_direct = dtype == LCE_BF16 && step == nullptr;
-  // At least one chunk, so that dW is written even when N == 0.
-  for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
+  const bool w_direct = !p.has_wt;
+
+  // H^T of token chunk c0 (the chunk's gathered valid rows, transposed);
+  // skipped on the device when the chunk holds no valid row
+  auto transpose_h = [&](int64_t c0) -> hipError_t {
     lce::TransposeArgs th{};
     th.src = H;
     th.ld_src = d;
@@ -379,111 +399,143 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     th.K = d;
     th.active_count = c0 > 0 ? valid_count : nullptr;
     th.active_c0 = c0;
-    e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(th, dtype, s); });
+    return run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(th, dtype, s); });
+  };
+  // W^T of vocabulary block v0 (skipped when chunk c0 holds no valid row)
+  auto transpose_w = [&](int64_t v0, int64_t c0) -> hipError_t {
+    lce::TransposeArgs tw{};
+    tw.src = W;
+    tw.ld_src = d;
+    tw.gather = nullptr;
+    tw.row0 = v0;
+    tw.count = nullptr;
+    tw.nrows_static = V;
+    tw.dst = WT;
+    tw.ncols = p.Vs;
+    tw.ld_dst = p.ldWT;
+    tw.K = d;
+    tw.active_count = c0 > 0 ? valid_count : nullptr;
+    tw.active_c0 = c0;
+    return run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
+  };
+  // recompute + G, dH and dW of token chunk c0 x vocabulary block v0
+  auto block = [&](int64_t c0, int64_t v0) -> lce_status {
+    lce::BwdGArgs ga{};
+    ga.H = H;
+    ga.W = W;
+    ga.labels = labels;
+    ga.lse = lse;
+    ga.valid_idx = valid_idx;
+    ga.valid_count = valid_count;
+    ga.grad_out = grad_out;
+    ga.reduction = reduction;
+    ga.N = N;
+    ga.d = d;
+    ga.V = V;
+    ga.y_off = y_off;
+    ga.c0 = c0;
+    ga.C = p.C;
+    ga.v0 = v0;
+    ga.Vs = p.Vs;
+    ga.G = G;
+    ga.GT = GT;
+    ga.ldG = p.ldG;
+    ga.ldGT = p.ldGT;
+    hipError_t err = run(LCE_K_BWD_G, s, [&] { return lce::launch_bwd_g(ga, dtype, s); });
+    if (err != hipSuccess) return hip_fail(err, "recompute launch");
+
+    lce::DhArgs ha{};
+    ha.G = G;
+    ha.WT = WT;
+    ha.W = w_direct ? W : nullptr;
+    ha.ldG = p.ldG;
+    ha.ldWT = p.ldWT;
+    ha.C = p.C;
+    ha.Vs = p.Vs;
+    ha.d = d;
+    ha.valid_idx = valid_idx;
+    ha.valid_count = valid_count;
+    ha.c0 = c0;
+    ha.v0 = v0;
+    ha.V = V;
+    ha.dH = dH;
+    ha.beta = (v0 > 0 || accumulate_dH) ? 1 : 0;
+    lce::DwArgs wa{};
+    wa.GT = GT;
+    wa.HT = HT;
+    wa.ldGT = p.ldGT;
+    wa.ldHT = p.ldHT;
+    wa.C = p.C;
+    wa.Vs = p.Vs;
+    wa.d = d;
+    wa.valid_count = valid_count;
+    wa.c0 = c0;
+    wa.v0 = v0;
+    wa.V = V;
+    wa.dW = dW;
+    wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
+    if (step) {  // optimizer epilogue instead of the dW store
+      wa.opt_kind = step->opt_kind;
+      wa.lr = step->lr;
+      wa.wd = step->wd;
+      wa.beta1 = step->beta1;
+      wa.beta2 = step->beta2;
+      wa.eps = step->eps;
+      wa.bc1 = step->bc1;
+      wa.bc2s = step->bc2s;
+      wa.master = step->master;
+      wa.exp_avg = step->exp_avg;
+      wa.exp_avg_sq = step->exp_avg_sq;
+      wa.w16 = step->w16;
+      wa.acc = Dacc;
+    }
+    // dH first: right after the recompute the G block is still largely in
+    // the Infinity Cache (measured faster; dW's time does not depend on
+    // the order).  When even the chunk's largest dH tile grid (C / 256
+    // token tiles x d / 256 hidden tiles) cannot give every CU a tile, dH
+    // and dW share one launch, so that the short dW tiles run on the CUs
+    // the long dH tiles leave idle.
+    if ((p.C / 256) * ((d + 255) / 256) < grid_persistent()) {
+      err = run(LCE_K_DH_DW, s, [&] { return lce::launch_dh_dw(ha, wa, dtype, s); });
+      if (err != hipSuccess) return hip_fail(err, "dH + dW launch");
+    } else {
+      err = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
+      if (err != hipSuccess) return hip_fail(err, "dH launch");
+      err = run(LCE_K_DW, s, [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
+      if (err != hipSuccess) return hip_fail(err, "dW launch");
+    }
+    return LCE_OK;
+  };
+
+  if (!step) {
+    // Token chunks outside, vocabulary blocks inside: each chunk's H^T is
+    // built once.  At least one chunk, so that dW is written even when N == 0.
+    for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
+      e = transpose_h(c0);
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
+        if (!w_direct) {
+          e = transpose_w(v0, c0);
+          if (e != hipSuccess) return hip_fail(e, "transpose launch");
+        }
+        st = block(c0, v0);
+        if (st != LCE_OK) return st;
+      }
+    }
+    return LCE_OK;
+  }
+  // Fused update: vocabulary blocks outside, token chunks inside, so that a
+  // block's dW is complete (summed over every chunk in the accumulator) when
+  // the last chunk holding valid rows applies the update; the W^T copy of
+  // the block is taken before any chunk, and H^T is rebuilt per chunk.
+  for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
+    e = transpose_w(v0, 0);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
-    for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
-      if (!w_direct) {
-        lce::TransposeArgs tw{};
-        tw.src = W;
-        tw.ld_src = d;
-        tw.gather = nullptr;
-        tw.row0 = v0;
-        tw.count = nullptr;
-        tw.nrows_static = V;
-        tw.dst = WT;
-        tw.ncols = p.Vs;
-        tw.ld_dst = p.ldWT;
-        tw.K = d;
-        tw.active_count = c0 > 0 ? valid_count : nullptr;
-        tw.active_c0 = c0;
-        e = run(LCE_K_TRANSPOSE, s, [&] { return lce::launch_transpose(tw, dtype, s); });
-        if (e != hipSuccess) return hip_fail(e, "transpose launch");
-      }
-
-      lce::BwdGArgs ga{};
-      ga.H = H;
-      ga.W = W;
-      ga.labels = labels;
-      ga.lse = lse;
-      ga.valid_idx = valid_idx;
-      ga.valid_count = valid_count;
-      ga.grad_out = grad_out;
-      ga.reduction = reduction;
-      ga.N = N;
-      ga.d = d;
-      ga.V = V;
-      ga.y_off = y_off;
-      ga.c0 = c0;
-      ga.C = p.C;
-      ga.v0 = v0;
-      ga.Vs = p.Vs;
-      ga.G = G;
-      ga.GT = GT;
-      ga.ldG = p.ldG;
-      ga.ldGT = p.ldGT;
-      e = run(LCE_K_BWD_G, s, [&] { return lce::launch_bwd_g(ga, dtype, s); });
-      if (e != hipSuccess) return hip_fail(e, "recompute launch");
-
-      lce::DhArgs ha{};
-      ha.G = G;
-      ha.WT = WT;
-      ha.W = w_direct ? W : nullptr;
-      ha.ldG = p.ldG;
-      ha.ldWT = p.ldWT;
-      ha.C = p.C;
-      ha.Vs = p.Vs;
-      ha.d = d;
-      ha.valid_idx = valid_idx;
-      ha.valid_count = valid_count;
-      ha.c0 = c0;
-      ha.v0 = v0;
-      ha.V = V;
-      ha.dH = dH;
-      ha.beta = (v0 > 0 || accumulate_dH) ? 1 : 0;
-      lce::DwArgs wa{};
-      wa.GT = GT;
-      wa.HT = HT;
-      wa.ldGT = p.ldGT;
-      wa.ldHT = p.ldHT;
-      wa.C = p.C;
-      wa.Vs = p.Vs;
-      wa.d = d;
-      wa.valid_count = valid_count;
-      wa.c0 = c0;
-      wa.v0 = v0;
-      wa.V = V;
-      wa.dW = dW;
-      wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
-      if (step) {  // optimizer epilogue instead of the dW store
-        wa.opt_kind = step->opt_kind;
-        wa.lr = step->lr;
-        wa.wd = step->wd;
-        wa.beta1 = step->beta1;
-        wa.beta2 = step->beta2;
-        wa.eps = step->eps;
-        wa.bc1 = step->bc1;
-        wa.bc2s = step->bc2s;
-        wa.master = step->master;
-        wa.exp_avg = step->exp_avg;
-        wa.exp_avg_sq = step->exp_avg_sq;
-        wa.w16 = step->w16;
-      }
-      // dH first: right after the recompute the G block is still largely in
-      // the Infinity Cache (measured faster; dW's time does not depend on
-      // the order).  When even the chunk's largest dH tile grid (C / 256
-      // token tiles x d / 256 hidden tiles) cannot give every CU a tile, dH
-      // and dW share one launch, so that the short dW tiles run on the CUs
-      // the long dH tiles leave idle.
-      if ((p.C / 256) * ((d + 255) / 256) < grid_persistent()) {
-        e = run(LCE_K_DH_DW, s, [&] { return lce::launch_dh_dw(ha, wa, dtype, s); });
-        if (e != hipSuccess) return hip_fail(e, "dH + dW launch");
-      } else {
-        e = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
-        if (e != hipSuccess) return hip_fail(e, "dH launch");
-        e = run(LCE_K_DW, s,
-                [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
-        if (e != hipSuccess) return hip_fail(e, "dW launch");
-      }
+    for (int64_t c0 = 0; c0 == 0 || c0 < N; c0 += p.C) {
+      e = transpose_h(c0);
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      st = block(c0, v0);
+      if (st != LCE_OK) return st;
     }
   }
   return LCE_OK;
@@ -529,10 +581,6 @@ lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int6
     return fail(LCE_ERR_INVALID_ARG, "W, valid_count, grad_out and opt must not be NULL");
   if (N > 0 && (!H || !labels || !lse || !valid_idx || !dH))
     return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
-  // each dW tile must be complete in one launch: every valid row in one token chunk
-  if (N > kChunkMax)
-    return fail(LCE_ERR_UNSUPPORTED, "the fused update needs N <= " + std::to_string(kChunkMax) +
-                                         " (all rows in one token chunk)");
   if (dtype == LCE_BF16 && !W_master)
     return fail(LCE_ERR_INVALID_ARG, "bf16 weights need fp32 master weights (W_master)");
   if (!(opt->lr >= 0.f) || !(opt->weight_decay >= 0.f))
@@ -590,6 +638,23 @@ lce_status lce_backward_shard(const void* H, const void* W_shard, const int64_t*
   return backward_impl(H, W_shard, labels, ignore_index, lse, valid_idx, valid_count, N, d, V_total,
                        v_begin, V_shard, dtype, grad_out, reduction, dH, accumulate_dH ? 1 : 0,
                        dW_shard, accumulate_dW, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_cast_bf16(const float* src, void* dst, int64_t n, void* stream) {
+  g_err.clear();
+  if (n < 0) return fail(LCE_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return LCE_OK;
+  if (!src || !dst) return fail(LCE_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  const char* a = (const char*)src;
+  const char* b = (const char*)dst;
+  if (a < b + 2 * n && b < a + 4 * n) return fail(LCE_ERR_INVALID_ARG, "src and dst overlap");
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e =
+      run(LCE_K_CAST, s, [&] { return lce::launch_cast_bf16(src, (uint16_t*)dst, n, s); });
+  if (e != hipSuccess) return hip_fail(e, "cast launch");
+  return LCE_OK;
 }
 
 size_t lce_embed_workspace_bytes(int64_t N, int64_t d, int64_t V) {

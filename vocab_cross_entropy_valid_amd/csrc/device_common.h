@@ -163,15 +163,19 @@ __device__ __forceinline__ RowPtrs make_row_ptrs(const RowSource& s, int tid) {
   const int64_t first = s.gather ? 0 : s.row0;
   const int64_t rows = s.gather ? s.phys_rows : s.nrows - s.row0;
   rp.rsrc = make_rsrc(s.base + first * s.ld, rows * s.ld);
+  // Row numbers stay 32-bit (every size is below 2^31): as 64-bit values the
+  // compiler hoisted the four per-lane rows out of the persistent item loop
+  // and spilled them.
+  const int row0 = (int)s.row0;
+  const int last = (int)s.nrows - 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 8 * (8 * i + w) + (L >> 3);
     const int chunk = (L & 7) ^ lds_swz(row);
     const int lr = kPerm ? tok_of_lds_row(row) : row;
-    int64_t r = s.row0 + lr;
-    if (r >= s.nrows) r = s.nrows - 1;
-    const int64_t rel = s.gather ? (int64_t)s.gather[r] : r - s.row0;
-    rp.off[i] = (uint32_t)(rel * s.ld) + chunk * 16;
+    const int r = min(row0 + lr, last);
+    const int rel = s.gather ? s.gather[r] : r - row0;
+    rp.off[i] = (uint32_t)rel * (uint32_t)s.ld + chunk * 16;
   }
   rp.stride = kRowBytes;
   return rp;

@@ -73,6 +73,9 @@ struct DwArgs {
   float* exp_avg;     // fp32 [V, d] (AdamW)
   float* exp_avg_sq;  // fp32 [V, d] (AdamW)
   uint16_t* w16;      // bf16 [V, d] operand copy refreshed from master (nullable)
+  // fp32 [Vs][d] sum of the block's dW over the token chunks before the last
+  // one holding valid rows (nullable when every row lies in one chunk)
+  float* acc;
 };
 
 struct TransposeArgs {
@@ -107,6 +110,7 @@ hipError_t launch_loss_reduce(const float* loss, const int32_t* gather, const in
 hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_index, int64_t V,
                                float* dH, int64_t d, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
 // grid: persistent workgroups (a multiple of 8; each walks slots grid apart)

@@ -39,6 +39,38 @@ hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_
   return hipGetLastError();
 }
 
+// ---------------------------------------------- fp32 -> bf16 output cast
+//
+// The gradients leave the backward pass in fp32; a bf16 parameter takes them
+// rounded to nearest, ties to even (NaN stays NaN, overflow becomes inf).
+// HBM-bound: 8 values (32 bytes read, 16 written) per thread and step, the
+// pairs converted by the hardware packing conversion; the n % 8 tail values
+// are converted one by one by the first workgroup.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
+                                                        uint16_t* __restrict__ dst, int64_t n) {
+  const int64_t n8 = n / 8;
+  const f32x4* s4 = (const f32x4*)src;
+  u32x4* d4 = (u32x4*)dst;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * 256) {
+    const f32x4 a = __builtin_nontemporal_load(s4 + 2 * i);
+    const f32x4 b = __builtin_nontemporal_load(s4 + 2 * i + 1);
+    const u32x4 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                     pack_bf16x2(b[2], b[3])};
+    d4[i] = o;
+  }
+  const int64_t t = n8 * 8 + threadIdx.x;
+  if (blockIdx.x == 0 && t < n) dst[t] = (uint16_t)(pack_bf16x2(src[t], 0.f) & 0xffffu);
+}
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 8192));
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- transpose
 //
 // dst[k][i] = src[row(row0 + i)][k] for i < rows available, 0 for the rest of
@@ -439,7 +471,15 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   if (kact < 0) kact = 0;
   if (kact > a.C) kact = a.C;
   const int nstages = (int)((kact + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
-  if (nstages == 0 && a.accumulate) return;
+  if (kStep == 0 && nstages == 0 && a.accumulate) return;
+  // Fused update over token chunks: the first chunk starts the block's sum,
+  // a chunk that leaves valid rows for later chunks stores the running sum in
+  // acc, and the last chunk holding valid rows (chunk 0 when there is none:
+  // the update then sees g = 0) adds acc and applies the optimizer.  Chunks
+  // past the valid rows do nothing.
+  if (kStep != 0 && nstages == 0 && a.c0 > 0) return;
+  const bool first = a.c0 == 0;
+  const bool last = (int64_t)count <= a.c0 + a.C;
 
   RowSource as{(const char*)a.GT, a.ldGT * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.Vs, 0};
   RowSource bs{(const char*)a.HT, a.ldHT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
@@ -491,6 +531,29 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
     // (1 - b1) g, v = b2 v + (1 - b2) g^2, p -= (lr / bc1) m / (sqrt(v) / bc2s
     // + eps).  Batches of 16 values per lane keep the loads in flight together.
     const int64_t row0 = a.v0;
+    if (!last) {
+      // running sum of the block's dW over the chunks so far: acc (+)= tile
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const int n = n_base + 32 * nt;
+          float old[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+            const bool in = !first && ml < nv && n < a.d;
+            old[i] = in ? a.acc[(int64_t)ml * a.d + n] : 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
+            if (ml < nv && n < a.d) a.acc[(int64_t)ml * a.d + n] = old[i] + acc[mt][nt][i];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      return;
+    }
     constexpr int kB = kStep == 2 ? 8 : 16;  // values per lane in flight (AdamW holds three)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -499,7 +562,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 #pragma unroll
         for (int i0 = 0; i0 < 16; i0 += kB) {
           const int n = n_base + 32 * nt;
-          float p[kB], m[kB], v[kB];
+          float p[kB], m[kB], v[kB], g0[kB];
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
             const int i = i0 + b;
@@ -511,6 +574,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
               m[b] = in ? a.exp_avg[o] : 0.f;
               v[b] = in ? a.exp_avg_sq[o] : 0.f;
             }
+            g0[b] = (in && !first) ? a.acc[(int64_t)ml * a.d + n] : 0.f;
           }
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
@@ -518,7 +582,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
             const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
             if (ml >= nv || n >= a.d) continue;
             const int64_t o = (row0 + ml) * a.d + n;
-            const float g = acc[mt][nt][i];
+            const float g = g0[b] + acc[mt][nt][i];
             float q;
             if constexpr (kStep == 1) {
               q = p[b] - a.lr * (g + a.wd * p[b]);

@@ -277,29 +277,40 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int grid, hipStream_t s) {
 // go out in batches of 16, one memory round trip per batch instead of one
 // per chunk (the merge is latency-bound); the sum runs over the chunks in
 // order.
-__device__ __forceinline__ void merge_chunks(const FwdArgs& a, int64_t i, float& M, float& S) {
+// Offsets of the 16 chunks of a batch are 32-bit products b * Nb (Nb <
+// 2^25: the sizes check keeps N * d * element size below 4 GiB with d >= 64):
+// as 64-bit values they kept 16 scalar register pairs live and the SGPR
+// spills reserved a private stack frame.
+__device__ __forceinline__ void merge_chunks(const float* __restrict__ pm_base,
+                                             const float* __restrict__ ps_base, int J, int64_t Nb,
+                                             int64_t i, float& M, float& S) {
   constexpr int kB = 16;
+  const float* pmi = pm_base + i;
+  const float* psi = ps_base + i;
+  const uint32_t nb = (uint32_t)Nb;
   M = -INFINITY;
-  for (int c0 = 0; c0 < a.J; c0 += kB) {
+  for (int c0 = 0; c0 < J; c0 += kB) {
+    const float* q = pmi + (int64_t)c0 * Nb;
     float pm[kB];
 #pragma unroll
-    for (int b = 0; b < kB; ++b)
-      pm[b] = (c0 + b < a.J) ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
+    for (int b = 0; b < kB; ++b) pm[b] = (c0 + b < J) ? q[(uint64_t)(b * nb)] : -INFINITY;
 #pragma unroll
     for (int b = 0; b < kB; ++b) M = fmaxf(M, pm[b]);
   }
   S = 0.f;
-  for (int c0 = 0; c0 < a.J; c0 += kB) {
+  for (int c0 = 0; c0 < J; c0 += kB) {
+    const float* q = pmi + (int64_t)c0 * Nb;
+    const float* r = psi + (int64_t)c0 * Nb;
     float pm[kB], ps[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const bool in = c0 + b < a.J;
-      pm[b] = in ? a.pm[(int64_t)(c0 + b) * a.Nb + i] : -INFINITY;
-      ps[b] = in ? a.ps[(int64_t)(c0 + b) * a.Nb + i] : 0.f;
+      const bool in = c0 + b < J;
+      pm[b] = in ? q[(uint64_t)(b * nb)] : -INFINITY;
+      ps[b] = in ? r[(uint64_t)(b * nb)] : 0.f;
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b)
-      if (c0 + b < a.J) S += ps[b] * fast_exp2(pm[b] - M);
+      if (c0 + b < J) S += ps[b] * fast_exp2(pm[b] - M);
   }
 }
 
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, float* __rest
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
   float M, S;
-  merge_chunks(a, i, M, S);
+  merge_chunks(a.pm, a.ps, a.J, a.Nb, i, M, S);
   const int r = a.valid_idx[i];
   const int64_t yv = a.labels[r];
   const int cy = (int)(yv / kVocabTile) / a.tpc;
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(256) void fwd_part_kernel(FwdArgs a, float* __restr
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
   float M, S;
-  merge_chunks(a, i, M, S);
+  merge_chunks(a.pm, a.ps, a.J, a.Nb, i, M, S);
   const int r = a.valid_idx[i];
   const int64_t yl = a.labels[r] - a.y_off;
   float zt = -INFINITY;

@@ -49,8 +49,14 @@ def workspace_bytes(N: int, d: int, V: int, dtype: torch.dtype) -> int:
     return _lib.lce_workspace_bytes(N, d, V, _DTYPES[dtype])
 
 
-def alloc_workspace(N: int, d: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
-    n = workspace_bytes(N, d, V, dtype)
+def step_workspace_bytes(N: int, d: int, V: int, dtype: torch.dtype) -> int:
+    return _lib.lce_step_workspace_bytes(N, d, V, _DTYPES[dtype])
+
+
+def alloc_workspace(N: int, d: int, V: int, dtype: torch.dtype, device,
+                    step: bool = False) -> torch.Tensor:
+    """Workspace for lce_forward / lce_backward (step=True: also lce_backward_step)."""
+    n = (step_workspace_bytes if step else workspace_bytes)(N, d, V, dtype)
     if n == 0:
         raise ValueError(f"unsupported sizes N={N} d={d} V={V}")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -164,7 +170,7 @@ def backward_step(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, fwd: F
         grad_out = torch.ones(1, dtype=torch.float32, device=dev)
     grad_out = grad_out.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
     if workspace is None:
-        workspace = alloc_workspace(N, d, V, H.dtype, dev)
+        workspace = alloc_workspace(N, d, V, H.dtype, dev, step=True)
     if dH is None:
         dH = torch.empty(N, d, dtype=torch.float32, device=dev)
     opt = _lib.LceOptimizer(kind=kinds[kind], lr=lr, weight_decay=weight_decay,
@@ -325,6 +331,22 @@ def embed_backward(dX: torch.Tensor, input_ids: torch.Tensor, emb: EmbedOut, dW:
     return dW
 
 
+def cast_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lce_cast_bf16: a float32 GPU tensor rounded to bfloat16 (nearest, ties to even)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of x's shape")
+    _lib.lce_cast_bf16(_ptr(x), _ptr(out), x.numel(), _stream(x.device))
+    return out
+
+
+def _as_param_dtype(g: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    return cast_bf16(g) if dtype == torch.bfloat16 else g
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, W, labels, ignore_index, reduction, check):
@@ -342,8 +364,9 @@ class _LinearCrossEntropy(torch.autograd.Function):
         fwd = ForwardOut(None, lse, valid_idx, valid_count, None, None, None)
         dH, dW = backward(H, W, labels, fwd, grad_out=g, reduction=ctx.reduction,
                           ignore_index=ctx.ignore_index)
-        gH = dH.to(H.dtype) if ctx.needs_input_grad[0] else None
-        gW = dW.to(W.dtype) if ctx.needs_input_grad[1] else None
+        # bf16 parameters take the fp32 gradients through the library's cast kernel
+        gH = _as_param_dtype(dH, H.dtype) if ctx.needs_input_grad[0] else None
+        gW = _as_param_dtype(dW, W.dtype) if ctx.needs_input_grad[1] else None
         return gH, gW, None, None, None, None
 
 
@@ -354,7 +377,8 @@ def linear_cross_entropy(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
 
     Returns the reduced loss (a 0-d float32 tensor; NaN for "mean" when every
     label is ignored).  With return_aux=True also (per-token loss, lse,
-    valid_count).  Gradients flow to H and W (cast to their dtype).
+    valid_count).  Gradients flow to H and W (fp32, rounded to bf16 by the
+    library's cast kernel for bf16 parameters).
     """
     if reduction not in _RED:
         raise ValueError("reduction must be 'mean' or 'sum'")
