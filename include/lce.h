@@ -98,6 +98,24 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
                        float* loss_mean, int32_t* err_flag, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* lce_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs, kernels and
+ * results as lce_forward (bit for bit).  The forward's scratch (its
+ * per-vocabulary-chunk partials: (3 J + 1) * N' * 4 bytes with J <= 64
+ * vocabulary chunks and N' = N rounded up to 256) lives in a static 16 MiB
+ * device array inside the library, one per GPU, held until the process ends.
+ * Every V fits up to N = 21504 rows (fewer vocabulary chunks, V < 16129,
+ * allow more); larger sizes return LCE_ERR_UNSUPPORTED before any launch.
+ * Every call on one GPU uses that GPU's array: calls that overlap in time on
+ * one GPU (different streams or threads) race and must be serialised by the
+ * caller.  Calls no hipMalloc / hipFree. */
+lce_status lce_forward_noalloc(const void* H, const void* W, const int64_t* labels,
+                               int64_t ignore_index, int64_t N, int64_t d, int64_t V, int dtype,
+                               float* loss, float* lse, int32_t* valid_idx, int32_t* valid_count,
+                               double* loss_sum, float* loss_mean, int32_t* err_flag,
+                               void* stream);
+
 /* Backward pass: dH = dL/dH [N, d] f32 and dW = dL/dW [V, d] f32 for
  * L = mean (reduction LCE_MEAN) or sum (LCE_SUM) of loss over valid rows,
  * scaled by the upstream gradient *grad_out (a device f32 scalar).

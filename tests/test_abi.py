@@ -245,3 +245,22 @@ def test_attention_backward_argument_checks_before_launch():
     assert call(dq=None) == _lib.LCE_ERR_INVALID_ARG
     assert call(delta=None) == _lib.LCE_ERR_INVALID_ARG
     assert call(S=0, dq=None, delta=None) == 0
+
+
+def test_forward_noalloc_rejects_sizes_beyond_its_static_scratch():
+    """lce_forward_noalloc keeps the forward's partials in a 16 MiB static
+    device array: (3 J + 1) * round_up(N, 256) * 4 bytes with J <= 64
+    vocabulary chunks, so every V fits up to N = 21504 and N = 21505 with 64
+    chunks does not.  The check happens before anything is launched."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    for N, V in ((21505, 260000), (65536, 128256)):
+        r = lib.lce_forward_noalloc(fake, fake, fake, -100, N, 64, V, 1, fake, fake, fake, fake,
+                                    fake, None, fake, None)
+        assert r == _lib.LCE_ERR_UNSUPPORTED
+        assert "static scratch" in _lib.lce_last_error()
+    # the same argument checks as lce_forward
+    assert lib.lce_forward_noalloc(fake, None, fake, -100, 10, 64, 10, 1, fake, fake, fake, fake,
+                                   fake, None, fake, None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_forward_noalloc(fake, fake, fake, -100, 10, 100, 10, 1, fake, fake, fake, fake,
+                                   fake, None, fake, None) == _lib.LCE_ERR_UNSUPPORTED

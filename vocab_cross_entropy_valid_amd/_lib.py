@@ -49,6 +49,8 @@ SIGNATURES = {
     "lce_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT]),
     "lce_forward": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P,
                            _P, _P, _SZ, _P]),
+    "lce_forward_noalloc": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P,
+                                   _P, _P, _P]),
     "lce_backward": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _INT,
                             _P, _P, _INT, _P, _SZ, _P]),
     "lce_cast_bf16": (_INT, [_P, _P, _I64, _P]),
@@ -135,6 +137,13 @@ def lce_forward(H, W, labels, ignore_index, N, d, V, dtype, loss, lse, valid_idx
     _check(load().lce_forward(H, W, labels, ignore_index, N, d, V, dtype, loss, lse,
                               valid_idx, valid_count, loss_sum, loss_mean, err_flag,
                               workspace, workspace_bytes, stream), "lce_forward")
+
+
+def lce_forward_noalloc(H, W, labels, ignore_index, N, d, V, dtype, loss, lse, valid_idx,
+                        valid_count, loss_sum, loss_mean, err_flag, stream) -> None:
+    _check(load().lce_forward_noalloc(H, W, labels, ignore_index, N, d, V, dtype, loss, lse,
+                                      valid_idx, valid_count, loss_sum, loss_mean, err_flag,
+                                      stream), "lce_forward_noalloc")
 
 
 def lce_backward(H, W, labels, ignore_index, lse, valid_idx, valid_count, N, d, V, dtype,

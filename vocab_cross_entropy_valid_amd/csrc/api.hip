@@ -15,6 +15,20 @@
 #include "kernels.h"
 #include "lce.h"
 
+// -------------------------------------------- forward without a workspace
+//
+// Scratch of lce_forward_noalloc: the forward's per-chunk partials (running
+// max, sum and target logit of every vocabulary chunk, and the compact loss
+// vector) live in this file-scope device array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code the array's name is a host-side stand-in, not
+// a device address: each device's copy is resolved once, with that device
+// current, by hipGetSymbolAddress, and only that pointer is handed to the
+// kernels.  The forward writes every partial it later reads, so nothing has
+// to start at zero.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -221,8 +235,9 @@ lce_status forward_impl(bool shard, const void* H, const void* W, const int64_t*
                         int64_t V, int dtype, float* loss, float* lse, float* part_max, float* part_sum,
                         float* part_target, int32_t* valid_idx, int32_t* valid_count,
                         double* loss_sum, float* loss_mean, int32_t* err_flag, void* workspace,
-                        size_t workspace_bytes, hipStream_t s) {
-  const Plan p = make_plan(N, d, V, dtype);
+                        size_t workspace_bytes, hipStream_t s, bool forward_bytes_only = false) {
+  Plan p = make_plan(N, d, V, dtype);
+  if (forward_bytes_only) p.total = p.fwd_bytes;  // the caller's scratch serves the forward only
   lce_status st = check_workspace(p, workspace, workspace_bytes);
   if (st != LCE_OK) return st;
   char* ws = (char*)workspace;
@@ -269,6 +284,25 @@ lce_status forward_impl(bool shard, const void* H, const void* W, const int64_t*
   return LCE_OK;
 }
 
+lce_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+    if (!p) return fail(LCE_ERR_HIP, "hipGetSymbolAddress of the static scratch returned NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return LCE_OK;
+}
+
 lce_status check_shard(int64_t V_total, int64_t v_begin, int64_t V_shard) {
   if (V_total <= 0 || V_total >= ((int64_t)1 << 31))
     return fail(LCE_ERR_INVALID_ARG, "V_total must be in [1, 2^31)");
@@ -296,6 +330,32 @@ lce_status lce_forward(const void* H, const void* W, const int64_t* labels, int6
   return forward_impl(false, H, W, labels, ignore_index, N, d, V, 0, V, dtype, loss, lse, nullptr,
                       nullptr, nullptr, valid_idx, valid_count, loss_sum, loss_mean, err_flag,
                       workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+lce_status lce_forward_noalloc(const void* H, const void* W, const int64_t* labels,
+                               int64_t ignore_index, int64_t N, int64_t d, int64_t V, int dtype,
+                               float* loss, float* lse, int32_t* valid_idx, int32_t* valid_count,
+                               double* loss_sum, float* loss_mean, int32_t* err_flag,
+                               void* stream) {
+  g_err.clear();
+  lce_status st = check_sizes(N, d, V, dtype);
+  if (st != LCE_OK) return st;
+  if (!W || !valid_count || !loss_sum || !err_flag)
+    return fail(LCE_ERR_INVALID_ARG, "W, valid_count, loss_sum and err_flag must not be NULL");
+  if (N > 0 && (!H || !labels || !loss || !lse || !valid_idx))
+    return fail(LCE_ERR_INVALID_ARG, "H, labels, loss, lse and valid_idx must not be NULL");
+  const size_t need = make_plan(N, d, V, dtype).fwd_bytes;
+  if (need > kScratchBytes)
+    return fail(LCE_ERR_UNSUPPORTED,
+                "lce_forward_noalloc: these sizes need " + std::to_string(need) +
+                    " bytes of scratch and the static scratch holds " +
+                    std::to_string(kScratchBytes) + " (use lce_forward with a workspace)");
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != LCE_OK) return st;
+  return forward_impl(false, H, W, labels, ignore_index, N, d, V, 0, V, dtype, loss, lse, nullptr,
+                      nullptr, nullptr, valid_idx, valid_count, loss_sum, loss_mean, err_flag, ws,
+                      kScratchBytes, (hipStream_t)stream, true);
 }
 
 lce_status lce_forward_shard(const void* H, const void* W_shard, const int64_t* labels,
