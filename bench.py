@@ -44,7 +44,7 @@ KERNEL_FILE = {"compact": "kernels_fwd.hip", "fwd": "kernels_fwd.hip", "merge": 
                "dw": "kernels_bwd.hip", "gemm": "kernels_bwd.hip", "embed": "kernels_embed.hip",
                "attn": "kernels_attn.hip", "attn_dq": "kernels_attn.hip",
                "attn_dkv": "kernels_attn.hip", "dh_dw": "kernels_bwd.hip",
-               "cast": "kernels_bwd.hip"}
+               "cast": "kernels_bwd.hip", "mfma": "kernels_bwd.hip"}
 
 
 def _log(msg):
@@ -259,6 +259,36 @@ def bench_attention(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+def bench_mfma_probe(args) -> None:
+    """lce_mfma_peak: the bf16 MFMA rate with register operands and no memory
+    traffic (the chip's own ceiling for the matrix cores, to set the path's
+    kernels against; under a counter run it also gives the clock)."""
+    import torch
+
+    from vocab_cross_entropy_valid_amd import _lib
+    dev = torch.device("cuda:0")
+    n_out, iters = 1024 * 512, 20000
+    out = torch.empty(n_out, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        _lib.lce_mfma_peak(out.data_ptr(), n_out, iters, s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        _lib.lce_mfma_peak(out.data_ptr(), n_out, iters, s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 1024 * 8 * 4 * iters * 32768.0
+    tf = flops / (ms * 1e-3) / 1e12
+    assert bool(torch.isfinite(out).all())
+    print(json.dumps({"metric": "bf16 MFMA rate, register operands, no memory traffic",
+                      "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "ms_per_launch":
+                      round(ms, 3), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "peak": PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +314,9 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="measure online-softmax attention (batch 8 x 32 heads x 2048 x 128, "
                          "causal) instead of the loss path")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="measure the pure bf16 MFMA rate (register operands, no memory "
+                         "traffic) instead of the loss path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -294,6 +327,9 @@ def main():
 
     if args.attention:
         bench_attention(args)
+        return
+    if args.mfma_probe:
+        bench_mfma_probe(args)
         return
 
     import numpy as np

@@ -348,6 +348,16 @@ lce_status lce_attention_backward(const void* Q, const void* K, const void* V, c
 lce_status lce_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                        int dtype, void* stream);
 
+/* MFMA calibration: 1024 workgroups x 512 threads, each thread issuing
+ * 4 * iters bf16 32x32x16 MFMAs (32768 FLOPs each) on register operands with
+ * no memory traffic, then storing one float to out (device, >= 1024 * 512
+ * floats).  Total FLOPs = 1024 * 8 * 4 * iters * 32768.  The rate (and, under
+ * a counter run, the clock) the chip sustains when only the matrix cores
+ * work: the reference the path's kernels are measured against ("6GB显卡预训练
+ * 11亿参数模型", section 为什么是375天: time the hardware's matrix rate before
+ * judging the model's).  iters in [1, 2^24]. */
+lce_status lce_mfma_peak(float* out, int64_t n_out, int64_t iters, void* stream);
+
 /* Kernel classes for the optional timing registry. */
 typedef enum {
   LCE_K_COMPACT = 0,   /* valid-token compaction                         */
@@ -366,7 +376,8 @@ typedef enum {
   LCE_K_ATTN_DKV = 13, /* attention backward, dK / dV pass               */
   LCE_K_DH_DW = 14,    /* dH and dW of one vocabulary block, one launch   */
   LCE_K_CAST = 15,     /* fp32 -> bf16 output cast                        */
-  LCE_K_COUNT = 16
+  LCE_K_MFMA = 16,     /* lce_mfma_peak                                   */
+  LCE_K_COUNT = 17
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -264,3 +264,25 @@ def test_forward_noalloc_rejects_sizes_beyond_its_static_scratch():
                                    fake, None, fake, None) == _lib.LCE_ERR_INVALID_ARG
     assert lib.lce_forward_noalloc(fake, fake, fake, -100, 10, 100, 10, 1, fake, fake, fake, fake,
                                    fake, None, fake, None) == _lib.LCE_ERR_UNSUPPORTED
+
+
+def test_mfma_peak_argument_checks():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.lce_mfma_peak(None, 1 << 19, 10, None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_mfma_peak(fake, (1 << 19) - 1, 10, None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_mfma_peak(fake, 1 << 19, 0, None) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_mfma_peak(fake, 1 << 19, (1 << 24) + 1, None) == _lib.LCE_ERR_INVALID_ARG
+
+
+def test_embed_workspace_is_host_computable():
+    """The input side's workspace is sized on the host (no device query): a
+    positive size on a machine without a GPU, 0 only for unsupported sizes;
+    O(N + N d / 32): keys, segment lists, sort histograms, chunk partials."""
+    n3 = _lib.lce_embed_workspace_bytes(8192, 4096, 128256)
+    n5 = _lib.lce_embed_workspace_bytes(65536, 4096, 128256)
+    assert n3 > 0 and n5 > n3
+    assert n5 < 65536 * 64 + 65536 * 4096 * 4 // 32 + (1 << 20)
+    assert _lib.lce_embed_workspace_bytes(100, 100, 10) == 0      # d % 64 != 0
+    assert _lib.lce_embed_workspace_bytes(-1, 64, 10) == 0
+    assert _lib.lce_embed_workspace_bytes(0, 64, 300) > 0

@@ -31,7 +31,7 @@ LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
                   "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv",
-                  "dh_dw", "cast")
+                  "dh_dw", "cast", "mfma")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""
@@ -73,6 +73,7 @@ SIGNATURES = {
     "lce_status_string": (ctypes.c_char_p, [_INT]),
     "lce_last_error": (ctypes.c_char_p, []),
     "lce_gemm_nt": (_INT, [_P, _P, _P, _I64, _I64, _I64, _INT, _P]),
+    "lce_mfma_peak": (_INT, [_P, _I64, _I64, _P]),
     "lce_timing_enable": (_INT, [_INT]),
     "lce_timing_reset": (_INT, []),
     "lce_timing_query": (_INT, [_INT, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
@@ -231,6 +232,10 @@ def lce_last_error() -> str:
 
 def lce_gemm_nt(A, B, C, M, N, K, dtype, stream) -> None:
     _check(load().lce_gemm_nt(A, B, C, M, N, K, dtype, stream), "lce_gemm_nt")
+
+
+def lce_mfma_peak(out, n_out, iters, stream) -> None:
+    _check(load().lce_mfma_peak(out, n_out, iters, stream), "lce_mfma_peak")
 
 
 def lce_timing_enable(on: bool) -> None:

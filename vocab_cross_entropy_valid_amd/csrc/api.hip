@@ -534,7 +534,12 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     wa.V = V;
     wa.dW = dW;
     wa.accumulate = (c0 > 0 || accumulate_dW) ? 1 : 0;
-    if (step) {  // optimizer epilogue instead of the dW store
+    if (step && Dacc) {
+      // rows over several chunks: the plain store sums the block's dW over
+      // the chunks into the accumulator (addressed as rows v0.. of a dW table)
+      wa.dW = (float*)((uintptr_t)Dacc - (uintptr_t)(v0 * d * sizeof(float)));
+      wa.accumulate = c0 > 0 ? 1 : 0;
+    } else if (step) {  // one chunk: the optimizer epilogue instead of the dW store
       wa.opt_kind = step->opt_kind;
       wa.lr = step->lr;
       wa.wd = step->wd;
@@ -547,7 +552,6 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       wa.exp_avg = step->exp_avg;
       wa.exp_avg_sq = step->exp_avg_sq;
       wa.w16 = step->w16;
-      wa.acc = Dacc;
     }
     // dH first: right after the recompute the G block is still largely in
     // the Infinity Cache (measured faster; dW's time does not depend on
@@ -584,10 +588,12 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     }
     return LCE_OK;
   }
-  // Fused update: vocabulary blocks outside, token chunks inside, so that a
-  // block's dW is complete (summed over every chunk in the accumulator) when
-  // the last chunk holding valid rows applies the update; the W^T copy of
-  // the block is taken before any chunk, and H^T is rebuilt per chunk.
+  // Fused update: vocabulary blocks outside, token chunks inside.  With one
+  // token chunk (N <= C) the dW epilogue applies the update to each tile as
+  // it is produced.  Beyond that, a block's dW is summed over the chunks in
+  // the accumulator and the update is applied to the whole block after its
+  // last chunk.  The W^T copy of a block is taken before any chunk (dH keeps
+  // reading the old weights), and H^T is rebuilt per chunk.
   for (int64_t v0 = 0; v0 < V; v0 += p.Vs) {
     e = transpose_w(v0, 0);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
@@ -596,6 +602,16 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       if (e != hipSuccess) return hip_fail(e, "transpose launch");
       st = block(c0, v0);
       if (st != LCE_OK) return st;
+    }
+    if (Dacc) {
+      lce::DwArgs oa = *step;
+      oa.acc = Dacc;
+      oa.v0 = v0;
+      oa.Vs = p.Vs;
+      oa.V = V;
+      oa.d = d;
+      e = run(LCE_K_DW, s, [&] { return lce::launch_apply_opt(oa, s); });
+      if (e != hipSuccess) return hip_fail(e, "optimizer launch");
     }
   }
   return LCE_OK;
@@ -643,6 +659,13 @@ lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int6
     return fail(LCE_ERR_INVALID_ARG, "H, labels, lse, valid_idx and dH must not be NULL");
   if (dtype == LCE_BF16 && !W_master)
     return fail(LCE_ERR_INVALID_ARG, "bf16 weights need fp32 master weights (W_master)");
+  // the block update moves 16-byte vectors of the fp32 arrays and 8-byte
+  // vectors of a bf16 W
+  for (const void* q : {(const void*)W_master, (const void*)exp_avg, (const void*)exp_avg_sq})
+    if ((reinterpret_cast<uintptr_t>(q) & 15) != 0)
+      return fail(LCE_ERR_INVALID_ARG, "W_master, exp_avg and exp_avg_sq must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(W) & (dtype == LCE_BF16 ? 7 : 15)) != 0)
+    return fail(LCE_ERR_INVALID_ARG, "W must be 8-byte (bf16) or 16-byte (fp32) aligned");
   if (!(opt->lr >= 0.f) || !(opt->weight_decay >= 0.f))
     return fail(LCE_ERR_INVALID_ARG, "lr and weight_decay must be >= 0");
   lce::DwArgs step{};
@@ -719,8 +742,7 @@ lce_status lce_cast_bf16(const float* src, void* dst, int64_t n, void* stream) {
 
 size_t lce_embed_workspace_bytes(int64_t N, int64_t d, int64_t V) {
   if (check_sizes(N, d, V, LCE_F32) != LCE_OK) return 0;
-  const lce::EmbedPlan p = lce::make_embed_plan(N, d, V);
-  return p.sort_bytes ? p.total : 0;
+  return lce::make_embed_plan(N, d, V).total;
 }
 
 lce_status lce_embed_forward(const void* W, const int64_t* input_ids, int64_t pad_id, int64_t N,
@@ -757,7 +779,6 @@ lce_status lce_embed_backward(const float* dX, const int64_t* input_ids, const i
   if (N > 0 && (!dX || !input_ids || !valid_idx))
     return fail(LCE_ERR_INVALID_ARG, "dX, input_ids and valid_idx must not be NULL");
   const lce::EmbedPlan p = lce::make_embed_plan(N, d, V);
-  if (!p.sort_bytes) return fail(LCE_ERR_HIP, "sort workspace query failed");
   if (workspace_bytes < p.total)
     return fail(LCE_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
                                        " bytes is smaller than the required " +
@@ -887,6 +908,21 @@ lce_status lce_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = run(LCE_K_GEMM, s, [&] { return lce::launch_gemm_nt(A, B, C, M, N, K, dtype, s); });
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return LCE_OK;
+}
+
+lce_status lce_mfma_peak(float* out, int64_t n_out, int64_t iters, void* stream) {
+  g_err.clear();
+  constexpr int64_t kBlocks = 1024, kThreadsPer = 512;
+  if (!out) return fail(LCE_ERR_INVALID_ARG, "out must not be NULL");
+  if (n_out < kBlocks * kThreadsPer)
+    return fail(LCE_ERR_INVALID_ARG, "out must hold 1024 * 512 floats");
+  if (iters < 1 || iters > ((int64_t)1 << 24))
+    return fail(LCE_ERR_INVALID_ARG, "iters must be in [1, 2^24]");
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e =
+      run(LCE_K_MFMA, s, [&] { return lce::launch_mfma_peak(out, (int)kBlocks, iters, s); });
+  if (e != hipSuccess) return hip_fail(e, "mfma calibration launch");
   return LCE_OK;
 }
 

@@ -73,8 +73,8 @@ struct DwArgs {
   float* exp_avg;     // fp32 [V, d] (AdamW)
   float* exp_avg_sq;  // fp32 [V, d] (AdamW)
   uint16_t* w16;      // bf16 [V, d] operand copy refreshed from master (nullable)
-  // fp32 [Vs][d] sum of the block's dW over the token chunks before the last
-  // one holding valid rows (nullable when every row lies in one chunk)
+  // apply_opt_kernel only: fp32 [Vs][d] sum of the block's dW over the token
+  // chunks (the plain store writes it when the rows span several chunks)
   float* acc;
 };
 
@@ -119,12 +119,15 @@ hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s);
 // (long K), then one workgroup per dW tile, dispatched onto the CUs the dH
 // tiles leave free.  For chunks whose dH tile grid cannot fill the GPU.
 hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s);
+// The optimizer over block [v0, v0 + nv) from the summed gradient in a.acc.
+hipError_t launch_apply_opt(const DwArgs& a, hipStream_t s);
 // Workspace layout of the embedding backward (byte offsets, 256-aligned).
 struct EmbedPlan {
   int end_bit;  // sort key bits: 2^end_bit > V (V itself is the padding sentinel)
+  int passes;   // radix passes of 9 bits
+  int nblocks;  // sort tiles of 2048 pairs
   size_t off_key, off_val, off_key_s, off_val_s, off_seg_start, off_seg_chunk0, off_seg_part0;
-  size_t off_chunk_seg, off_meta, off_sort, off_part;
-  size_t sort_bytes;
+  size_t off_chunk_seg, off_meta, off_hist, off_part;
   int64_t max_chunks, max_parts;
   size_t total;
 };
@@ -137,6 +140,9 @@ hipError_t launch_embed_backward(const EmbedPlan& p, const float* dX, const int6
                                  int grid, hipStream_t s);
 hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                           int dtype, hipStream_t s);
+// blocks workgroups of 512 threads, each thread 4 * iters bf16 32x32x16 MFMAs;
+// out holds blocks * 512 floats
+hipError_t launch_mfma_peak(float* out, int blocks, int64_t iters, hipStream_t s);
 
 
 // Online-softmax attention forward over [B*H, S, D] bf16 Q, K, V.

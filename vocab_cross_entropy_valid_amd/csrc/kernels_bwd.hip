@@ -450,7 +450,13 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
 // (rows = hidden units from H^T, columns = vocabulary entries from G^T): a
 // lane then holds four consecutive hidden units of one dW row and writes
 // them as one 16-byte vector (2% faster than four 4-byte stores on the
-// Llama-3 head).  The optimizer epilogues keep rows = vocabulary entries.
+// Llama-3 head).  The optimizer epilogue keeps rows = vocabulary entries, so
+// that each of its load / store instructions covers two whole 128-byte rows
+// of the weights and moments (with the dW^T layout, 32-byte pieces of 32 rows
+// per instruction made the AdamW epilogue 26% slower on the Llama-3 head).
+// It applies the update from the tile itself, so it serves the case where
+// every valid row lies in one token chunk; otherwise the plain store sums the
+// chunks into the block accumulator and apply_opt_kernel updates the block.
 template <typename T, int kStep>  // 0: store dW; 1: SGD; 2: AdamW
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
@@ -471,15 +477,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   if (kact < 0) kact = 0;
   if (kact > a.C) kact = a.C;
   const int nstages = (int)((kact + Elem<T>::kPerStage - 1) / Elem<T>::kPerStage);
-  if (kStep == 0 && nstages == 0 && a.accumulate) return;
-  // Fused update over token chunks: the first chunk starts the block's sum,
-  // a chunk that leaves valid rows for later chunks stores the running sum in
-  // acc, and the last chunk holding valid rows (chunk 0 when there is none:
-  // the update then sees g = 0) adds acc and applies the optimizer.  Chunks
-  // past the valid rows do nothing.
-  if (kStep != 0 && nstages == 0 && a.c0 > 0) return;
-  const bool first = a.c0 == 0;
-  const bool last = (int64_t)count <= a.c0 + a.C;
+  if (nstages == 0 && a.accumulate) return;
 
   RowSource as{(const char*)a.GT, a.ldGT * Elem<T>::kSize, nullptr, (int64_t)tm * kTile, a.Vs, 0};
   RowSource bs{(const char*)a.HT, a.ldHT * Elem<T>::kSize, nullptr, (int64_t)tn * kTile, a.d, 0};
@@ -531,30 +529,9 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
     // (1 - b1) g, v = b2 v + (1 - b2) g^2, p -= (lr / bc1) m / (sqrt(v) / bc2s
     // + eps).  Batches of 16 values per lane keep the loads in flight together.
     const int64_t row0 = a.v0;
-    if (!last) {
-      // running sum of the block's dW over the chunks so far: acc (+)= tile
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int n = n_base + 32 * nt;
-          float old[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-            const bool in = !first && ml < nv && n < a.d;
-            old[i] = in ? a.acc[(int64_t)ml * a.d + n] : 0.f;
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-            if (ml < nv && n < a.d) a.acc[(int64_t)ml * a.d + n] = old[i] + acc[mt][nt][i];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      return;
-    }
-    constexpr int kB = kStep == 2 ? 8 : 16;  // values per lane in flight (AdamW holds three)
+    // values per lane in flight (AdamW holds three arrays; 16 fp32 values
+    // for SGD spilled)
+    constexpr int kB = (kStep == 2 || sizeof(T) == 4) ? 8 : 16;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -562,7 +539,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
 #pragma unroll
         for (int i0 = 0; i0 < 16; i0 += kB) {
           const int n = n_base + 32 * nt;
-          float p[kB], m[kB], v[kB], g0[kB];
+          float p[kB], m[kB], v[kB];
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
             const int i = i0 + b;
@@ -574,7 +551,6 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
               m[b] = in ? a.exp_avg[o] : 0.f;
               v[b] = in ? a.exp_avg_sq[o] : 0.f;
             }
-            g0[b] = (in && !first) ? a.acc[(int64_t)ml * a.d + n] : 0.f;
           }
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
@@ -582,7 +558,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
             const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
             if (ml >= nv || n >= a.d) continue;
             const int64_t o = (row0 + ml) * a.d + n;
-            const float g = g0[b] + acc[mt][nt][i];
+            const float g = acc[mt][nt][i];
             float q;
             if constexpr (kStep == 1) {
               q = p[b] - a.lr * (g + a.wd * p[b]);
@@ -600,6 +576,66 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
           __builtin_amdgcn_sched_barrier(0);
         }
   }
+}
+
+// ------------------------------------------- optimizer over a whole block
+//
+// When the valid rows span several token chunks, the plain dW store sums the
+// block's gradient over the chunks in the fp32 accumulator acc ([Vs][d],
+// row-major), and this kernel then applies the update to the block's rows
+// [v0, v0 + nv): the same formulas as the fused epilogue, one thread per
+// four consecutive values (16-byte vectors), grid-stride.  No dW table
+// beyond the one block is ever held.
+template <int kOpt>
+__global__ __launch_bounds__(256) void apply_opt_kernel(DwArgs a) {
+  const int64_t nv = min(a.Vs, a.V - a.v0);
+  const int64_t n4 = nv * a.d / 4;
+  const int64_t base = a.v0 * a.d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t o = base + 4 * i;
+    const f32x4 g = ((const f32x4*)a.acc)[i];
+    const f32x4 p = *(const f32x4*)(a.master + o);
+    f32x4 m, v, q;
+    if constexpr (kOpt == 2) {
+      m = *(const f32x4*)(a.exp_avg + o);
+      v = *(const f32x4*)(a.exp_avg_sq + o);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (kOpt == 1) {
+        q[e] = p[e] - a.lr * (g[e] + a.wd * p[e]);
+      } else {
+        const float pd = p[e] * (1.f - a.lr * a.wd);
+        m[e] = a.beta1 * m[e] + (1.f - a.beta1) * g[e];
+        v[e] = a.beta2 * v[e] + (1.f - a.beta2) * g[e] * g[e];
+        q[e] = pd - (a.lr / a.bc1) * m[e] / (__builtin_sqrtf(v[e]) / a.bc2s + a.eps);
+      }
+    }
+    *(f32x4*)(a.master + o) = q;
+    if constexpr (kOpt == 2) {
+      *(f32x4*)(a.exp_avg + o) = m;
+      *(f32x4*)(a.exp_avg_sq + o) = v;
+    }
+    if (a.w16) {
+      u32x2 w;
+      w[0] = bf16_bits(q[0]) | (bf16_bits(q[1]) << 16);
+      w[1] = bf16_bits(q[2]) | (bf16_bits(q[3]) << 16);
+      *(u32x2*)(a.w16 + o) = w;
+    }
+  }
+}
+
+hipError_t launch_apply_opt(const DwArgs& a, hipStream_t s) {
+  const int64_t nv = std::min<int64_t>(a.Vs, a.V - a.v0);
+  const int64_t n4 = nv * a.d / 4;
+  if (n4 <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
+  if (a.opt_kind == 1)
+    hipLaunchKernelGGL(apply_opt_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(apply_opt_kernel<2>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ launches
@@ -663,7 +699,7 @@ hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s) {
 
 // Slots for the dW tiles of one vocabulary block: 4 x 8 blocks of tiles per
 // XCD, over (hidden, vocabulary) tiles for the plain store and over
-// (vocabulary, hidden) tiles for the optimizer epilogues (as dw_tile maps them).
+// (vocabulary, hidden) tiles for the optimizer epilogue (as dw_tile maps them).
 int dw_slots(const DwArgs& a) {
   const int TV = (int)((a.Vs + kTile - 1) / kTile), TD = (int)((a.d + kTile - 1) / kTile);
   const int TM = a.opt_kind == 0 ? TD : TV, TN = a.opt_kind == 0 ? TV : TD;
@@ -758,6 +794,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(const void* A, con
         if (n < N) C[m * N + n] = acc[mt][nt][i];
       }
     }
+}
+
+// ----------------------------------------------------- MFMA calibration
+//
+// The matrix cores alone: four independent chains of the bf16 32x32x16 MFMA
+// on register operands, no memory traffic inside the loop.  It gives the
+// MFMA rate (and, under a counter run, the clock) the chip sustains when
+// only the matrix cores work, the reference the fused kernels are held
+// against.  Each thread stores one float (so the loop is not removed).
+__global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float* __restrict__ out,
+                                                             int64_t iters) {
+  u32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = 0x3c003c00u + (uint32_t)i + ((threadIdx.x & 7) << 4);  // small finite bf16 values
+    b[i] = 0x3c003c00u - (uint32_t)i;
+  }
+  f32x16 c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[j][i] = 0.f;
+  for (int64_t it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Mma<bf16_t>::run(c[j], a, b);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[j][i];
+  out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = sum;
+}
+
+hipError_t launch_mfma_peak(float* out, int blocks, int64_t iters, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(kThreads), 0, s, out, iters);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,

@@ -9,7 +9,10 @@
 // is dW[v] += sum of dX[n] over valid n with id[n] = v; rows sharing an id
 // are summed in a fixed order (ascending position inside fixed 64-row
 // chunks, then the chunks in order) so the result is bitwise reproducible.
-#include <rocprim/device/device_radix_sort.hpp>
+// The rows are grouped by id with a stable least-significant-digit radix
+// sort written here (8-bit digits, wave ballots for the ranks of equal
+// digits), so the whole pass is this file's kernels.
+#include <algorithm>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -66,6 +69,117 @@ __global__ __launch_bounds__(256) void embed_keys_kernel(const int64_t* __restri
   } else {
     key[i] = (uint32_t)V;
     val[i] = 0;
+  }
+}
+
+// ---------------------------------------------- backward: radix sort
+//
+// Stable sort of (key, value) pairs by key, least significant 9-bit digit
+// first (two passes cover every vocabulary below 2^18).  A pass over n pairs
+// runs two kernels:
+//   hist     block b counts the digits of its tile of kSortTile pairs (LDS
+//            integer atomics: exact counts, order-free) into
+//            hist[digit * nblocks + b];
+//   scatter  block b first derives where its run of each digit starts in the
+//            output (the pairs of smaller digits, plus those of the same
+//            digit in earlier tiles), then walks its tile in order, 1024
+//            pairs at a time: a lane's rank among the lanes of its wave with
+//            the same digit comes from nine ballots (one per digit bit) and a
+//            popcount, the waves' digit counts are scanned in wave order, and
+//            the pair lands after every pair of that digit already placed by
+//            earlier rows, waves and lanes.
+// Equal keys keep their input order (tiles, rows, waves and lanes are all
+// taken in ascending input position), which is what makes the sort stable
+// and the later sums bitwise reproducible.
+constexpr int kSortThreads = 1024;
+constexpr int kSortTile = 2048;  // pairs per block and pass: 2 rows of 1024
+constexpr int kRadixBits = 9;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortWaves = kSortThreads / 64;
+
+__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const uint32_t* __restrict__ key,
+                                                                  int64_t n, int shift,
+                                                                  int32_t* __restrict__ hist,
+                                                                  int nblocks) {
+  __shared__ int h[kRadix];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if (tid < kRadix) h[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSortTile / kSortThreads; ++r) {
+    const int64_t i = (int64_t)b * kSortTile + r * kSortThreads + tid;
+    if (i < n) atomicAdd(&h[(key[i] >> shift) & (kRadix - 1)], 1);
+  }
+  __syncthreads();
+  if (tid < kRadix) hist[(int64_t)tid * nblocks + b] = h[tid];
+}
+
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int* wbase, int& total);
+
+__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
+    const uint32_t* __restrict__ key_in, const int32_t* __restrict__ val_in,
+    uint32_t* __restrict__ key_out, int32_t* __restrict__ val_out, int64_t n, int shift,
+    const int32_t* __restrict__ hist, int nblocks) {
+  __shared__ int cnt[kSortWaves][kRadix];  // per wave: pairs of each digit in this row
+  __shared__ int run[kRadix];              // next output slot of each digit
+  __shared__ int wtot[16];
+  __shared__ int wbase[17];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.x;
+  // output start of this block's run of digit tid: every pair of a smaller
+  // digit (exclusive scan of the digit totals) plus the pairs of the same
+  // digit in earlier tiles
+  int total = 0, before = 0;
+  if (tid < kRadix)
+    for (int q = 0; q < nblocks; ++q) {
+      const int c = hist[(int64_t)tid * nblocks + q];
+      total += c;
+      before += q < b ? c : 0;
+    }
+  int all;
+  const int start = wg_exclusive_scan(tid < kRadix ? total : 0, wtot, wbase, all);
+  if (tid < kRadix) run[tid] = start + before;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
+#pragma unroll 1
+  for (int r = 0; r < kSortTile / kSortThreads; ++r) {
+    const int64_t i = (int64_t)b * kSortTile + r * kSortThreads + tid;
+    const bool valid = i < n;
+    const uint32_t k = valid ? key_in[i] : 0u;
+    const int32_t v = valid ? val_in[i] : 0;
+    const int d = (int)((k >> shift) & (kRadix - 1));
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < kRadixBits; ++bit) {
+      const uint64_t m = __ballot((d >> bit) & 1);
+      peers &= ((d >> bit) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+#pragma unroll
+    for (int q = 0; q < kSortWaves * kRadix / kSortThreads; ++q)
+      (&cnt[0][0])[q * kSortThreads + tid] = 0;
+    __syncthreads();
+    if (valid && rank == 0) cnt[wave][d] = __popcll(peers);  // the group's first lane
+    __syncthreads();
+    if (tid < kRadix) {  // digit tid: exclusive scan over the waves, in order
+      int acc = run[tid];
+#pragma unroll
+      for (int w = 0; w < kSortWaves; ++w) {
+        const int c = cnt[w][tid];
+        cnt[w][tid] = acc;
+        acc += c;
+      }
+      run[tid] = acc;
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = cnt[wave][d] + rank;
+      key_out[pos] = k;
+      val_out[pos] = v;
+    }
+    __syncthreads();
   }
 }
 
@@ -223,12 +337,8 @@ EmbedPlan make_embed_plan(int64_t N, int64_t d, int64_t V) {
   const size_t n = (size_t)std::max<int64_t>(N, 1);
   p.end_bit = 1;
   while (p.end_bit < 32 && ((uint64_t)1 << p.end_bit) <= (uint64_t)V) ++p.end_bit;
-  size_t sort_bytes = 0;
-  // size query only (no launch); it needs a device, and reports 0 without one
-  if (rocprim::radix_sort_pairs(nullptr, sort_bytes, (uint32_t*)nullptr, (uint32_t*)nullptr,
-                                (int32_t*)nullptr, (int32_t*)nullptr, (unsigned)n, 0,
-                                (unsigned)p.end_bit, (hipStream_t)0) != hipSuccess)
-    sort_bytes = 0;
+  p.passes = (p.end_bit + kRadixBits - 1) / kRadixBits;
+  p.nblocks = (int)((n + kSortTile - 1) / kSortTile);
   size_t o = 0;
   p.off_key = o; o += al(n * 4);
   p.off_val = o; o += al(n * 4);
@@ -241,8 +351,7 @@ EmbedPlan make_embed_plan(int64_t N, int64_t d, int64_t V) {
   p.max_chunks = (int64_t)n / kChunkRows + (int64_t)n;
   p.off_chunk_seg = o; o += al((size_t)p.max_chunks * 4);
   p.off_meta = o; o += al(16);
-  p.off_sort = o; o += al(sort_bytes);
-  p.sort_bytes = sort_bytes;
+  p.off_hist = o; o += al((size_t)kRadix * p.nblocks * 4);
   // partial slots: only segments longer than one chunk, at most 2 count / 64
   p.max_parts = 2 * (int64_t)n / kChunkRows + 1;
   p.off_part = o; o += al((size_t)p.max_parts * (size_t)d * 4);
@@ -273,14 +382,26 @@ hipError_t launch_embed_backward(const EmbedPlan& p, const float* dX, const int6
     if (e != hipSuccess) return e;
   }
   if (N <= 0) return hipSuccess;
+  // The keys start in the buffer pair that makes the last pass land in
+  // (key_s, val_s): each pass moves them to the other pair.
+  uint32_t* kbuf[2] = {key, key_s};
+  int32_t* vbuf[2] = {val, val_s};
+  int cur = (p.passes % 2 == 0) ? 1 : 0;
   hipLaunchKernelGGL(embed_keys_kernel, dim3((int)((N + 255) / 256)), dim3(256), 0, s, ids,
-                     valid_idx, valid_count, N, V, key, val);
+                     valid_idx, valid_count, N, V, kbuf[cur], vbuf[cur]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  size_t sb = p.sort_bytes;
-  e = rocprim::radix_sort_pairs(w + p.off_sort, sb, key, key_s, val, val_s, (unsigned)N, 0,
-                                (unsigned)p.end_bit, s);
-  if (e != hipSuccess) return e;
+  int32_t* hist = (int32_t*)(w + p.off_hist);
+  for (int pass = 0; pass < p.passes; ++pass) {
+    const int shift = kRadixBits * pass;
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(p.nblocks), dim3(kSortThreads), 0, s, kbuf[cur], N,
+                       shift, hist, p.nblocks);
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3(p.nblocks), dim3(kSortThreads), 0, s, kbuf[cur],
+                       vbuf[cur], kbuf[1 - cur], vbuf[1 - cur], N, shift, hist, p.nblocks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cur = 1 - cur;
+  }
   hipLaunchKernelGGL(embed_segments_kernel, dim3(1), dim3(1024), 0, s, key_s, valid_count,
                      seg_start, seg_chunk0, seg_part0, chunk_seg, meta);
   e = hipGetLastError();
