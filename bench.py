@@ -44,7 +44,7 @@ KERNEL_FILE = {"compact": "kernels_fwd.hip", "fwd": "kernels_fwd.hip", "merge": 
                "dw": "kernels_bwd.hip", "gemm": "kernels_bwd.hip", "embed": "kernels_embed.hip",
                "attn": "kernels_attn.hip", "attn_dq": "kernels_attn.hip",
                "attn_dkv": "kernels_attn.hip", "dh_dw": "kernels_bwd.hip",
-               "cast": "kernels_bwd.hip", "mfma": "kernels_bwd.hip"}
+               "cast": "kernels_bwd.hip", "mfma": "kernels_bwd.hip", "opt": "kernels_bwd.hip"}
 
 
 def _log(msg):

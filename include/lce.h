@@ -367,8 +367,8 @@ typedef enum {
   LCE_K_ZERO = 4,      /* zeroing dH rows of ignored tokens              */
   LCE_K_TRANSPOSE = 5, /* W / H^T operand layout for backward            */
   LCE_K_BWD_G = 6,     /* logit recompute + G tile                       */
-  LCE_K_DH = 7,        /* dH += G W                                      */
-  LCE_K_DW = 8,        /* dW += G^T H                                    */
+  LCE_K_DH = 7,        /* not launched: dH runs in LCE_K_DH_DW           */
+  LCE_K_DW = 8,        /* not launched: dW runs in LCE_K_DH_DW           */
   LCE_K_GEMM = 9,      /* lce_gemm_nt                                    */
   LCE_K_EMBED = 10,    /* embedding gather / gradient scatter-sum        */
   LCE_K_ATTN = 11,     /* online-softmax attention forward               */
@@ -377,7 +377,9 @@ typedef enum {
   LCE_K_DH_DW = 14,    /* dH and dW of one vocabulary block, one launch   */
   LCE_K_CAST = 15,     /* fp32 -> bf16 output cast                        */
   LCE_K_MFMA = 16,     /* lce_mfma_peak                                   */
-  LCE_K_COUNT = 17
+  LCE_K_OPT = 17,      /* optimizer update of a vocabulary block (the fused
+                          step beyond one token chunk)                     */
+  LCE_K_COUNT = 18
 } lce_kernel_class;
 
 /* When enabled, every launch is bracketed by HIP events recorded on the

@@ -31,7 +31,7 @@ LCE_SUM = 1
 
 KERNEL_CLASSES = ("compact", "fwd", "merge", "reduce", "zero", "transpose",
                   "bwd_g", "dh", "dw", "gemm", "embed", "attn", "attn_dq", "attn_dkv",
-                  "dh_dw", "cast", "mfma")
+                  "dh_dw", "cast", "mfma", "opt")
 
 class LceOptimizer(ctypes.Structure):
     """lce_optimizer of include/lce.h."""

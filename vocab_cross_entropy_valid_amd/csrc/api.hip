@@ -553,21 +553,11 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       wa.exp_avg_sq = step->exp_avg_sq;
       wa.w16 = step->w16;
     }
-    // dH first: right after the recompute the G block is still largely in
-    // the Infinity Cache (measured faster; dW's time does not depend on
-    // the order).  When even the chunk's largest dH tile grid (C / 256
-    // token tiles x d / 256 hidden tiles) cannot give every CU a tile, dH
-    // and dW share one launch, so that the short dW tiles run on the CUs
-    // the long dH tiles leave idle.
-    if ((p.C / 256) * ((d + 255) / 256) < grid_persistent()) {
-      err = run(LCE_K_DH_DW, s, [&] { return lce::launch_dh_dw(ha, wa, dtype, s); });
-      if (err != hipSuccess) return hip_fail(err, "dH + dW launch");
-    } else {
-      err = run(LCE_K_DH, s, [&] { return lce::launch_dh(ha, dtype, s); });
-      if (err != hipSuccess) return hip_fail(err, "dH launch");
-      err = run(LCE_K_DW, s, [&] { return lce::launch_dw(wa, dtype, grid_persistent(), s); });
-      if (err != hipSuccess) return hip_fail(err, "dW launch");
-    }
+    // dH and dW share one launch: the dH tiles (long K) are dispatched first,
+    // right after the recompute while the G block is still largely in the
+    // Infinity Cache, and the short dW tiles fill the CUs they leave idle
+    err = run(LCE_K_DH_DW, s, [&] { return lce::launch_dh_dw(ha, wa, dtype, s); });
+    if (err != hipSuccess) return hip_fail(err, "dH + dW launch");
     return LCE_OK;
   };
 
@@ -610,7 +600,7 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
       oa.Vs = p.Vs;
       oa.V = V;
       oa.d = d;
-      e = run(LCE_K_DW, s, [&] { return lce::launch_apply_opt(oa, s); });
+      e = run(LCE_K_OPT, s, [&] { return lce::launch_apply_opt(oa, s); });
       if (e != hipSuccess) return hip_fail(e, "optimizer launch");
     }
   }

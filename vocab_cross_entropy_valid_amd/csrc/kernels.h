@@ -112,12 +112,9 @@ hipError_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t ignore_
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_g(BwdGArgs a, int dtype, hipStream_t s);
-hipError_t launch_dh(const DhArgs& a, int dtype, hipStream_t s);
-// grid: persistent workgroups (a multiple of 8; each walks slots grid apart)
-hipError_t launch_dw(DwArgs a, int dtype, int grid, hipStream_t s);
 // dH and dW of one vocabulary block in a single launch: the dH tiles first
 // (long K), then one workgroup per dW tile, dispatched onto the CUs the dH
-// tiles leave free.  For chunks whose dH tile grid cannot fill the GPU.
+// tiles leave free.
 hipError_t launch_dh_dw(const DhArgs& ha, DwArgs wa, int dtype, hipStream_t s);
 // The optimizer over block [v0, v0 + nv) from the summed gradient in a.acc.
 hipError_t launch_apply_opt(const DwArgs& a, hipStream_t s);
