@@ -159,6 +159,8 @@ BWD_CASES = [
     (1, 3, 512, 128, True, 625),     # several key groups of 128, diagonal skips
     (1, 2, 40, 64, False, 628),      # two query blocks: the pipeline's shortest loop
     (2, 1, 96, 128, True, 629),      # three query blocks (every LDS slot used once)
+    (1, 2, 700, 128, True, 630),     # 11 blocks of 64 queries: odd count, ragged tail
+    (1, 1, 384, 128, False, 631),    # non-causal, 6 blocks of 64 (no masked path)
 ]
 
 

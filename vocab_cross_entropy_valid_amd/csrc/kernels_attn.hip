@@ -397,16 +397,19 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 //    dP^T = V dO^T on the MFMA (Q and dO fragments stay in registers),
 //    dS^T formed in the lane, dQ^T += K^T dS^T with K^T laid out in LDS in
 //    the paired-chunk order of the forward's V^T.  It also writes D.
-//  * dK / dV pass: a workgroup takes 128 keys (lane = key) and streams the
-//    queries in blocks of 32: S = Q K^T and dP = dO V^T (lse and D of the
-//    block's queries from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T
-//    with dO^T and Q^T in the paired-chunk layout.
+//  * dK / dV pass: a workgroup takes 128 keys and streams the queries in
+//    blocks: S = Q K^T and dP = dO V^T (lse and D of the block's queries
+//    from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T.  D = 128 runs 8
+//    waves of 16 keys on the 16 x 16 x 32 product (two waves per SIMD,
+//    blocks of 64 queries, attn_bwd_dkv16_kernel); D = 64 runs 4 waves of 32
+//    keys on the 32 x 32 x 16 product (one wave per SIMD, blocks of 32).
 //
-// Both passes run one wave per SIMD and stage their streamed tiles through
-// registers: the next block is loaded while the current one computes, and
-// each thread's load unit (4 rows x 8 dims) feeds both the row-major and the
-// transposed LDS copy.  The dQ pass keeps two LDS slots, the dK / dV pass
-// three (its accumulation runs one block late); one barrier per block.
+// The dQ pass and the D = 64 dK / dV pass run one wave per SIMD and stage
+// their streamed tiles through registers: the next block is loaded while the
+// current one computes, and each thread's load unit (4 rows x 8 dims) feeds
+// both the row-major and the transposed LDS copy.  The dQ pass keeps two LDS
+// slots, the dK / dV pass three (its accumulation runs one block late); one
+// barrier per block.
 
 namespace {
 
@@ -624,28 +627,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
     // the blocks that need them
     const int lim = a.causal ? min(q, S - 1) : S - 1;
     u32x4 dsf[2][2];
-    auto softmax = [&](const bool masked) {
+    // masks (sequence end, causal diagonal) set the scores to -inf in place,
+    // only on the blocks that need them; one softmax code path, so that the
+    // register allocation is the same on every path
+    if (k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0)) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int i = 0; i < 16; ++i)
+          if (k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) sc[mt][i] = -INFINITY;
+    }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            float ds[2];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int i = 8 * g + 2 * w + e;
-              float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
-              if (masked && k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) p = 0.f;
-              ds[e] = p * (dp[mt][i] - Dq);
-            }
-            dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float ds[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 8 * g + 2 * w + e;
+            const float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
+            ds[e] = p * (dp[mt][i] - Dq);
           }
-    };
-    if (k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0))
-      softmax(true);
-    else
-      softmax(false);
+          dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
+        }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MD; ++m)
@@ -780,12 +786,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     }
   };
 
-  // P and dS of the previous block (B operands of its deferred accumulation)
+  // P and dS of the previous block (B operands of its deferred accumulation);
+  // zero until a block has run, so that the first accumulation adds nothing
   u32x4 pp[2], ps[2];
-  bool pending = false;  // C of the previous block still to run
-  // C(qbk): dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot qbk
-  auto accumulate = [&](int qbk) {
-    const char* sl = slot_of(qbk);
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pp[g][w] = 0u;
+      ps[g][w] = 0u;
+    }
+  int prev_slot = -1;  // slot of the block whose accumulation is pending
+  // C: dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot sl
+  auto accumulate = [&](const char* sl) {
     if constexpr (kTr) {
       const char* lq = sl;         // Q rows, read transposed
       const char* ldo = sl + kQT;  // dO rows, read transposed
@@ -810,7 +823,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     }
   };
 
-  // block qbk: A(qbk), then its softmax with C(qbk - 1) issued alongside
+  // block qbk: A(qbk), then its softmax with the pending accumulation issued
+  // alongside.  One code path for every block: the first accumulation reads
+  // this block's slot (finite data) against zero P and dS, and the causal
+  // mask sets the diagonal block's scores to -inf in place, so that the
+  // register allocation is the same on every path.
   auto compute = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
     const char* sl = slot_of(qbk);
@@ -818,10 +835,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     const char* ldo = sl + kQT;                             // dO rows
     const float* llse = (const float*)(sl + kTiles * kQT);  // lse log2(e) (+inf past S)
     const float* ldel = llse + kKvQ;                   // D
-    // S = Q K^T, dP = dO V^T: lane = key, values i = queries 8 (i / 4) + 4 h + i % 4.
-    // Each phase's LDS fragments are read together into their own registers
-    // (sched_barrier fences): left alone, the compiler funnels each read
-    // through one register quad and waits on it right before its MFMA.
     u32x4 fq[KS], fdo[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -848,45 +861,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
       l4[r4] = *(const f32x4*)(llse + 8 * r4 + 4 * h);
       d4[r4] = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
     }
-    // softmax of this block; the causal mask only on the wave's diagonal
-    // block (a wave-uniform branch), and the previous block's accumulation
-    // in the same region, so that its MFMAs interleave with the VALU work
-    auto softmax = [&](const bool masked, const bool prev) {
-      if (prev) accumulate(qbk - 1);
-      u32x4 np[2], ns[2];
+    accumulate(slot_of(prev_slot < 0 ? qbk : prev_slot));
+    if (a.causal && qb0 < k0w + 32) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        float p[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r4 + e;
-          float pv = fast_exp2(fmaf(sc[i], c, -l4[r4][e]));  // 0 past S (lse = +inf)
-          if (masked && qb0 + 8 * r4 + 4 * h + e < kk) pv = 0.f;
-          p[e] = pv;
-          ds[e] = pv * (dp[i] - d4[r4][e]);
-        }
-        // values i = 8 g .. 8 g + 7 form operand g: r4 = 2 g, 2 g + 1
-        const int g = r4 >> 1, w0 = (r4 & 1) * 2;
-        np[g][w0] = cvt_pk_bf16(p[0], p[1]);
-        np[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
-        ns[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
-        ns[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
-      }
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        pp[g] = np[g];
-        ps[g] = ns[g];
-      }
-    };
-    const bool diag = a.causal && qb0 < k0w + 32;
-    if (pending) {
-      if (diag) softmax(true, true);
-      else softmax(false, true);
-    } else {
-      if (diag) softmax(true, false);
-      else softmax(false, false);
+      for (int i = 0; i < 16; ++i)
+        if (qb0 + 8 * (i >> 2) + 4 * h + (i & 3) < kk) sc[i] = -INFINITY;
     }
-    pending = true;
+    u32x4 np[2], ns[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * r4 + e;
+        const float pv = fast_exp2(fmaf(sc[i], c, -l4[r4][e]));  // 0 past S (lse = +inf)
+        p[e] = pv;
+        ds[e] = pv * (dp[i] - d4[r4][e]);
+      }
+      const int g = r4 >> 1, w0 = (r4 & 1) * 2;
+      np[g][w0] = cvt_pk_bf16(p[0], p[1]);
+      np[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
+      ns[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
+      ns[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      pp[g] = np[g];
+      ps[g] = ns[g];
+    }
+    prev_slot = qbk;
   };
 
   // Prologue: blocks qstart and qstart + 1 staged, qstart + 2 in registers.
@@ -908,7 +911,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
       if (qbk + 3 < nq) prefetch(qbk + 3);
     }
   }
-  if (pending) accumulate(nq - 1);
+  if (prev_slot >= 0) accumulate(slot_of(prev_slot));
 
   if (kk >= S) return;
   float* dKk = a.dK + head + (int64_t)kk * D;
@@ -924,6 +927,322 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
       *(f32x4*)(dKk + d0) = vk;
       *(f32x4*)(dVk + d0) = vv;
     }
+}
+
+// dK / dV pass for D = 128 on v_mfma_f32_16x16x32_bf16, two waves per SIMD.
+// A workgroup of 8 waves takes 128 keys, 16 per wave, and streams the
+// queries in blocks of 32 NH (NH = 2 is launched) through four LDS slots
+// (Q rows, dO rows, lse, D).  Operand layouts of the 16 x 16 x 32 product:
+// A lane l holds row l % 16 with K entries 8 (l / 16) .. + 7, B lane l
+// column l % 16 with the same K entries, the result lane l column l % 16
+// with rows 4 (l / 16) .. + 3.
+//  * S = Q K^T and dP = dO V^T per 16-query quarter h of the block: lane l
+//    (g = l / 16) holds key l % 16 and queries 16 h + 4 g + e (e = 0..3);
+//    K and V stay in registers (the B operands).  Eight independent
+//    accumulation chains for NH = 2.
+//  * dV^T += dO^T P^T and dK^T += Q^T dS^T over K = 32 queries at a time:
+//    the B operand is P (dS) of the lane's 8 queries of that half in the
+//    order above, the A operand the matching dO^T (Q^T) entries, read
+//    straight from the row-major tile with two transposing reads (queries
+//    4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half).  The accumulation of
+//    block b runs in block b + 1, next to its softmax.
+//  * Query blocks are loaded into registers (buffer loads: rows past S read
+//    as zeros, and so add nothing) and written to LDS at the end of an
+//    iteration, two blocks ahead of their use; with 32-query blocks the
+//    loads are issued an iteration earlier still (two register sets).
+//  * The causal blocks that overlap the workgroup's keys (the first 128 / QB)
+//    take the masked path; the main loop carries no mask.
+namespace {
+constexpr int kDkv16Threads = 512;
+
+__device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                              __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Row-major Q / dO tiles of this pass (256-byte rows of 16 sixteen-byte
+// chunks): chunk c of row r sits at position c ^ swz16(r), swz16(r) =
+// 2 (r % 8) + (r / 8) % 2.  The S / dP fragment reads (16 lanes: one chunk
+// of 16 consecutive rows) hit 16 distinct positions, and so do the
+// transposing reads (32 lanes: chunks 2 m, 2 m + 1 of 8 consecutive rows).
+__device__ __forceinline__ int swz16_offset(int row, int chunk) {
+  return row * 256 + ((chunk ^ (((row & 7) << 1) | ((row >> 3) & 1))) << 4);
+}
+
+// A fragment of the transposed tile for the 16 x 16 x 32 product: operand row
+// = tile column 16 m + lane % 16, K entries = tile rows 4 (lane / 16) + {0..3}
+// and 16 + the same, from two ds_read_b64_tr_b16 at per-lane offset off (and
+// off + 16 rows).  Lane L of a 16-lane group addresses row 4 (group) + L / 4,
+// columns 16 m + 4 (L % 4) .. + 3.
+__device__ __forceinline__ u32x4 tr_frag16(const char* p) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p + 4096));
+  const u32x2 x = __builtin_bit_cast(u32x2, lo);
+  const u32x2 y = __builtin_bit_cast(u32x2, hi);
+  u32x4 r = {x[0], x[1], y[0], y[1]};
+  return r;
+}
+}  // namespace
+
+template <int NH>
+__global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBwdArgs a) {
+  constexpr int D = 128;
+  constexpr int QB = 32 * NH;             // queries per block
+  constexpr int kKV = kKvKeys * D * 2;    // K (or V) rows of the workgroup
+  constexpr int kQT = QB * D * 2;         // one block's Q (or dO) tile
+  constexpr int kSlot = 2 * kQT + 512;    // Q, dO, lse[64], D[64]
+  constexpr int kLds = 2 * kKV > 4 * kSlot ? 2 * kKV : 4 * kSlot;
+  constexpr int kPre = QB / 32;           // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int S = a.S;
+  const int kblk = (int)(blockIdx.x / a.BH);
+  const int64_t bh = blockIdx.x % a.BH;
+  const int64_t head = bh * (int64_t)S * D;
+  const int kbase = kblk * kKvKeys;
+  const int k0w = kbase + 16 * wave;  // first key of this wave
+  const int kk = k0w + i16;           // this lane's key
+  const float c = a.scale_log2;
+
+  // K and V fragments (B operands of S and dP) for the whole pass
+  u32x4 kf[4], vf[4];
+  {
+    char* lk = lds;
+    char* lv = lds + kKV;
+    stage_rows<D, kKvKeys, kDkv16Threads>(lk, a.K + head, kbase, S, tid);
+    stage_rows<D, kKvKeys, kDkv16Threads>(lv, a.V + head, kbase, S, tid);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ko = k_offset(16 * wave + i16, 4 * s + g, D / 8);
+      kf[s] = *(const u32x4*)(lk + ko);
+      vf[s] = *(const u32x4*)(lv + ko);
+    }
+    __syncthreads();  // the query slots reuse this LDS
+  }
+
+  f32x4 dk[8], dv[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dk[m][e] = 0.f;
+      dv[m][e] = 0.f;
+    }
+
+  const int nq = (S + QB - 1) / QB;
+  const int qstart = a.causal ? kbase / QB : 0;
+  // Register-staged loads: thread t carries chunk t % 16 of rows t / 16 + 32 i
+  // (i < kPre) of the Q and the dO tile, stored at position t % 16 of its row,
+  // i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves carry the
+  // block's lse values, odd waves its D values (the waves of a parity write
+  // identical values).  Two register sets, by block parity relative to
+  // qstart: block b is loaded in iteration b - 3 and written to LDS at the
+  // end of iteration b - 2, into the slot of block b - 4.  The parity is a
+  // compile-time constant at every use.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)(a.Q + head), (int64_t)S * D * 2);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)(a.dO + head), (int64_t)S * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = (wave & 1)
+      ? make_rsrc((const char*)(a.delta + bh * S), (int64_t)S * 4)
+      : make_rsrc((const char*)(a.lse + bh * S), (int64_t)S * 4);
+  const int srow = tid >> 4;
+  const uint32_t gvoff = (uint32_t)swz16_offset(srow, tid & 15);
+  const int lvoff = srow * 256 + ((tid & 15) << 4);
+  // one register set when a block holds 64 queries (an iteration is then
+  // long enough to hide the loads, and two sets would not fit)
+  constexpr int kSets = NH == 1 ? 2 : 1;
+  u32x4 pre[kSets][2 * kPre];
+  float pre_v[kSets];
+  auto slot_of = [&](int qbk) { return lds + ((qbk - qstart) & 3) * kSlot; };
+  auto load_regs = [&](int qbk, auto par) {
+    constexpr int r = decltype(par)::value;
+    const uint32_t soff = (uint32_t)(qbk * QB) * 256u;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      pre[r][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + 8192 * i, soff, 0));
+      pre[r][kPre + i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + 8192 * i, soff, 0));
+    }
+    pre_v[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rv, lane * 4, (uint32_t)(qbk * QB) * 4u, 0));
+    __builtin_amdgcn_sched_barrier(0);  // issued first: an iteration of latency to hide
+  };
+  auto store_regs = [&](int qbk, auto par) {
+    constexpr int r = decltype(par)::value;
+    char* sl = slot_of(qbk);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      *(u32x4*)(sl + lvoff + 8192 * i) = pre[r][i];
+      *(u32x4*)(sl + kQT + lvoff + 8192 * i) = pre[r][kPre + i];
+    }
+    *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = pre_v[r];
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  // per-lane LDS offsets: S / dP fragments (row i16 of a 16-query quarter,
+  // chunk 4 s + g) and the transposing reads of the accumulation
+  int aoff[4], toff[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = swz16_offset(i16, 4 * s + g);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int row = 4 * g + (i16 >> 2);
+    const int dim = 16 * m + 4 * (lane & 3);
+    toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
+  }
+  // P and dS of the pending block, one B operand per 32-query half
+  u32x4 pp[NH], ps[NH];
+#pragma unroll
+  for (int n = 0; n < NH; ++n)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pp[n][w] = 0u;
+      ps[n][w] = 0u;
+    }
+  int prev = -1;  // the block whose accumulation is pending (none: zero P / dS)
+
+  // dV^T += dO^T P^T, dK^T += Q^T dS^T over the 32 queries of each half
+  auto accumulate = [&](const char* sp) {
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        mma16(dv[m], tr_frag16(sp + kQT + 8192 * n + toff[m]), pp[n]);
+        mma16(dk[m], tr_frag16(sp + 8192 * n + toff[m]), ps[n]);
+      }
+  };
+
+  // S and dP of block qbk, then its softmax with the pending accumulation
+  auto block = [&](int qbk, const bool masked) {
+    const char* sl = slot_of(qbk);
+    f32x4 sc[2 * NH], dp[2 * NH];  // 16-query quarters
+#pragma unroll
+    for (int h = 0; h < 2 * NH; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[h][e] = 0.f;
+        dp[h][e] = 0.f;
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int h = 0; h < 2 * NH; ++h) {
+        mma16(sc[h], *(const u32x4*)(sl + aoff[s] + 4096 * h), kf[s]);
+        mma16(dp[h], *(const u32x4*)(sl + kQT + aoff[s] + 4096 * h), vf[s]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    const float* lv = (const float*)(sl + 2 * kQT);
+    f32x4 l4[2 * NH], d4[2 * NH];
+#pragma unroll
+    for (int h = 0; h < 2 * NH; ++h) {
+      l4[h] = *(const f32x4*)(lv + 16 * h + 4 * g);
+      d4[h] = *(const f32x4*)(lv + 64 + 16 * h + 4 * g);
+    }
+    accumulate(slot_of(prev < 0 ? qbk : prev));
+    if (masked) {
+#pragma unroll
+      for (int h = 0; h < 2 * NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc[h][e] = (qbk * QB + 16 * h + 4 * g + e < kk) ? -INFINITY : sc[h][e];
+    }
+#pragma unroll
+    for (int n = 0; n < NH; ++n) {
+      float pv[2][4], dsv[2][4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 2 * n + hh;
+          // rows past S: lse = 0, S = 0, dO = 0, so P = 1 and dS = 0 there,
+          // and their dO^T / Q^T entries are 0
+          pv[hh][e] = fast_exp2(fmaf(sc[h][e], c, -l4[h][e] * kLog2e));
+          dsv[hh][e] = pv[hh][e] * (dp[h][e] - d4[h][e]);
+        }
+      pp[n][0] = cvt_pk_bf16(pv[0][0], pv[0][1]);
+      pp[n][1] = cvt_pk_bf16(pv[0][2], pv[0][3]);
+      pp[n][2] = cvt_pk_bf16(pv[1][0], pv[1][1]);
+      pp[n][3] = cvt_pk_bf16(pv[1][2], pv[1][3]);
+      ps[n][0] = cvt_pk_bf16(dsv[0][0], dsv[0][1]);
+      ps[n][1] = cvt_pk_bf16(dsv[0][2], dsv[0][3]);
+      ps[n][2] = cvt_pk_bf16(dsv[1][0], dsv[1][1]);
+      ps[n][3] = cvt_pk_bf16(dsv[1][2], dsv[1][3]);
+    }
+    prev = qbk;
+  };
+
+  // prologue: blocks qstart, qstart + 1 in LDS (and qstart + 2 in registers)
+  using PS = std::integral_constant<int, kSets - 1>;
+  load_regs(qstart, P0{});
+  store_regs(qstart, P0{});
+  if (qstart + 1 < nq) {
+    load_regs(qstart + 1, PS{});
+    store_regs(qstart + 1, PS{});
+  }
+  if (kSets == 2 && qstart + 2 < nq) load_regs(qstart + 2, P0{});
+  __syncthreads();
+  // iteration qbk: the loads of block qbk + 3 issued, block qbk + 2 written
+  // to the slot of block qbk - 2 (its accumulation ran in iteration qbk - 1).
+  // kDiag: a causal block that overlaps the workgroup's keys, skipped by the
+  // waves whose keys all come after its queries and masked for the others
+  // (with one register set: block qbk + 2 loaded at the start of the
+  // iteration and written at its end)
+  auto iter = [&](int qbk, auto par, auto diag) {
+    constexpr int P = kSets == 2 ? decltype(par)::value : 0;
+    constexpr bool kDiag = decltype(diag)::value;
+    using Pc = std::integral_constant<int, P>;
+    using Pn = std::integral_constant<int, kSets == 2 ? 1 - P : 0>;
+    if (kSets == 2) {
+      if (qbk + 3 < nq) load_regs(qbk + 3, Pn{});
+    } else {
+      if (qbk + 2 < nq) load_regs(qbk + 2, Pc{});
+    }
+    if (kDiag) {
+      if (qbk * QB + QB - 1 >= k0w) block(qbk, qbk * QB < k0w + 16);
+    } else {
+      block(qbk, false);
+    }
+    if (qbk + 2 < nq) store_regs(qbk + 2, Pc{});
+    __syncthreads();
+  };
+  using Diag = std::integral_constant<bool, true>;
+  using Plain = std::integral_constant<bool, false>;
+  int qbk = qstart;
+  if (a.causal) {
+    // the workgroup's 128 keys span blocks qstart .. qstart + 128 / QB - 1
+    if (qbk < nq) iter(qbk++, P0{}, Diag{});
+    if (qbk < nq) iter(qbk++, P1{}, Diag{});
+    if constexpr (NH == 1) {
+      if (qbk < nq) iter(qbk++, P0{}, Diag{});
+      if (qbk < nq) iter(qbk++, P1{}, Diag{});
+    }
+  }
+  // qbk - qstart is even here
+  for (; qbk + 1 < nq; qbk += 2) {
+    iter(qbk, P0{}, Plain{});
+    iter(qbk + 1, P1{}, Plain{});
+  }
+  if (qbk < nq) iter(qbk, P0{}, Plain{});
+  if (prev >= 0) accumulate(slot_of(prev));
+
+  if (kk >= S) return;
+  float* dKk = a.dK + head + (int64_t)kk * D;
+  float* dVk = a.dV + head + (int64_t)kk * D;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int d0 = 16 * m + 4 * g;
+    f32x4 vk = {dk[m][0] * a.scale, dk[m][1] * a.scale, dk[m][2] * a.scale, dk[m][3] * a.scale};
+    *(f32x4*)(dKk + d0) = vk;
+    *(f32x4*)(dVk + d0) = dv[m];
+  }
 }
 
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
@@ -942,7 +1261,7 @@ hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s) {
   const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
   const dim3 grid((unsigned)(nkb * a.BH));
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, grid, dim3(kAttnThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkv16_kernel<2>, grid, dim3(kDkv16Threads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
