@@ -92,52 +92,6 @@ __device__ __forceinline__ int vt_unit_offset(int dv, int u) {
   return vt_chunk_offset(dv, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
 }
 
-// Row-major bf16 tile of 128-dim rows (16 sixteen-byte chunks per 256-byte
-// row) that is also read transposed: chunk c of row r sits at position
-// c ^ trs(r), trs(r) = (r % 16) ^ 4 (r % 4).  trs is a bijection on any 16
-// consecutive rows, so 16 lanes reading one chunk of consecutive rows hit
-// distinct banks; a transposing read of 8 consecutive rows x 4 chunks puts
-// two rows' chunks on each group of four banks, i.e. each bank twice (the
-// minimum for 512 bytes); the staging writes spread evenly as well.
-__device__ __forceinline__ int trs_offset(int row, int chunk) {
-  return row * 256 + ((chunk ^ ((row & 15) ^ ((row & 3) << 2))) << 4);
-}
-
-// A fragment of the transposed tile, straight from such a row-major tile
-// with two ds_read_b64_tr_b16: operand row = tile column dim0 + lane % 32, K =
-// tile rows r0 + 4 (lane / 32) + {0..3} and the same + 8, the paired order
-// in which the accumulator-derived B operands hold the queries.  Within a
-// group of 16 lanes, lane i receives as element e the element i % 4 of the
-// 8 bytes lane 4 e + i / 4 addressed, so lane l addresses row r0 + 4 (l / 32)
-// + (l % 16) / 4 at column dim0 + 16 ((l / 16) % 2) + 4 (l % 4).
-__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int dim0, int lane) {
-  typedef short i16x4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int dim = dim0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const char* p1 = tile + trs_offset(row, dim >> 3) + (dim & 7) * 2;
-  const char* p2 = tile + trs_offset(row + 8, dim >> 3) + (dim & 7) * 2;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p1));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p2));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo);
-  const u32x2 b = __builtin_bit_cast(u32x2, hi);
-  u32x4 r = {a[0], a[1], b[0], b[1]};
-  return r;
-}
-
-// A load unit (see load_unit) of an R-row tile into such a layout, rows past
-// S zeroed.
-template <int R>
-__device__ __forceinline__ void store_unit_trs(const u32x4 (&vin)[4], char* tile, int row0, int S,
-                                               int unit) {
-  const int kg = unit % (R / 4);
-  const int dg = unit / (R / 4);
-  const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *(u32x4*)(tile + trs_offset(4 * kg + q, dg)) = row0 + 4 * kg + q < S ? vin[q] : z;
-}
-
 template <int D>
 struct BlockRegs {
   static constexpr int kKLoads = kKBlock * D / 8 / kAttnThreads;              // 16-B K loads
@@ -392,11 +346,14 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 // probabilities are never stored in the backward pass either.  Two passes,
 // no atomics (results are deterministic):
 //
-//  * dQ pass: a workgroup takes 128 queries (lane = query, as in the
-//    forward) and streams the keys in blocks of 64: S^T = K Q^T and
-//    dP^T = V dO^T on the MFMA (Q and dO fragments stay in registers),
-//    dS^T formed in the lane, dQ^T += K^T dS^T with K^T laid out in LDS in
-//    the paired-chunk order of the forward's V^T.  It also writes D.
+//  * dQ pass: a workgroup takes 128 queries and streams the keys in blocks
+//    of 64: S^T = K Q^T and dP^T = V dO^T on the MFMA (Q and dO fragments
+//    stay in registers), dS formed in the lane, dQ += dS K.  It also writes
+//    D.  D = 128 runs 8 waves of 16 queries on the 16 x 16 x 32 product (two
+//    waves per SIMD, attn_bwd_dq16_kernel); D = 64 runs 4 waves of 32
+//    queries on the 32 x 32 x 16 product (one wave per SIMD, lane = query,
+//    dQ^T += K^T dS^T with K^T in the paired-chunk order of the forward's
+//    V^T).
 //  * dK / dV pass: a workgroup takes 128 keys and streams the queries in
 //    blocks: S = Q K^T and dP = dO V^T (lse and D of the block's queries
 //    from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T.  D = 128 runs 8
@@ -404,12 +361,13 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 //    blocks of 64 queries, attn_bwd_dkv16_kernel); D = 64 runs 4 waves of 32
 //    keys on the 32 x 32 x 16 product (one wave per SIMD, blocks of 32).
 //
-// The dQ pass and the D = 64 dK / dV pass run one wave per SIMD and stage
-// their streamed tiles through registers: the next block is loaded while the
-// current one computes, and each thread's load unit (4 rows x 8 dims) feeds
-// both the row-major and the transposed LDS copy.  The dQ pass keeps two LDS
-// slots, the dK / dV pass three (its accumulation runs one block late); one
-// barrier per block.
+// The D = 64 passes run one wave per SIMD and stage their streamed tiles
+// through registers: the next block is loaded while the current one
+// computes, and each thread's load unit (4 rows x 8 dims) feeds both the
+// row-major and the transposed LDS copy.  The dQ pass keeps two LDS slots,
+// the dK / dV pass three (its accumulation runs one block late); one barrier
+// per block.  The D = 128 passes read the transposed operands straight from
+// row-major tiles (transposing LDS reads) and stage through buffer loads.
 
 namespace {
 
@@ -503,11 +461,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int kTile = kKBlock * D * 2;  // 64 rows x D (= D rows x 64 entries)
-  // D = 128: K^T for the dQ product is read straight from the K rows
-  // (transposing LDS reads), so a slot holds K and V; D = 64 keeps a
-  // transposed copy of K in the paired-chunk layout
-  constexpr bool kTr = D == 128;
-  constexpr int kSlot = (kTr ? 2 : 3) * kTile;  // K rows, [K^T,] V rows
+  static_assert(D == 64, "D = 128 runs attn_bwd_dq16_kernel");
+  constexpr int kSlot = 3 * kTile;  // K rows, K^T (paired-chunk layout), V rows
   __shared__ __attribute__((aligned(16))) char lds[2 * kSlot];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -571,13 +526,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
     for (int it = 0; it < kIt; ++it) {
       const int u = it * kAttnThreads + tid;
       if (u < kKU) {
-        if constexpr (kTr)
-          store_unit_trs<kKBlock>(pre[it], sl, kb * kKBlock, S, u);
-        else
-          store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
+        store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
       } else if (u < 2 * kKU) {
-        store_unit<D, kKBlock, false>(pre[it], sl + (kTr ? 1 : 2) * kTile, nullptr, kb * kKBlock,
-                                      S, u - kKU);
+        store_unit<D, kKBlock, false>(pre[it], sl + 2 * kTile, nullptr, kb * kKBlock, S,
+                                      u - kKU);
       }
     }
   };
@@ -585,8 +537,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
     const int k0 = kb * kKBlock;
     if (a.causal && k0 > q0 + 31) return;  // every key after the wave's queries
     const char* lk = lds + slot * kSlot;
-    const char* lkt = lk + kTile;  // D = 64 only
-    const char* lv = lk + (kTr ? 1 : 2) * kTile;
+    const char* lkt = lk + kTile;
+    const char* lv = lk + 2 * kTile;
     // S^T = K Q^T and dP^T = V dO^T, one 32-key half (mt) at a time
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -595,7 +547,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int off = k_offset(32 * mt + j, 2 * s + h, C);
-        fk[s] = *(const u32x4*)(lk + (kTr ? trs_offset(32 * mt + j, 2 * s + h) : off));
+        fk[s] = *(const u32x4*)(lk + off);
         fv[s] = *(const u32x4*)(lv + off);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -619,9 +571,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          ft[m][mt][g] = kTr ? tr_frag(lk, 32 * mt + 16 * g, 32 * m, lane)
-                             : *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(
-                                   32 * m + j, 4 * mt + 2 * g + h));
+          ft[m][mt][g] = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(
+              32 * m + j, 4 * mt + 2 * g + h));
     __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); masks (sequence end, causal diagonal) only on
     // the blocks that need them
@@ -703,11 +654,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   constexpr int MD = D / 32;
   constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
   constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  // D = 128: the accumulation reads Q^T and dO^T straight from the row-major
-  // tiles (transposing LDS reads), so a slot holds Q, dO, lse and D only;
-  // D = 64 keeps transposed copies in the paired-chunk layout
-  constexpr bool kTr = D == 128;
-  constexpr int kTiles = kTr ? 2 : 4;
+  static_assert(D == 64, "D = 128 runs attn_bwd_dkv16_kernel");
+  constexpr int kTiles = 4;  // Q, dO, and their transposed copies (paired-chunk layout)
   constexpr int kSlot = kTiles * kQT + 2 * kKvQ * 4;
   constexpr int kLds = 2 * kKV > 3 * kSlot ? 2 * kKV : 3 * kSlot;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
@@ -772,13 +720,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   auto stage = [&](int qbk) {
     const int qb0 = qbk * kKvQ;
     char* sl = slot_of(qbk);
-    if (unit_on) {
-      if constexpr (kTr)
-        store_unit_trs<kKvQ>(pre, sl + (unit_q ? 0 : kQT), qb0, S, unit);
-      else
-        store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S,
-                            unit);
-    }
+    if (unit_on)
+      store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S, unit);
     if (tid < 2 * kKvQ) {
       float* lv4 = (float*)(sl + kTiles * kQT);
       const bool in = qb0 + (tid & (kKvQ - 1)) < S;
@@ -799,28 +742,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   int prev_slot = -1;  // slot of the block whose accumulation is pending
   // C: dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot sl
   auto accumulate = [&](const char* sl) {
-    if constexpr (kTr) {
-      const char* lq = sl;         // Q rows, read transposed
-      const char* ldo = sl + kQT;  // dO rows, read transposed
+    const char* lqt = sl + 2 * kQT;   // Q^T
+    const char* ldot = sl + 3 * kQT;  // dO^T
 #pragma unroll
-      for (int m = 0; m < MD; ++m)
+    for (int m = 0; m < MD; ++m)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          Mma<bf16_t>::run(dv[m], tr_frag(ldo, 16 * g, 32 * m, lane), pp[g]);
-          Mma<bf16_t>::run(dk[m], tr_frag(lq, 16 * g, 32 * m, lane), ps[g]);
-        }
-    } else {
-      const char* lqt = sl + 2 * kQT;   // Q^T
-      const char* ldot = sl + 3 * kQT;  // dO^T
-#pragma unroll
-      for (int m = 0; m < MD; ++m)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
-          Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
-          Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
-        }
-    }
+      for (int g = 0; g < 2; ++g) {
+        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
+        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
+        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
+      }
   };
 
   // block qbk: A(qbk), then its softmax with the pending accumulation issued
@@ -838,7 +769,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     u32x4 fq[KS], fdo[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int qo = kTr ? trs_offset(j, 2 * s + h) : k_offset(j, 2 * s + h, C);
+      const int qo = k_offset(j, 2 * s + h, C);
       fq[s] = *(const u32x4*)(lq + qo);
       fdo[s] = *(const u32x4*)(ldo + qo);
     }
@@ -972,8 +903,9 @@ __device__ __forceinline__ int swz16_offset(int row, int chunk) {
 // A fragment of the transposed tile for the 16 x 16 x 32 product: operand row
 // = tile column 16 m + lane % 16, K entries = tile rows 4 (lane / 16) + {0..3}
 // and 16 + the same, from two ds_read_b64_tr_b16 at per-lane offset off (and
-// off + 16 rows).  Lane L of a 16-lane group addresses row 4 (group) + L / 4,
-// columns 16 m + 4 (L % 4) .. + 3.
+// off + 16 rows).  Within a group of 16 lanes, lane i receives as element e
+// the element i % 4 of the 8 bytes that lane 4 e + i / 4 addressed; so lane L
+// of group G addresses row 4 G + L / 4, columns 16 m + 4 (L % 4) .. + 3.
 __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
   typedef short i16x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -1245,12 +1177,220 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   }
 }
 
+// dQ pass for D = 128 on the 16 x 16 x 32 product, two waves per SIMD: a
+// workgroup of 8 waves takes 128 queries, 16 per wave, and streams the keys
+// in blocks of 64 through two LDS slots (K rows, V rows, in the swizzle of
+// swz16_offset).
+//  * S^T = K Q^T and dP^T = V dO^T per 16-key quarter of the block: lane l
+//    (g = l / 16) holds query l % 16 and keys 16 kq + 4 g + e; the wave's Q
+//    and dO rows stay in registers (the B operands), so lse and D are one
+//    value per lane.
+//  * dQ += dS K over K = 32 keys at a time: the A operand is dS of the
+//    lane's query for keys 4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half
+//    (the lane's own values), the B operand the matching K entries, read
+//    straight from the row-major K tile with two transposing reads.
+//  * Key blocks are loaded into registers (buffer loads: rows past S read as
+//    zeros) an iteration ahead and written to LDS at the end of the
+//    iteration before their use.  The last two blocks (the causal diagonal,
+//    the sequence tail) take the masked path.
+//  * It also writes D = rowsum(dO O) for the dK / dV pass.
+__global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArgs a) {
+  constexpr int D = 128;
+  constexpr int KB = 64;               // keys per block
+  constexpr int kT = KB * D * 2;       // one block's K (or V) tile
+  constexpr int kSlot = 2 * kT;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kSlot];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int S = a.S;
+  const int nqb = (S + kQBlock - 1) / kQBlock;
+  const int qb = nqb - 1 - (int)(blockIdx.x / a.BH);  // heaviest first
+  const int64_t bh = blockIdx.x % a.BH;
+  const int64_t head = bh * (int64_t)S * D;
+  const int q0w = qb * kQBlock + 16 * wave;  // first query of this wave
+  const int q = q0w + i16;                   // this lane's query
+  const int qc = q < S ? q : S - 1;
+  const float c = a.scale_log2;
+
+  // Q and dO fragments (B operands: query i16, dims 32 s + 8 g .. + 7), and
+  // D = rowsum(dO O) of the lane's query (the four lanes of a query each sum
+  // a quarter of the dims)
+  u32x4 qf[4], df[4];
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t off = head + (int64_t)qc * D + 32 * s + 8 * g;
+    qf[s] = *(const u32x4*)(a.Q + off);
+    df[s] = *(const u32x4*)(a.dO + off);
+    const f32x4 o0 = *(const f32x4*)(a.O + off);
+    const f32x4 o1 = *(const f32x4*)(a.O + off + 4);
+    dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
+             bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
+             bf16_lo(df[s][3]) * o1[2] + bf16_hi(df[s][3]) * o1[3];
+  }
+  dpart += __shfl_xor(dpart, 16);
+  const float Dq = dpart + __shfl_xor(dpart, 32);
+  if (g == 0 && q < S) a.delta[bh * S + q] = Dq;
+  const float lse2 = (q < S ? a.lse[bh * S + q] : 0.f) * kLog2e;
+
+  f32x4 dq[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dq[m][e] = 0.f;
+
+  const int kend = a.causal ? min(S, qb * kQBlock + kQBlock) : S;
+  const int nkb = (kend + KB - 1) / KB;
+  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 and
+  // t / 16 + 32 of the K and the V tile (position t % 16 of the row in LDS);
+  // two register sets by block parity, compile-time at every use
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)(a.K + head), (int64_t)S * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)(a.V + head), (int64_t)S * D * 2);
+  const int srow = tid >> 4;
+  const uint32_t gvoff = (uint32_t)swz16_offset(srow, tid & 15);
+  const int lvoff = srow * 256 + ((tid & 15) << 4);
+  u32x4 pre[2][4];
+  auto slot_of = [&](int kb) { return lds + (kb & 1) * kSlot; };
+  auto load_regs = [&](int kb, auto par) {
+    constexpr int r = decltype(par)::value;
+    const uint32_t soff = (uint32_t)(kb * KB) * 256u;
+    pre[r][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, gvoff, soff, 0));
+    pre[r][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, gvoff + 8192, soff, 0));
+    pre[r][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvoff, soff, 0));
+    pre[r][3] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvoff + 8192, soff, 0));
+    __builtin_amdgcn_sched_barrier(0);  // issued first
+  };
+  auto store_regs = [&](int kb, auto par) {
+    constexpr int r = decltype(par)::value;
+    char* sl = slot_of(kb);
+    *(u32x4*)(sl + lvoff) = pre[r][0];
+    *(u32x4*)(sl + lvoff + 8192) = pre[r][1];
+    *(u32x4*)(sl + kT + lvoff) = pre[r][2];
+    *(u32x4*)(sl + kT + lvoff + 8192) = pre[r][3];
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  int aoff[4], toff[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = swz16_offset(i16, 4 * s + g);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int row = 4 * g + (i16 >> 2);
+    const int dim = 16 * m + 4 * (lane & 3);
+    toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
+  }
+  const int lim = a.causal ? min(q, S - 1) : S - 1;  // last key this lane may see
+
+  auto block = [&](int kb, const bool masked) {
+    const char* sl = slot_of(kb);
+    f32x4 sc[4], dp[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[kq][e] = 0.f;
+        dp[kq][e] = 0.f;
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        mma16(sc[kq], *(const u32x4*)(sl + aoff[s] + 4096 * kq), qf[s]);
+        mma16(dp[kq], *(const u32x4*)(sl + kT + aoff[s] + 4096 * kq), df[s]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    if (masked) {
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc[kq][e] = (kb * KB + 16 * kq + 4 * g + e > lim) ? -INFINITY : sc[kq][e];
+    }
+    u32x4 dsf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float ds[2][4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kq = 2 * j + hh;
+          const float p = fast_exp2(fmaf(sc[kq][e], c, -lse2));
+          ds[hh][e] = p * (dp[kq][e] - Dq);
+        }
+      dsf[j][0] = cvt_pk_bf16(ds[0][0], ds[0][1]);
+      dsf[j][1] = cvt_pk_bf16(ds[0][2], ds[0][3]);
+      dsf[j][2] = cvt_pk_bf16(ds[1][0], ds[1][1]);
+      dsf[j][3] = cvt_pk_bf16(ds[1][2], ds[1][3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) mma16(dq[m], dsf[j], tr_frag16(sl + 8192 * j + toff[m]));
+  };
+
+  // prologue: block 0 in LDS, block 1 in registers
+  load_regs(0, P0{});
+  store_regs(0, P0{});
+  if (1 < nkb) load_regs(1, P1{});
+  __syncthreads();
+  // iteration kb: loads of block kb + 2, block kb + 1 written to the other
+  // slot (read in iteration kb - 1) at the end
+  auto iter = [&](int kb, auto par, auto last) {
+    constexpr int P = decltype(par)::value;
+    constexpr bool kMasked = decltype(last)::value;
+    using Pn = std::integral_constant<int, 1 - P>;
+    if (kb + 2 < nkb) load_regs(kb + 2, par);
+    if (kMasked) {
+      // every key of the block after the wave's queries: nothing to add
+      if (!(a.causal && kb * KB > q0w + 15)) block(kb, true);
+    } else {
+      block(kb, false);
+    }
+    if (kb + 1 < nkb) store_regs(kb + 1, Pn{});
+    __syncthreads();
+  };
+  using Masked = std::integral_constant<bool, true>;
+  using Plain = std::integral_constant<bool, false>;
+  const int nplain = nkb >= 2 ? nkb - 2 : 0;  // the last two blocks take the mask
+  int kb = 0;
+  for (; kb + 1 < nplain; kb += 2) {
+    iter(kb, P0{}, Plain{});
+    iter(kb + 1, P1{}, Plain{});
+  }
+  if (kb < nplain) {
+    iter(kb, P0{}, Plain{});
+    ++kb;
+    if (kb < nkb) iter(kb, P1{}, Masked{});
+    ++kb;
+    if (kb < nkb) iter(kb, P0{}, Masked{});
+  } else {
+    if (kb < nkb) iter(kb, P0{}, Masked{});
+    ++kb;
+    if (kb < nkb) iter(kb, P1{}, Masked{});
+  }
+
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int qq = q0w + 4 * g + e;
+    if (qq < S) {
+      float* dQq = a.dQ + head + (int64_t)qq * D + i16;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) dQq[16 * m] = dq[m][e] * a.scale;
+    }
+  }
+}
+
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
   if (a.S <= 0 || a.BH <= 0) return hipSuccess;
   const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
   const dim3 grid((unsigned)(nqb * a.BH));
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(kAttnThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq16_kernel, grid, dim3(kDkv16Threads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
