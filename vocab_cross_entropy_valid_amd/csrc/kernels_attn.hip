@@ -875,8 +875,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
 //    the B operand is P (dS) of the lane's 8 queries of that half in the
 //    order above, the A operand the matching dO^T (Q^T) entries, read
 //    straight from the row-major tile with two transposing reads (queries
-//    4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half).  The accumulation of
-//    block b runs in block b + 1, next to its softmax.
+//    4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half).  With two waves per
+//    SIMD the accumulation runs right after the softmax of the same block
+//    (deferring it to the next block, next to that block's softmax, was 3%
+//    slower).
 //  * Query blocks are loaded into registers (buffer loads: rows past S read
 //    as zeros, and so add nothing) and written to LDS at the end of an
 //    iteration, two blocks ahead of their use; with 32-query blocks the
@@ -1030,29 +1032,9 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
     const int dim = 16 * m + 4 * (lane & 3);
     toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
   }
-  // P and dS of the pending block, one B operand per 32-query half
-  u32x4 pp[NH], ps[NH];
-#pragma unroll
-  for (int n = 0; n < NH; ++n)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      pp[n][w] = 0u;
-      ps[n][w] = 0u;
-    }
-  int prev = -1;  // the block whose accumulation is pending (none: zero P / dS)
-
-  // dV^T += dO^T P^T, dK^T += Q^T dS^T over the 32 queries of each half
-  auto accumulate = [&](const char* sp) {
-#pragma unroll
-    for (int n = 0; n < NH; ++n)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        mma16(dv[m], tr_frag16(sp + kQT + 8192 * n + toff[m]), pp[n]);
-        mma16(dk[m], tr_frag16(sp + 8192 * n + toff[m]), ps[n]);
-      }
-  };
-
-  // S and dP of block qbk, then its softmax with the pending accumulation
+  // S and dP of block qbk, its softmax, then dV^T += dO^T P^T and
+  // dK^T += Q^T dS^T over the 32 queries of each half (P and dS as the B
+  // operands, one per half)
   auto block = [&](int qbk, const bool masked) {
     const char* sl = slot_of(qbk);
     f32x4 sc[2 * NH], dp[2 * NH];  // 16-query quarters
@@ -1078,7 +1060,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
       l4[h] = *(const f32x4*)(lv + 16 * h + 4 * g);
       d4[h] = *(const f32x4*)(lv + 64 + 16 * h + 4 * g);
     }
-    accumulate(slot_of(prev < 0 ? qbk : prev));
     if (masked) {
 #pragma unroll
       for (int h = 0; h < 2 * NH; ++h)
@@ -1086,6 +1067,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
         for (int e = 0; e < 4; ++e)
           sc[h][e] = (qbk * QB + 16 * h + 4 * g + e < kk) ? -INFINITY : sc[h][e];
     }
+    u32x4 pp[NH], ps[NH];
 #pragma unroll
     for (int n = 0; n < NH; ++n) {
       float pv[2][4], dsv[2][4];
@@ -1108,7 +1090,13 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
       ps[n][2] = cvt_pk_bf16(dsv[1][0], dsv[1][1]);
       ps[n][3] = cvt_pk_bf16(dsv[1][2], dsv[1][3]);
     }
-    prev = qbk;
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        mma16(dv[m], tr_frag16(sl + kQT + 8192 * n + toff[m]), pp[n]);
+        mma16(dk[m], tr_frag16(sl + 8192 * n + toff[m]), ps[n]);
+      }
   };
 
   // prologue: blocks qstart, qstart + 1 in LDS (and qstart + 2 in registers)
@@ -1122,7 +1110,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   if (kSets == 2 && qstart + 2 < nq) load_regs(qstart + 2, P0{});
   __syncthreads();
   // iteration qbk: the loads of block qbk + 3 issued, block qbk + 2 written
-  // to the slot of block qbk - 2 (its accumulation ran in iteration qbk - 1).
+  // to the slot of block qbk - 2 (read in iteration qbk - 2).
   // kDiag: a causal block that overlaps the workgroup's keys, skipped by the
   // waves whose keys all come after its queries and masked for the others
   // (with one register set: block qbk + 2 loaded at the start of the
@@ -1163,7 +1151,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
     iter(qbk + 1, P1{}, Plain{});
   }
   if (qbk < nq) iter(qbk, P0{}, Plain{});
-  if (prev >= 0) accumulate(slot_of(prev));
 
   if (kk >= S) return;
   float* dKk = a.dK + head + (int64_t)kk * D;
