@@ -69,9 +69,9 @@ typedef enum { LCE_MEAN = 0, LCE_SUM = 1 } lce_reduction;
  * sizes (the larger of the two; the calls may share one buffer).  Returns 0
  * for invalid sizes.  Bounded by the token chunk (8192 rows), the vocabulary
  * block (16384 entries) and d, plus O(N) per-token vectors: for bf16 the
- * bounded G block and its transpose (bf16 [8192, 16384] each) and the
- * chunk's transposed H rows (bf16 [d, 8192]); fp32 adds the transposed W
- * block (fp32 [d, 16384]).  It never grows with N * V. */
+ * bounded G block (bf16 [8192, 16384]) and the chunk's transposed H rows
+ * (bf16 [d, 8192]); fp32 adds the transposed G and W blocks (fp32
+ * [16384, 8192] and [d, 16384]).  It never grows with N * V. */
 size_t lce_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype);
 
 /* Forward pass.
@@ -181,9 +181,10 @@ typedef struct {
  */
 /* Bytes of device workspace lce_backward_step needs: lce_workspace_bytes plus
  * the transposed W block (dH keeps reading the block's old weights while the
- * update rewrites them) and, when N exceeds one token chunk (8192 rows), the
- * fp32 dW block accumulator ([16384, d]).  Independent of N beyond that and
- * of V.  Returns 0 for invalid sizes. */
+ * update rewrites them) and either, when every valid row lies in one token
+ * chunk (8192 rows), the transposed G block the optimizer epilogue reads
+ * ([16384, 8192]), or else the fp32 dW block accumulator ([16384, d]).
+ * Independent of N beyond that and of V.  Returns 0 for invalid sizes. */
 size_t lce_step_workspace_bytes(int64_t N, int64_t d, int64_t V, int dtype);
 
 lce_status lce_backward_step(const void* H, void* W, const int64_t* labels, int64_t ignore_index,

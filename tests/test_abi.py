@@ -46,13 +46,13 @@ def test_workspace_bounded_independent_of_n_times_v():
     assert w3 == w5
     # the backward block is bounded by constants (token chunk C <= 8192,
     # vocabulary block Vs <= 16384, padded strides) and d, never by N or V:
-    # G [C, Vs], G^T [Vs, C], H^T [d, C] in bf16 (dH reads W itself)
+    # G [C, Vs] and H^T [d, C] in bf16 (dH reads W itself, dW reads G K-major)
     C, Vs, pad, d = 8192, 16384, 64, 4096
-    exact = 2 * (C * (Vs + pad) + Vs * (C + pad) + d * (C + pad))
+    exact = 2 * (C * (Vs + pad) + d * (C + pad))
     assert w5 == exact
-    # fp32 adds the W^T block [d, Vs]
+    # fp32 adds G^T [Vs, C] and the W^T block [d, Vs]
     wf = _lib.lce_workspace_bytes(65536, d, 128256, _lib.LCE_F32)
-    assert wf == 2 * exact + 4 * d * (Vs + pad)
+    assert wf == 4 * (C * (Vs + pad) + Vs * (C + pad) + d * (C + pad)) + 4 * d * (Vs + pad)
     # far below the [N, V] fp32 logits table it replaces
     assert w5 < 65536 * 128256 * 4 / 40
     # growing V past the vocabulary block does not grow the workspace
@@ -193,16 +193,17 @@ def test_backward_step_argument_checks_before_launch():
 
 
 def test_step_workspace_is_bounded():
-    """The fused step adds the transposed W block and, beyond one token chunk,
-    the fp32 dW block accumulator: bounded by constants and d, not by N or V."""
+    """The fused step adds the transposed W block and either G^T (one token
+    chunk: the optimizer epilogue reads it) or the fp32 dW block accumulator
+    (several chunks): bounded by constants and d, not by N or V."""
     bf = _lib.LCE_BF16
     d, Vs, C, pad = 4096, 16384, 8192, 64
     plain3 = _lib.lce_workspace_bytes(8192, d, 128256, bf)
     step3 = _lib.lce_step_workspace_bytes(8192, d, 128256, bf)
-    assert step3 - plain3 == 2 * d * (Vs + pad)                # W^T block, one chunk
+    assert step3 - plain3 == 2 * d * (Vs + pad) + 2 * Vs * (C + pad)   # W^T and G^T blocks
     step4 = _lib.lce_step_workspace_bytes(16384, d, 260000, bf)
     step5 = _lib.lce_step_workspace_bytes(65536, d, 128256, bf)
-    assert step4 == step5 == step3 + 4 * Vs * d                # + fp32 dW block accumulator
+    assert step4 == step5 == plain3 + 2 * d * (Vs + pad) + 4 * Vs * d  # W^T + fp32 dW accumulator
     assert _lib.lce_step_workspace_bytes(1 << 20, d, 128256, bf) - step5 < (1 << 20) * 64 * 13
     assert _lib.lce_step_workspace_bytes(10, 100, 10, bf) == 0
 

@@ -66,6 +66,7 @@ struct Plan {
   int64_t C, Vs;
   int64_t ldG, ldGT, ldHT, ldWT;  // padded row strides (elements)
   size_t off_G, off_GT, off_HT, off_WT, off_D, bwd_bytes;
+  bool has_gt;  // G^T block: fp32 and the one-chunk fused step (bf16 dW reads G K-major)
   bool has_wt;  // W^T block: fp32 (no transposing LDS read) and the fused step
   bool has_d;   // fp32 dW block accumulator: fused step over several token chunks
   size_t total;
@@ -103,12 +104,16 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype, bool step = false) {
   p.ldGT = p.C + kStridePad;
   p.ldHT = p.C + kStridePad;
   p.ldWT = p.Vs + kStridePad;
-  o = 0;
-  p.off_G = o; o += align_up((size_t)p.C * (size_t)p.ldG * p.esz);
-  p.off_GT = o; o += align_up((size_t)p.Vs * (size_t)p.ldGT * p.esz);
-  p.off_HT = o; o += align_up((size_t)d * (size_t)p.ldHT * p.esz);
   p.has_wt = dtype != LCE_BF16 || step;
   p.has_d = step && N > p.C;
+  // the optimizer epilogue (one chunk) reads G^T; the plain bf16 dW store
+  // (also the fused step's accumulation over several chunks) reads G K-major
+  p.has_gt = dtype != LCE_BF16 || (step && !p.has_d);
+  o = 0;
+  p.off_G = o; o += align_up((size_t)p.C * (size_t)p.ldG * p.esz);
+  p.off_GT = o;
+  if (p.has_gt) o += align_up((size_t)p.Vs * (size_t)p.ldGT * p.esz);
+  p.off_HT = o; o += align_up((size_t)d * (size_t)p.ldHT * p.esz);
   p.off_WT = o;
   if (p.has_wt) o += align_up((size_t)d * (size_t)p.ldWT * p.esz);
   p.off_D = o;
@@ -425,7 +430,7 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
   if (st != LCE_OK) return st;
   char* ws = (char*)workspace;
   void* G = ws + p.off_G;
-  void* GT = ws + p.off_GT;
+  void* GT = p.has_gt ? ws + p.off_GT : nullptr;
   void* HT = ws + p.off_HT;
   void* WT = p.has_wt ? ws + p.off_WT : nullptr;
   float* Dacc = p.has_d ? (float*)(ws + p.off_D) : nullptr;
@@ -524,6 +529,8 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     wa.GT = GT;
     wa.HT = HT;
     wa.ldGT = p.ldGT;
+    wa.G = G;
+    wa.ldG = p.ldG;
     wa.ldHT = p.ldHT;
     wa.C = p.C;
     wa.Vs = p.Vs;

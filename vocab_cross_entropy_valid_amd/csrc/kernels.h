@@ -56,10 +56,12 @@ struct DhArgs {
 };
 
 struct DwArgs {
-  const void* GT;  // [Vs][ldGT]
+  const void* GT;  // [Vs][ldGT]: fp32, and the bf16 optimizer epilogue
   const void* HT;  // [d][ldHT]
   int64_t C, Vs, d;
   int64_t ldGT, ldHT;
+  const void* G;   // [C][ldG]: the bf16 plain store reads G K-major instead of G^T
+  int64_t ldG;
   const int32_t* valid_count;
   int64_t c0, v0, V;
   float* dW;

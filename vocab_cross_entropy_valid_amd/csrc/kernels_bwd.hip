@@ -189,7 +189,9 @@ template <> __device__ __forceinline__ void stream2<float>(void* p, float a, flo
 // holds 2 consecutive tokens).  Epilogue: p = exp(z - lse), subtract 1 at the
 // label, scale by w = grad / N_valid (mean) or grad (sum); entries past V or
 // past the valid tokens are 0.  G is written row-major [token][vocab] for the
-// dH contraction and transposed [vocab][token] for the dW contraction.
+// dH contraction (and the bf16 dW store, which reads it K-major) and, where
+// the dW contraction needs it (fp32, the bf16 optimizer epilogue), also
+// transposed [vocab][token].
 template <typename T>
 __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* lds) {
   const int tid = threadIdx.x;
@@ -278,15 +280,19 @@ __device__ __forceinline__ void bwd_g_tile(const BwdGArgs& a, int slot, char* ld
   // accumulator register the 32 lanes of a half-wave cover 128 contiguous
   // bytes.  Non-temporal stores: 1% faster than ordinary ones on the Llama-3
   // head (dW reads the block once, after the whole recompute).
+  // (only where a dW contraction reads it: fp32, and the bf16 optimizer
+  // epilogue; the bf16 dW store reads G K-major)
   const int il0 = tn * kTile + wb * kWaveN + 2 * j;  // local token of nt = 0
   char* GT = (char*)a.GT;
+  if (GT) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      stream2<T>(GT + (vl * a.ldGT + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int64_t vl = vl0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+        stream2<T>(GT + (vl * a.ldGT + il0) * Elem<T>::kSize, acc[mt][0][i], acc[mt][1][i]);
+      }
+  }
 
   char* G = (char*)a.G;
   if constexpr (sizeof(T) == 2) {
@@ -492,8 +498,16 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
   Acc acc;
   zero_acc(acc);
   if constexpr (kStep == 0) {
-    tile_mainloop<T>(acc, lds, make_row_ptrs<false>(bs, tid), make_row_ptrs<false>(as, tid),
-                     nstages, tid);
+    if constexpr (sizeof(T) == 2) {
+      // B = the block's G rows, K-major (token rows past the chunk's valid
+      // count read as zeros): no G^T copy
+      const RowPtrs pg = make_kmajor_ptrs((const char*)a.G, a.ldG * 2, 0, kact,
+                                          (int64_t)tm * kTile, tid);
+      tile_mainloop<T, true>(acc, lds, make_row_ptrs<false>(bs, tid), pg, nstages, tid);
+    } else {
+      tile_mainloop<T>(acc, lds, make_row_ptrs<false>(bs, tid), make_row_ptrs<false>(as, tid),
+                       nstages, tid);
+    }
     // acc[mt][nt][4 g + e] is dW[v_base + 32 nt][k_base + 32 mt + 8 g + e]
     float* out0 = a.dW + a.v0 * a.d;
     const int v_base = tm * kTile + wb * kWaveN + (lane & 31);
