@@ -1146,9 +1146,11 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
 //    (the lane's own values), the B operand the matching K entries, read
 //    straight from the row-major K tile with two transposing reads.
 //  * Key blocks are loaded into registers (buffer loads: rows past S read as
-//    zeros) an iteration ahead and written to LDS at the end of the
-//    iteration before their use.  The last two blocks (the causal diagonal,
-//    the sequence tail) take the masked path.
+//    zeros) two iterations ahead (two register sets) and written to LDS at
+//    the start of the iteration before their use, into the other of two
+//    slots, so that the writes overlap that iteration's products.  The last
+//    two blocks (the causal diagonal, the sequence tail) take the masked
+//    path.
 //  * It also writes D = rowsum(dO O) for the dK / dV pass.
 __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArgs a) {
   constexpr int D = 128;
@@ -1289,25 +1291,28 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwd
       for (int m = 0; m < 8; ++m) mma16(dq[m], dsf[j], tr_frag16(sl + 8192 * j + toff[m]));
   };
 
-  // prologue: block 0 in LDS, block 1 in registers
+  // prologue: block 0 in LDS, blocks 1 and 2 in registers
   load_regs(0, P0{});
   store_regs(0, P0{});
   if (1 < nkb) load_regs(1, P1{});
+  if (2 < nkb) load_regs(2, P0{});
   __syncthreads();
-  // iteration kb: loads of block kb + 2, block kb + 1 written to the other
-  // slot (read in iteration kb - 1) at the end
+  // iteration kb: block kb + 1 (loaded two iterations earlier) written to
+  // the other slot (block kb - 1's, read in iteration kb - 1), block kb + 3
+  // loaded into the register set it freed, block kb computed
   auto iter = [&](int kb, auto par, auto last) {
-    constexpr int P = decltype(par)::value;
+    constexpr int P = decltype(par)::value;  // parity of kb
     constexpr bool kMasked = decltype(last)::value;
     using Pn = std::integral_constant<int, 1 - P>;
-    if (kb + 2 < nkb) load_regs(kb + 2, par);
+    if (kb + 1 < nkb) store_regs(kb + 1, Pn{});
+    if (kb + 3 < nkb) load_regs(kb + 3, Pn{});
+    __builtin_amdgcn_sched_barrier(0);
     if (kMasked) {
       // every key of the block after the wave's queries: nothing to add
       if (!(a.causal && kb * KB > q0w + 15)) block(kb, true);
     } else {
       block(kb, false);
     }
-    if (kb + 1 < nkb) store_regs(kb + 1, Pn{});
     __syncthreads();
   };
   using Masked = std::integral_constant<bool, true>;
