@@ -976,7 +976,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   // Register-staged loads: thread t carries chunk t % 16 of rows t / 16 + 32 i
   // (i < kPre) of the Q and the dO tile, stored at position t % 16 of its row,
   // i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves carry the
-  // block's lse values, odd waves its D values (the waves of a parity write
+  // block's lse values (times log2 e), odd waves its D values (the waves of a parity write
   // identical values).  Block b is loaded during iteration b - 2 and written
   // to LDS at the start of iteration b - 1, into the slot block b - 2 used
   // (two slots), so that the writes overlap the iteration's products instead
@@ -1011,7 +1011,8 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
       *(u32x4*)(sl + lvoff + 8192 * i) = pre[i];
       *(u32x4*)(sl + kQT + lvoff + 8192 * i) = pre[kPre + i];
     }
-    *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = pre_v;
+    // lse in log2 units (one multiply here instead of one per score)
+    *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = (wave & 1) ? pre_v : pre_v * kLog2e;
   };
 
   // per-lane LDS offsets: S / dP fragments (row i16 of a 16-query quarter,
@@ -1071,7 +1072,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
           const int h = 2 * n + hh;
           // rows past S: lse = 0, S = 0, dO = 0, so P = 1 and dS = 0 there,
           // and their dO^T / Q^T entries are 0
-          pv[hh][e] = fast_exp2(fmaf(sc[h][e], c, -l4[h][e] * kLog2e));
+          pv[hh][e] = fast_exp2(fmaf(sc[h][e], c, -l4[h][e]));
           dsv[hh][e] = pv[hh][e] * (dp[h][e] - d4[h][e]);
         }
       pp[n][0] = cvt_pk_bf16(pv[0][0], pv[0][1]);
