@@ -185,7 +185,7 @@ def test_single_row():
     _check(run_path(H, W, y, "bf16"), H, W, y, "bf16")
 
 
-@pytest.mark.parametrize("N", [63, 64, 65, 1023, 1024, 1025, 2049])
+@pytest.mark.parametrize("N", [63, 64, 65, 1023, 1024, 1025, 2049, 8191, 8192, 8193, 16385])
 def test_compaction_boundaries(N):
     announce(f"compaction N={N}")
     H, W, y = workloads.custom(N, 64, 300, seed=N, ignore_frac=0.37)
