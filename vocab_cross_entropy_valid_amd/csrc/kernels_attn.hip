@@ -896,11 +896,15 @@ __device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b) 
 
 // Row-major Q / dO tiles of this pass (256-byte rows of 16 sixteen-byte
 // chunks): chunk c of row r sits at position c ^ swz16(r), swz16(r) =
-// 2 (r % 8) + (r / 8) % 2.  The S / dP fragment reads (16 lanes: one chunk
-// of 16 consecutive rows) hit 16 distinct positions, and so do the
-// transposing reads (32 lanes: chunks 2 m, 2 m + 1 of 8 consecutive rows).
+// 2 (r % 8).  The S / dP fragment reads (16 lanes: one chunk of 16
+// consecutive rows; lane groups 16 g read chunk 4 s + g) and the transposing
+// reads (32 lanes: chunks 2 m, 2 m + 1 of 8 consecutive rows) run at the LDS
+// rate of conflict-free reads on gfx950 (16-byte reads 4 clocks per wave,
+// measured).  Adding (r / 8) % 2 to the swizzle, which separates rows r and
+// r + 8 but pairs the chunk of lane group g with that of group g ^ 1 in rows
+// r ^ 8, halves the rate of the 16-byte reads.
 __device__ __forceinline__ int swz16_offset(int row, int chunk) {
-  return row * 256 + ((chunk ^ (((row & 7) << 1) | ((row >> 3) & 1))) << 4);
+  return row * 256 + ((chunk ^ ((row & 7) << 1)) << 4);
 }
 
 // A fragment of the transposed tile for the 16 x 16 x 32 product: operand row
