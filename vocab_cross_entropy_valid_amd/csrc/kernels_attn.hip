@@ -384,20 +384,33 @@ __device__ __forceinline__ int tt_unit_offset(int row, int u) {
   return tt_chunk_offset<T>(row, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
 }
 
-// rows [row0, row0 + R) of a [S, D] bf16 head into a row-major swizzled tile
-// (rows past S are zeros)
+// rows [row0, row0 + R) of two [S, D] bf16 heads (K and V) into row-major
+// swizzled tiles.  Buffer loads read rows past S as zeros, and every load is
+// issued before the first LDS write, so the staging costs one memory round
+// trip (loads issued before the call, e.g. the first query block, complete
+// in the same wait).
 template <int D, int R, int NT>
-__device__ __forceinline__ void stage_rows(char* dst, const bf16_t* src, int row0, int S, int tid) {
+__device__ __forceinline__ void stage_rows2(char* dst0, const bf16_t* src0, char* dst1,
+                                            const bf16_t* src1, int row0, int S, int tid) {
   constexpr int C = D / 8;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  constexpr int kIt = R * C / NT;
+  static_assert(R * C % NT == 0, "whole 16-byte chunks per thread");
+  const int64_t bytes = row0 < S ? (int64_t)(S - row0) * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t r0 = make_rsrc((const char*)(src0 + (int64_t)row0 * D), bytes);
+  const __amdgpu_buffer_rsrc_t r1 = make_rsrc((const char*)(src1 + (int64_t)row0 * D), bytes);
+  u32x4 v0[kIt], v1[kIt];
 #pragma unroll
-  for (int it = 0; it < (R * C + NT - 1) / NT; ++it) {
+  for (int it = 0; it < kIt; ++it) {
+    const uint32_t off = (uint32_t)(it * NT + tid) * 16u;  // row idx / C, chunk idx % C
+    v0[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, 0));
+    v1[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, 0));
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
     const int idx = it * NT + tid;
-    if (idx >= R * C) break;
-    const int row = idx / C, c = idx % C;
-    const int r = row0 + row;
-    const u32x4 v = r < S ? *(const u32x4*)(src + (int64_t)r * D + 8 * c) : z;
-    *(u32x4*)(dst + k_offset(row, c, C)) = v;
+    const int o = k_offset(idx / C, idx % C, C);
+    *(u32x4*)(dst0 + o) = v0[it];
+    *(u32x4*)(dst1 + o) = v1[it];
   }
 }
 
@@ -678,8 +691,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   {
     char* lk = lds;
     char* lv = lds + kKV;
-    stage_rows<D, kKvKeys, kAttnThreads>(lk, a.K + head, kbase, S, tid);
-    stage_rows<D, kKvKeys, kAttnThreads>(lv, a.V + head, kbase, S, tid);
+    stage_rows2<D, kKvKeys, kAttnThreads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -949,23 +961,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   const int kk = k0w + i16;           // this lane's key
   const float c = a.scale_log2;
 
-  // K and V fragments (B operands of S and dP) for the whole pass
-  u32x4 kf[4], vf[4];
-  {
-    char* lk = lds;
-    char* lv = lds + kKV;
-    stage_rows<D, kKvKeys, kDkv16Threads>(lk, a.K + head, kbase, S, tid);
-    stage_rows<D, kKvKeys, kDkv16Threads>(lv, a.V + head, kbase, S, tid);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ko = k_offset(16 * wave + i16, 4 * s + g, D / 8);
-      kf[s] = *(const u32x4*)(lk + ko);
-      vf[s] = *(const u32x4*)(lv + ko);
-    }
-    __syncthreads();  // the query slots reuse this LDS
-  }
-
   f32x4 dk[8], dv[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
@@ -993,31 +988,61 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   const int srow = tid >> 4;
   const uint32_t gvoff = (uint32_t)swz16_offset(srow, tid & 15);
   const int lvoff = srow * 256 + ((tid & 15) << 4);
-  u32x4 pre[2 * kPre];
+  typedef u32x4 BlockRegs16[2 * kPre];
+  BlockRegs16 pre;
   float pre_v;
   auto slot_of = [&](int qbk) { return lds + ((qbk - qstart) & 1) * kSlot; };
-  auto load_regs = [&](int qbk) {
+  auto load_into = [&](BlockRegs16& r, float& rv_, int qbk) {
     const uint32_t soff = (uint32_t)(qbk * QB) * 256u;
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      pre[i] = __builtin_bit_cast(
+      r[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + 8192 * i, soff, 0));
-      pre[kPre + i] = __builtin_bit_cast(
+      r[kPre + i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + 8192 * i, soff, 0));
     }
-    pre_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                          rv, lane * 4, (uint32_t)(qbk * QB) * 4u, 0));
+    rv_ = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       rv, lane * 4, (uint32_t)(qbk * QB) * 4u, 0));
   };
-  auto store_regs = [&](int qbk) {
+  auto store_from = [&](const BlockRegs16& r, float rv_, int qbk) {
     char* sl = slot_of(qbk);
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      *(u32x4*)(sl + lvoff + 8192 * i) = pre[i];
-      *(u32x4*)(sl + kQT + lvoff + 8192 * i) = pre[kPre + i];
+      *(u32x4*)(sl + lvoff + 8192 * i) = r[i];
+      *(u32x4*)(sl + kQT + lvoff + 8192 * i) = r[kPre + i];
     }
     // lse in log2 units (one multiply here instead of one per score)
-    *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = (wave & 1) ? pre_v : pre_v * kLog2e;
+    *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = (wave & 1) ? rv_ : rv_ * kLog2e;
   };
+  auto load_regs = [&](int qbk) { load_into(pre, pre_v, qbk); };
+  auto store_regs = [&](int qbk) { store_from(pre, pre_v, qbk); };
+
+  // Prologue, one memory round trip: the loads of query blocks qstart (into
+  // a prologue register set) and qstart + 1 (into the loop's) go out first,
+  // then the K / V rows are staged (their wait covers all of them); the K and
+  // V fragments (B operands of S and dP) stay in registers for the whole
+  // pass; block qstart then takes its slot (which reuses the K / V staging
+  // LDS), and block qstart + 1 waits in registers for the first iteration.
+  u32x4 kf[4], vf[4];
+  {
+    BlockRegs16 pre0;
+    float pre0_v;
+    load_into(pre0, pre0_v, qstart);
+    if (qstart + 1 < nq) load_regs(qstart + 1);
+    char* lk = lds;
+    char* lv = lds + kKV;
+    stage_rows2<D, kKvKeys, kDkv16Threads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ko = k_offset(16 * wave + i16, 4 * s + g, D / 8);
+      kf[s] = *(const u32x4*)(lk + ko);
+      vf[s] = *(const u32x4*)(lv + ko);
+    }
+    __syncthreads();
+    store_from(pre0, pre0_v, qstart);
+    __syncthreads();
+  }
 
   // per-lane LDS offsets: S / dP fragments (row i16 of a 16-query quarter,
   // chunk 4 s + g) and the transposing reads of the accumulation
@@ -1097,11 +1122,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
       }
   };
 
-  // prologue: block qstart in LDS, block qstart + 1 in registers
-  load_regs(qstart);
-  store_regs(qstart);
-  if (qstart + 1 < nq) load_regs(qstart + 1);
-  __syncthreads();
   // iteration qbk: block qbk + 1 written to the other slot (block qbk - 1's,
   // read in iteration qbk - 1), block qbk + 2 loaded, block qbk computed.
   // kDiag: a causal block that overlaps the workgroup's keys, skipped by the
@@ -1178,27 +1198,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwd
   const int qc = q < S ? q : S - 1;
   const float c = a.scale_log2;
 
-  // Q and dO fragments (B operands: query i16, dims 32 s + 8 g .. + 7), and
-  // D = rowsum(dO O) of the lane's query (the four lanes of a query each sum
-  // a quarter of the dims)
-  u32x4 qf[4], df[4];
-  float dpart = 0.f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int64_t off = head + (int64_t)qc * D + 32 * s + 8 * g;
-    qf[s] = *(const u32x4*)(a.Q + off);
-    df[s] = *(const u32x4*)(a.dO + off);
-    const f32x4 o0 = *(const f32x4*)(a.O + off);
-    const f32x4 o1 = *(const f32x4*)(a.O + off + 4);
-    dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
-             bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
-             bf16_lo(df[s][3]) * o1[2] + bf16_hi(df[s][3]) * o1[3];
-  }
-  dpart += __shfl_xor(dpart, 16);
-  const float Dq = dpart + __shfl_xor(dpart, 32);
-  if (g == 0 && q < S) a.delta[bh * S + q] = Dq;
-  const float lse2 = (q < S ? a.lse[bh * S + q] : 0.f) * kLog2e;
-
   f32x4 dq[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
@@ -1236,6 +1235,43 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwd
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+
+  // Prologue, one memory round trip: the loads of key blocks 0 and 1 go out
+  // first, then the lane's Q, dO and O rows (their wait covers all of them);
+  // block 0 then takes its slot, block 1 waits in registers for the first
+  // iteration, and block 2 is loaded.
+  load_regs(0, P0{});
+  if (1 < nkb) load_regs(1, P1{});
+  // the Q and dO fragments (B operands: query i16, dims 32 s + 8 g .. + 7), and
+  // D = rowsum(dO O) of the lane's query (the four lanes of a query each sum
+  // a quarter of the dims)
+  u32x4 qf[4], df[4];
+  f32x4 of[8];
+  // lse of the lane's query (0 past S: buffer bounds)
+  const float lse_q = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 make_rsrc((const char*)(a.lse + bh * S), (int64_t)S * 4), (uint32_t)q * 4u, 0, 0));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t off = head + (int64_t)qc * D + 32 * s + 8 * g;
+    qf[s] = *(const u32x4*)(a.Q + off);
+    df[s] = *(const u32x4*)(a.dO + off);
+    of[2 * s] = *(const f32x4*)(a.O + off);
+    of[2 * s + 1] = *(const f32x4*)(a.O + off + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f32x4 o0 = of[2 * s], o1 = of[2 * s + 1];
+    dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
+             bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
+             bf16_lo(df[s][3]) * o1[2] + bf16_hi(df[s][3]) * o1[3];
+  }
+  dpart += __shfl_xor(dpart, 16);
+  const float Dq = dpart + __shfl_xor(dpart, 32);
+  if (g == 0 && q < S) a.delta[bh * S + q] = Dq;
+  const float lse2 = lse_q * kLog2e;
 
   int aoff[4], toff[8];
 #pragma unroll
@@ -1296,10 +1332,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwd
       for (int m = 0; m < 8; ++m) mma16(dq[m], dsf[j], tr_frag16(sl + 8192 * j + toff[m]));
   };
 
-  // prologue: block 0 in LDS, blocks 1 and 2 in registers
-  load_regs(0, P0{});
   store_regs(0, P0{});
-  if (1 < nkb) load_regs(1, P1{});
   if (2 < nkb) load_regs(2, P0{});
   __syncthreads();
   // iteration kb: block kb + 1 (loaded two iterations earlier) written to
