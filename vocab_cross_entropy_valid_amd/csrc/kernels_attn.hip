@@ -357,9 +357,10 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 //  * dK / dV pass: a workgroup takes 128 keys and streams the queries in
 //    blocks: S = Q K^T and dP = dO V^T (lse and D of the block's queries
 //    from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T.  D = 128 runs 8
-//    waves of 16 keys on the 16 x 16 x 32 product (two waves per SIMD,
-//    blocks of 64 queries, attn_bwd_dkv16_kernel); D = 64 runs 4 waves of 32
-//    keys on the 32 x 32 x 16 product (one wave per SIMD, blocks of 32).
+//    waves on the 16 x 16 x 32 product (two waves per SIMD, blocks of 64
+//    queries, attn_bwd_dkv_pair_kernel: per 32 keys one wave for P and dV,
+//    one for dS and dK); D = 64 runs 4 waves of 32 keys on the 32 x 32 x 16
+//    product (one wave per SIMD, blocks of 32).
 //
 // The D = 64 passes run one wave per SIMD and stage their streamed tiles
 // through registers: the next block is loaded while the current one
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
   constexpr int MD = D / 32;
   constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
   constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  static_assert(D == 64, "D = 128 runs attn_bwd_dkv16_kernel");
+  static_assert(D == 64, "D = 128 runs attn_bwd_dkv_pair_kernel");
   constexpr int kTiles = 4;  // Q, dO, and their transposed copies (paired-chunk layout)
   constexpr int kSlot = kTiles * kQT + 2 * kKvQ * 4;
   constexpr int kLds = 2 * kKV > 3 * kSlot ? 2 * kKV : 3 * kSlot;
@@ -872,34 +873,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdAr
     }
 }
 
-// dK / dV pass for D = 128 on v_mfma_f32_16x16x32_bf16, two waves per SIMD.
-// A workgroup of 8 waves takes 128 keys, 16 per wave, and streams the
-// queries in blocks of 32 NH (NH = 2 is launched) through two LDS slots
-// (Q rows, dO rows, lse, D).  Operand layouts of the 16 x 16 x 32 product:
-// A lane l holds row l % 16 with K entries 8 (l / 16) .. + 7, B lane l
-// column l % 16 with the same K entries, the result lane l column l % 16
-// with rows 4 (l / 16) .. + 3.
-//  * S = Q K^T and dP = dO V^T per 16-query quarter h of the block: lane l
-//    (g = l / 16) holds key l % 16 and queries 16 h + 4 g + e (e = 0..3);
-//    K and V stay in registers (the B operands).  Eight independent
-//    accumulation chains for NH = 2.
-//  * dV^T += dO^T P^T and dK^T += Q^T dS^T over K = 32 queries at a time:
-//    the B operand is P (dS) of the lane's 8 queries of that half in the
-//    order above, the A operand the matching dO^T (Q^T) entries, read
-//    straight from the row-major tile with two transposing reads (queries
-//    4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half).  With two waves per
-//    SIMD the accumulation runs right after the softmax of the same block
-//    (deferring it to the next block, next to that block's softmax, was 3%
-//    slower).
-//  * Query blocks are loaded into registers (buffer loads: rows past S read
-//    as zeros, and so add nothing) an iteration ahead and written to LDS at
-//    the start of the iteration before their use, into the other of two
-//    slots, so that the writes overlap that iteration's products (3% faster
-//    than writing them in front of its closing barrier).
-//  * The causal blocks that overlap the workgroup's keys (the first 128 / QB)
-//    take the masked path; the main loop carries no mask.
+// Shared by the D = 128 backward passes: 8 waves (two per SIMD) on
+// v_mfma_f32_16x16x32_bf16.  Operand layouts of the 16 x 16 x 32 product: A
+// lane l holds row l % 16 with K entries 8 (l / 16) .. + 7, B lane l column
+// l % 16 with the same K entries, the result lane l column l % 16 with rows
+// 4 (l / 16) .. + 3.
 namespace {
-constexpr int kDkv16Threads = 512;
+constexpr int k16Threads = 512;
 
 __device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -937,19 +917,54 @@ __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
 }
 }  // namespace
 
-template <int NH>
-__global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBwdArgs a) {
+// dK / dV pass for D = 128, split by gradient: a workgroup of 8 waves takes
+// 128 keys as 4 pairs of 32 and streams the queries in blocks of 64 through
+// two LDS slots (Q rows, dO rows in the swizzle of swz16_offset, lse, D).
+// Of the two waves of a pair, which share a SIMD (waves w and w + 4), the P
+// wave computes S = Q K^T, the softmax P and dV^T += dO^T P^T, the dS wave
+// dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS^T.  Against one wave per
+// 16 keys doing all four products, every Q / dO fragment read from LDS
+// feeds two MFMAs (the pair's two 16-key tiles) instead of one, and a
+// SIMD's vector work (the exponentials in the first half of an iteration,
+// dS in the second) sits next to the other wave's MFMAs.
+//  * S and dP per key tile t and 16-query quarter h of the block: lane l
+//    (g = l / 16) holds key 16 t + l % 16 and queries 16 h + 4 g + e
+//    (e = 0..3); the K (or V) rows of the pair stay in registers as the B
+//    operands.
+//  * P goes from the P wave to the dS wave through LDS, rounded to bf16 as
+//    the dV product takes it, in the lane / register order both waves
+//    share; a second barrier in each iteration separates its writes from
+//    the reads.  (Sending fp32 P, with dP - D formed while the P wave
+//    exponentiates, measured 2-4% slower.)
+//  * dV^T += dO^T P^T and dK^T += Q^T dS^T over K = 32 queries at a time:
+//    the B operand is P (dS) of the lane's 8 queries of that half in the
+//    order above, the A operand the matching dO^T (Q^T) entries, read
+//    straight from the row-major tile with two transposing reads (queries
+//    4 g .. 4 g + 3 and 16 + 4 g .. + 3 of the half); each such fragment
+//    feeds both key tiles.
+//  * Query blocks are loaded into registers (buffer loads: rows past S read
+//    as zeros, and so add nothing) an iteration ahead and written to LDS at
+//    the start of the iteration before their use, into the other slot, so
+//    that the writes overlap that iteration's products.  The prologue is
+//    one memory round trip: the first block's loads go out beside the K / V
+//    staging loads.
+//  * The causal blocks that overlap the workgroup's keys (the first two)
+//    take the masked path, with the mask applied to S only (dS = P (dP - D)
+//    is then 0); the main loop carries no mask.
+__global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBwdArgs a) {
   constexpr int D = 128;
-  constexpr int QB = 32 * NH;             // queries per block
+  constexpr int QB = 64;                  // queries per block
   constexpr int kKV = kKvKeys * D * 2;    // K (or V) rows of the workgroup
   constexpr int kQT = QB * D * 2;         // one block's Q (or dO) tile
   constexpr int kSlot = 2 * kQT + 512;    // Q, dO, lse[64], D[64]
-  constexpr int kLds = 2 * kKV > 2 * kSlot ? 2 * kKV : 2 * kSlot;
+  constexpr int kXch = 4 * 4 * 64 * 16;   // P of 4 pairs: 4 fragments x 64 lanes x 16 B
+  constexpr int kLds = 2 * kKV > 2 * kSlot + kXch ? 2 * kKV : 2 * kSlot + kXch;
   constexpr int kPre = QB / 32;           // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
   const int i16 = lane & 15;
   const int g = lane >> 4;
   const int S = a.S;
@@ -957,29 +972,17 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   const int64_t bh = blockIdx.x % a.BH;
   const int64_t head = bh * (int64_t)S * D;
   const int kbase = kblk * kKvKeys;
-  const int k0w = kbase + 16 * wave;  // first key of this wave
-  const int kk = k0w + i16;           // this lane's key
+  const int k0p = kbase + 32 * pair;  // first key of this pair
   const float c = a.scale_log2;
-
-  f32x4 dk[8], dv[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dk[m][e] = 0.f;
-      dv[m][e] = 0.f;
-    }
+  char* xch = lds + 2 * kSlot + pair * 4096 + lane * 16;  // this lane's P fragments
 
   const int nq = (S + QB - 1) / QB;
   const int qstart = a.causal ? kbase / QB : 0;
-  // Register-staged loads: thread t carries chunk t % 16 of rows t / 16 + 32 i
-  // (i < kPre) of the Q and the dO tile, stored at position t % 16 of its row,
-  // i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves carry the
-  // block's lse values (times log2 e), odd waves its D values (the waves of a parity write
-  // identical values).  Block b is loaded during iteration b - 2 and written
-  // to LDS at the start of iteration b - 1, into the slot block b - 2 used
-  // (two slots), so that the writes overlap the iteration's products instead
-  // of queueing in front of its closing barrier.
+  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 and
+  // t / 16 + 32 of the Q and the dO tile, stored at position t % 16 of its
+  // row, i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves
+  // carry the block's lse values (times log2 e), odd waves its D values (the
+  // waves of a parity write identical values)
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)(a.Q + head), (int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)(a.dO + head), (int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t rv = (wave & 1)
@@ -1017,33 +1020,6 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
   auto load_regs = [&](int qbk) { load_into(pre, pre_v, qbk); };
   auto store_regs = [&](int qbk) { store_from(pre, pre_v, qbk); };
 
-  // Prologue, one memory round trip: the loads of query blocks qstart (into
-  // a prologue register set) and qstart + 1 (into the loop's) go out first,
-  // then the K / V rows are staged (their wait covers all of them); the K and
-  // V fragments (B operands of S and dP) stay in registers for the whole
-  // pass; block qstart then takes its slot (which reuses the K / V staging
-  // LDS), and block qstart + 1 waits in registers for the first iteration.
-  u32x4 kf[4], vf[4];
-  {
-    BlockRegs16 pre0;
-    float pre0_v;
-    load_into(pre0, pre0_v, qstart);
-    if (qstart + 1 < nq) load_regs(qstart + 1);
-    char* lk = lds;
-    char* lv = lds + kKV;
-    stage_rows2<D, kKvKeys, kDkv16Threads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ko = k_offset(16 * wave + i16, 4 * s + g, D / 8);
-      kf[s] = *(const u32x4*)(lk + ko);
-      vf[s] = *(const u32x4*)(lv + ko);
-    }
-    __syncthreads();
-    store_from(pre0, pre0_v, qstart);
-    __syncthreads();
-  }
-
   // per-lane LDS offsets: S / dP fragments (row i16 of a 16-query quarter,
   // chunk 4 s + g) and the transposing reads of the accumulation
   int aoff[4], toff[8];
@@ -1055,107 +1031,196 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
     const int dim = 16 * m + 4 * (lane & 3);
     toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
   }
-  // S and dP of block qbk, its softmax, then dV^T += dO^T P^T and
-  // dK^T += Q^T dS^T over the 32 queries of each half (P and dS as the B
-  // operands, one per half)
-  auto block = [&](int qbk, const bool masked) {
-    const char* sl = slot_of(qbk);
-    f32x4 sc[2 * NH], dp[2 * NH];  // 16-query quarters
+
+  // The two roles take separate code paths, each with its own registers.
+  auto run = [&](auto role) {
+    constexpr bool kP = decltype(role)::value;
+    // K (P wave) or V (dS wave) fragments of the pair's two 16-key tiles:
+    // B operands of S and dP for the whole pass
+    u32x4 bf[2][4];
+    f32x4 acc[2][8];  // dV^T (P wave) or dK^T (dS wave) per key tile
 #pragma unroll
-    for (int h = 0; h < 2 * NH; ++h)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[h][e] = 0.f;
-        dp[h][e] = 0.f;
-      }
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+        for (int e = 0; e < 4; ++e) acc[t][m][e] = 0.f;
+
+    // prologue in one memory round trip: the loads of query blocks qstart
+    // (into a prologue register set) and qstart + 1 (into the loop's) go out
+    // first, then the K / V rows are staged (their wait covers all of them);
+    // block qstart then takes its slot (which reuses the K / V staging LDS),
+    // and block qstart + 1 waits in registers for the first iteration
+    {
+      BlockRegs16 pre0;
+      float pre0_v;
+      load_into(pre0, pre0_v, qstart);
+      if (qstart + 1 < nq) load_regs(qstart + 1);
+      char* lk = lds;
+      char* lv = lds + kKV;
+      stage_rows2<D, kKvKeys, k16Threads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
+      __syncthreads();
+      const char* lb = kP ? lk : lv;
 #pragma unroll
-      for (int h = 0; h < 2 * NH; ++h) {
-        mma16(sc[h], *(const u32x4*)(sl + aoff[s] + 4096 * h), kf[s]);
-        mma16(dp[h], *(const u32x4*)(sl + kQT + aoff[s] + 4096 * h), vf[s]);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    const float* lv = (const float*)(sl + 2 * kQT);
-    f32x4 l4[2 * NH], d4[2 * NH];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int h = 0; h < 2 * NH; ++h) {
-      l4[h] = *(const f32x4*)(lv + 16 * h + 4 * g);
-      d4[h] = *(const f32x4*)(lv + 64 + 16 * h + 4 * g);
+        for (int s = 0; s < 4; ++s)
+          bf[t][s] = *(const u32x4*)(lb + k_offset(32 * pair + 16 * t + i16, 4 * s + g, D / 8));
+      __syncthreads();
+      store_from(pre0, pre0_v, qstart);
+      __syncthreads();
     }
-    if (masked) {
+
+    // one block: products, then (after the middle barrier) the accumulation
+    auto block = [&](int qbk, const bool masked, const bool live) {
+      const char* sl = slot_of(qbk);
+      f32x4 sc[2][4];  // S (P wave) or dP (dS wave): key tile x 16-query quarter
+      u32x4 pp[2][2];  // P (bf16) per key tile and 32-query half, B operand order
+      if (live) {
 #pragma unroll
-      for (int h = 0; h < 2 * NH; ++h)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sc[h][e] = (qbk * QB + 16 * h + 4 * g + e < kk) ? -INFINITY : sc[h][e];
-    }
-    u32x4 pp[NH], ps[NH];
+          for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int n = 0; n < NH; ++n) {
-      float pv[2][4], dsv[2][4];
+            for (int e = 0; e < 4; ++e) sc[t][h][e] = 0.f;
+        const char* op = sl + (kP ? 0 : kQT);  // Q or dO tile
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int h = 2 * n + hh;
-          // rows past S: lse = 0, S = 0, dO = 0, so P = 1 and dS = 0 there,
-          // and their dO^T / Q^T entries are 0
-          pv[hh][e] = fast_exp2(fmaf(sc[h][e], c, -l4[h][e]));
-          dsv[hh][e] = pv[hh][e] * (dp[h][e] - d4[h][e]);
+          for (int h = 0; h < 4; ++h) {
+            const u32x4 af = *(const u32x4*)(op + aoff[s] + 4096 * h);
+            mma16(sc[0][h], af, bf[0][s]);
+            mma16(sc[1][h], af, bf[1][s]);
+          }
+        // the first 6 fragment reads go out together, then one read after
+        // every two MFMAs (the compiler's order waits on each read right in
+        // front of its MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int q = 0; q < 10; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      pp[n][0] = cvt_pk_bf16(pv[0][0], pv[0][1]);
-      pp[n][1] = cvt_pk_bf16(pv[0][2], pv[0][3]);
-      pp[n][2] = cvt_pk_bf16(pv[1][0], pv[1][1]);
-      pp[n][3] = cvt_pk_bf16(pv[1][2], pv[1][3]);
-      ps[n][0] = cvt_pk_bf16(dsv[0][0], dsv[0][1]);
-      ps[n][1] = cvt_pk_bf16(dsv[0][2], dsv[0][3]);
-      ps[n][2] = cvt_pk_bf16(dsv[1][0], dsv[1][1]);
-      ps[n][3] = cvt_pk_bf16(dsv[1][2], dsv[1][3]);
-    }
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kP) {
+          const float* lv = (const float*)(sl + 2 * kQT);
+          f32x4 l4[4];
 #pragma unroll
-    for (int n = 0; n < NH; ++n)
+          for (int h = 0; h < 4; ++h) l4[h] = *(const f32x4*)(lv + 16 * h + 4 * g);
+          if (masked) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        mma16(dv[m], tr_frag16(sl + kQT + 8192 * n + toff[m]), pp[n]);
-        mma16(dk[m], tr_frag16(sl + 8192 * n + toff[m]), ps[n]);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  sc[t][h][e] = (qbk * QB + 16 * h + 4 * g + e < k0p + 16 * t + i16) ? -INFINITY
+                                                                                      : sc[t][h][e];
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              float pv[2][4];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  pv[hh][e] = fast_exp2(fmaf(sc[t][2 * n + hh][e], c, -l4[2 * n + hh][e]));
+              pp[t][n][0] = cvt_pk_bf16(pv[0][0], pv[0][1]);
+              pp[t][n][1] = cvt_pk_bf16(pv[0][2], pv[0][3]);
+              pp[t][n][2] = cvt_pk_bf16(pv[1][0], pv[1][1]);
+              pp[t][n][3] = cvt_pk_bf16(pv[1][2], pv[1][3]);
+              *(u32x4*)(xch + (2 * t + n) * 1024) = pp[t][n];
+            }
+        }
       }
-  };
-
-  // iteration qbk: block qbk + 1 written to the other slot (block qbk - 1's,
-  // read in iteration qbk - 1), block qbk + 2 loaded, block qbk computed.
-  // kDiag: a causal block that overlaps the workgroup's keys, skipped by the
-  // waves whose keys all come after its queries and masked for the others
-  auto iter = [&](int qbk, auto diag) {
-    constexpr bool kDiag = decltype(diag)::value;
-    if (qbk + 1 < nq) store_regs(qbk + 1);
-    if (qbk + 2 < nq) load_regs(qbk + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kDiag) {
-      if (qbk * QB + QB - 1 >= k0w) block(qbk, qbk * QB < k0w + 16);
-    } else {
-      block(qbk, false);
-    }
-    __syncthreads();
-  };
-  int qbk = qstart;
-  if (a.causal) {
-    // the workgroup's 128 keys span blocks qstart .. qstart + 128 / QB - 1
-    const int qd = min(qstart + kKvKeys / QB, nq);
-    for (; qbk < qd; ++qbk) iter(qbk, std::integral_constant<bool, true>{});
-  }
-  for (; qbk < nq; ++qbk) iter(qbk, std::integral_constant<bool, false>{});
-
-  if (kk >= S) return;
-  float* dKk = a.dK + head + (int64_t)kk * D;
-  float* dVk = a.dV + head + (int64_t)kk * D;
+      __syncthreads();  // P written
+      if (live) {
+        if (!kP) {
+          // dS = P (dP - D), P as the P wave rounded it for dV
+          const float* dv4 = (const float*)(sl + 2 * kQT + 256);
+          f32x4 d4[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int d0 = 16 * m + 4 * g;
-    f32x4 vk = {dk[m][0] * a.scale, dk[m][1] * a.scale, dk[m][2] * a.scale, dk[m][3] * a.scale};
-    *(f32x4*)(dKk + d0) = vk;
-    *(f32x4*)(dVk + d0) = dv[m];
-  }
+          for (int h = 0; h < 4; ++h) d4[h] = *(const f32x4*)(dv4 + 16 * h + 4 * g);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const u32x4 pw = *(const u32x4*)(xch + (2 * t + n) * 1024);
+              float dsv[2][4];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                  const uint32_t w = pw[2 * hh + e];
+                  dsv[hh][2 * e] = bf16_lo(w) * (sc[t][2 * n + hh][2 * e] - d4[2 * n + hh][2 * e]);
+                  dsv[hh][2 * e + 1] =
+                      bf16_hi(w) * (sc[t][2 * n + hh][2 * e + 1] - d4[2 * n + hh][2 * e + 1]);
+                }
+              pp[t][n][0] = cvt_pk_bf16(dsv[0][0], dsv[0][1]);
+              pp[t][n][1] = cvt_pk_bf16(dsv[0][2], dsv[0][3]);
+              pp[t][n][2] = cvt_pk_bf16(dsv[1][0], dsv[1][1]);
+              pp[t][n][3] = cvt_pk_bf16(dsv[1][2], dsv[1][3]);
+            }
+        }
+        // dV^T += dO^T P^T (P wave) or dK^T += Q^T dS^T (dS wave), K = 32
+        // queries per half; each transposed fragment feeds both key tiles
+        const char* tp = sl + (kP ? kQT : 0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const u32x4 tf = tr_frag16(tp + 8192 * n + toff[m]);
+            mma16(acc[0][m], tf, pp[0][n]);
+            mma16(acc[1][m], tf, pp[1][n]);
+          }
+      }
+    };
+
+    // iteration qbk: block qbk + 1 written to the other slot, block qbk + 2
+    // loaded, block qbk computed.  kDiag: a causal block that overlaps the
+    // workgroup's keys, skipped by the pairs whose keys all come after its
+    // queries and masked for the others
+    auto iter = [&](int qbk, auto diag) {
+      constexpr bool kDiag = decltype(diag)::value;
+      if (qbk + 1 < nq) store_regs(qbk + 1);
+      if (qbk + 2 < nq) load_regs(qbk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kDiag)
+        block(qbk, qbk * QB < k0p + 32, qbk * QB + QB - 1 >= k0p);
+      else
+        block(qbk, false, true);
+      __syncthreads();
+    };
+    int qbk = qstart;
+    if (a.causal) {
+      const int qd = min(qstart + kKvKeys / QB, nq);
+      for (; qbk < qd; ++qbk) iter(qbk, std::integral_constant<bool, true>{});
+    }
+    for (; qbk < nq; ++qbk) iter(qbk, std::integral_constant<bool, false>{});
+
+    float* out = kP ? a.dV : a.dK;
+    const float sc_out = kP ? 1.f : a.scale;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kk = k0p + 16 * t + i16;
+      if (kk < S) {
+        float* row = out + head + (int64_t)kk * D;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          f32x4 v = {acc[t][m][0] * sc_out, acc[t][m][1] * sc_out, acc[t][m][2] * sc_out,
+                     acc[t][m][3] * sc_out};
+          *(f32x4*)(row + 16 * m + 4 * g) = v;
+        }
+      }
+    }
+  };
+  if (wave < 4)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
 }
 
 // dQ pass for D = 128 on the 16 x 16 x 32 product, two waves per SIMD: a
@@ -1177,7 +1242,7 @@ __global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dkv16_kernel(AttnBw
 //    two blocks (the causal diagonal, the sequence tail) take the masked
 //    path.
 //  * It also writes D = rowsum(dO O) for the dK / dV pass.
-__global__ __launch_bounds__(kDkv16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArgs a) {
   constexpr int D = 128;
   constexpr int KB = 64;               // keys per block
   constexpr int kT = KB * D * 2;       // one block's K (or V) tile
@@ -1389,7 +1454,7 @@ hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
   const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
   const dim3 grid((unsigned)(nqb * a.BH));
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dq16_kernel, grid, dim3(kDkv16Threads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq16_kernel, grid, dim3(k16Threads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
@@ -1400,7 +1465,7 @@ hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s) {
   const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
   const dim3 grid((unsigned)(nkb * a.BH));
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dkv16_kernel<2>, grid, dim3(kDkv16Threads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_pair_kernel, grid, dim3(k16Threads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
