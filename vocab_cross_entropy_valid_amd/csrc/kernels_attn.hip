@@ -951,35 +951,42 @@ __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
 //  * The causal blocks that overlap the workgroup's keys (the first two)
 //    take the masked path, with the mask applied to S only (dS = P (dP - D)
 //    is then 0); the main loop carries no mask.
-__global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBwdArgs a) {
+//  * NP pairs per workgroup (32 NP keys).  NP = 4 is launched: NP = 2 (two
+//    workgroups per CU, each staging every query block for its 64 keys) ran
+//    15% slower.
+template <int NP>
+__global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(AttnBwdArgs a) {
   constexpr int D = 128;
   constexpr int QB = 64;                  // queries per block
-  constexpr int kKV = kKvKeys * D * 2;    // K (or V) rows of the workgroup
+  constexpr int NT = 128 * NP;            // threads
+  constexpr int KK = 32 * NP;             // keys of the workgroup
+  constexpr int kKV = KK * D * 2;         // K (or V) rows of the workgroup
   constexpr int kQT = QB * D * 2;         // one block's Q (or dO) tile
   constexpr int kSlot = 2 * kQT + 512;    // Q, dO, lse[64], D[64]
-  constexpr int kXch = 4 * 4 * 64 * 16;   // P of 4 pairs: 4 fragments x 64 lanes x 16 B
+  constexpr int kXch = NP * 4 * 64 * 16;  // P of the pairs: 4 fragments x 64 lanes x 16 B
   constexpr int kLds = 2 * kKV > 2 * kSlot + kXch ? 2 * kKV : 2 * kSlot + kXch;
-  constexpr int kPre = QB / 32;           // 16-byte chunks per thread per tile
+  constexpr int kRows = NT / 16;          // tile rows staged per pass
+  constexpr int kPre = QB / kRows;        // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave & 3;
+  const int pair = wave % NP;
   const int i16 = lane & 15;
   const int g = lane >> 4;
   const int S = a.S;
   const int kblk = (int)(blockIdx.x / a.BH);
   const int64_t bh = blockIdx.x % a.BH;
   const int64_t head = bh * (int64_t)S * D;
-  const int kbase = kblk * kKvKeys;
+  const int kbase = kblk * KK;
   const int k0p = kbase + 32 * pair;  // first key of this pair
   const float c = a.scale_log2;
   char* xch = lds + 2 * kSlot + pair * 4096 + lane * 16;  // this lane's P fragments
 
   const int nq = (S + QB - 1) / QB;
   const int qstart = a.causal ? kbase / QB : 0;
-  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 and
-  // t / 16 + 32 of the Q and the dO tile, stored at position t % 16 of its
+  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 +
+  // kRows i of the Q and the dO tile, stored at position t % 16 of its
   // row, i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves
   // carry the block's lse values (times log2 e), odd waves its D values (the
   // waves of a parity write identical values)
@@ -1000,9 +1007,9 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBw
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       r[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + 8192 * i, soff, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + 256 * kRows * i, soff, 0));
       r[kPre + i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + 8192 * i, soff, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + 256 * kRows * i, soff, 0));
     }
     rv_ = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        rv, lane * 4, (uint32_t)(qbk * QB) * 4u, 0));
@@ -1011,8 +1018,8 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBw
     char* sl = slot_of(qbk);
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      *(u32x4*)(sl + lvoff + 8192 * i) = r[i];
-      *(u32x4*)(sl + kQT + lvoff + 8192 * i) = r[kPre + i];
+      *(u32x4*)(sl + lvoff + 256 * kRows * i) = r[i];
+      *(u32x4*)(sl + kQT + lvoff + 256 * kRows * i) = r[kPre + i];
     }
     // lse in log2 units (one multiply here instead of one per score)
     *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = (wave & 1) ? rv_ : rv_ * kLog2e;
@@ -1058,7 +1065,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBw
       if (qstart + 1 < nq) load_regs(qstart + 1);
       char* lk = lds;
       char* lv = lds + kKV;
-      stage_rows2<D, kKvKeys, k16Threads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
+      stage_rows2<D, KK, NT>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
       __syncthreads();
       const char* lb = kP ? lk : lv;
 #pragma unroll
@@ -1196,7 +1203,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBw
     };
     int qbk = qstart;
     if (a.causal) {
-      const int qd = min(qstart + kKvKeys / QB, nq);
+      const int qd = min(qstart + (KK + QB - 1) / QB, nq);
       for (; qbk < qd; ++qbk) iter(qbk, std::integral_constant<bool, true>{});
     }
     for (; qbk < nq; ++qbk) iter(qbk, std::integral_constant<bool, false>{});
@@ -1217,7 +1224,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dkv_pair_kernel(AttnBw
       }
     }
   };
-  if (wave < 4)
+  if (wave < NP)
     run(std::integral_constant<bool, true>{});
   else
     run(std::integral_constant<bool, false>{});
@@ -1472,12 +1479,16 @@ hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
 
 hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s) {
   if (a.S <= 0 || a.BH <= 0) return hipSuccess;
+  if (D == 128) {
+    constexpr int NP = 4;
+    const int64_t nkb = (a.S + 32 * NP - 1) / (32 * NP);
+    hipLaunchKernelGGL(attn_bwd_dkv_pair_kernel<NP>, dim3((unsigned)(nkb * a.BH)),
+                       dim3(128 * NP), 0, s, a);
+    return hipGetLastError();
+  }
   const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
-  const dim3 grid((unsigned)(nkb * a.BH));
-  if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dkv_pair_kernel, grid, dim3(k16Threads), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 
