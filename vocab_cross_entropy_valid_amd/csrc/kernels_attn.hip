@@ -229,6 +229,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
           Mma<bf16_t>::run(sc[mt], af, qf[s]);
         }
       }
+      // the first 4 fragment reads go out together, then one read after each
+      // MFMA (the compiler's order waits on each read right in front of its
+      // MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int q = 0; q < 2 * KS - 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
 
       // mask: keys past the end, and past the query under a causal mask
       const bool tail = k0 + kKBlock > S;
