@@ -49,6 +49,9 @@ CASES = [
     (1, 1, 300, 128, False, 605),
     (2, 2, 130, 128, True, 606),     # second query block holds 2 queries
     (1, 4, 512, 128, True, 607),     # several query blocks, diagonal skips
+    # B * H a multiple of 8: the blocks of a head run back to back on one XCD
+    (2, 4, 300, 128, True, 608),
+    (1, 8, 130, 64, False, 609),
 ]
 
 
@@ -161,6 +164,10 @@ BWD_CASES = [
     (2, 1, 96, 128, True, 629),      # three query blocks (every LDS slot used once)
     (1, 2, 700, 128, True, 630),     # 11 blocks of 64 queries: odd count, ragged tail
     (1, 1, 384, 128, False, 631),    # non-causal, 6 blocks of 64 (no masked path)
+    # B * H a multiple of 8: the blocks of a head run back to back on one XCD
+    (2, 4, 300, 128, True, 632),
+    (1, 8, 200, 64, True, 633),
+    (1, 16, 257, 128, False, 634),
 ]
 
 
