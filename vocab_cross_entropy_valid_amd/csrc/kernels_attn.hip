@@ -376,44 +376,20 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, hipStream_t s) {
 // probabilities are never stored in the backward pass either.  Two passes,
 // no atomics (results are deterministic):
 //
-//  * dQ pass: a workgroup takes 128 queries and streams the keys in blocks
-//    of 64: S^T = K Q^T and dP^T = V dO^T on the MFMA (Q and dO fragments
-//    stay in registers), dS formed in the lane, dQ += dS K.  It also writes
-//    D.  D = 128 runs 8 waves of 16 queries on the 16 x 16 x 32 product (two
-//    waves per SIMD, attn_bwd_dq16_kernel); D = 64 runs 4 waves of 32
-//    queries on the 32 x 32 x 16 product (one wave per SIMD, lane = query,
-//    dQ^T += K^T dS^T with K^T in the paired-chunk order of the forward's
-//    V^T).
-//  * dK / dV pass: a workgroup takes 128 keys and streams the queries in
-//    blocks: S = Q K^T and dP = dO V^T (lse and D of the block's queries
-//    from LDS), then dV^T += dO^T P^T and dK^T += Q^T dS^T.  D = 128 runs 8
-//    waves on the 16 x 16 x 32 product (two waves per SIMD, blocks of 64
-//    queries, attn_bwd_dkv_pair_kernel: per 32 keys one wave for P and dV,
-//    one for dS and dK); D = 64 runs 4 waves of 32 keys on the 32 x 32 x 16
-//    product (one wave per SIMD, blocks of 32).
+//  * dQ pass (attn_bwd_dq16_kernel<D>): a workgroup of 8 waves takes 128
+//    queries, 16 per wave, and streams the keys in blocks of 64: S^T = K Q^T
+//    and dP^T = V dO^T on the 16 x 16 x 32 product (Q and dO fragments stay
+//    in registers), dS formed in the lane, dQ += dS K.  It also writes D.
+//  * dK / dV pass (attn_bwd_dkv_pair_kernel<4, D>): a workgroup of 8 waves
+//    takes 128 keys as 4 pairs of 32 and streams the queries in blocks of 64:
+//    per pair one wave computes S, P and dV^T += dO^T P^T, the other dP, dS
+//    and dK^T += Q^T dS^T.
 //
-// The D = 64 passes run one wave per SIMD and stage their streamed tiles
-// through registers: the next block is loaded while the current one
-// computes, and each thread's load unit (4 rows x 8 dims) feeds both the
-// row-major and the transposed LDS copy.  The dQ pass keeps two LDS slots,
-// the dK / dV pass three (its accumulation runs one block late); one barrier
-// per block.  The D = 128 passes read the transposed operands straight from
-// row-major tiles (transposing LDS reads) and stage through buffer loads.
+// Both read their transposed operands straight from row-major tiles
+// (transposing LDS reads) and stage the streamed tiles through registers
+// with buffer loads; two waves per SIMD for D = 128, four for D = 64.
 
 namespace {
-
-// transposed tile of T keys (or queries) per row: 16-byte chunks pairing
-// units u0 and u0 + 2 of 4 entries, XOR-swizzled by (row / 2) % (T / 8)
-template <int T>
-__device__ __forceinline__ int tt_chunk_offset(int row, int c) {
-  return row * (T * 2) + ((c ^ ((row >> 1) & (T / 8 - 1))) << 4);
-}
-
-template <int T>
-__device__ __forceinline__ int tt_unit_offset(int row, int u) {
-  const int u0 = u & ~2;
-  return tt_chunk_offset<T>(row, (u0 >> 1) | (u0 & 1)) + ((u >> 1) & 1) * 8;
-}
 
 // rows [row0, row0 + R) of two [S, D] bf16 heads (K and V) into row-major
 // swizzled tiles.  Buffer loads read rows past S as zeros, and every load is
@@ -448,466 +424,9 @@ __device__ __forceinline__ void stage_rows2(char* dst0, const bf16_t* src0, char
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// A load unit: rows 4 kg .. 4 kg + 3 and dims 8 dg .. 8 dg + 7 of an R-row
-// tile of a [S, D] head, unit = dg * (R / 4) + kg.  The rows are clamped to
-// S - 1 at load time (always in bounds) and zeroed at store time.
-template <int D, int R>
-__device__ __forceinline__ void load_unit(u32x4 (&v)[4], const bf16_t* src, int row0, int S,
-                                          int unit) {
-  const int kg = unit % (R / 4);
-  const int dg = unit / (R / 4);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = min(row0 + 4 * kg + q, S - 1);
-    v[q] = *(const u32x4*)(src + (int64_t)r * D + 8 * dg);
-  }
-}
-
-// The unit into the row-major swizzled tile rm (the layout of stage_rows)
-// and, transposed (row = dimension, entries = the tile's R rows), into the
-// paired-chunk tile tt of tt_unit_offset<R>; with kT false the row-major
-// copy only.
-template <int D, int R, bool kT = true>
-__device__ __forceinline__ void store_unit(const u32x4 (&vin)[4], char* rm, char* tt, int row0,
-                                           int S, int unit) {
-  constexpr int C = D / 8;
-  const int kg = unit % (R / 4);
-  const int dg = unit / (R / 4);
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  u32x4 v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    v[q] = row0 + 4 * kg + q < S ? vin[q] : z;
-    *(u32x4*)(rm + k_offset(4 * kg + q, dg, C)) = v[q];
-  }
-  if (!kT) return;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    u32x2 u;
-    u[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
-    u[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
-    *(u32x2*)(tt + tt_unit_offset<R>(8 * dg + e, kg)) = u;
-  }
-}
-
 }  // namespace
 
-// dQ pass (and D = rowsum(dO O)).  One wave per SIMD: the next key block is
-// loaded into registers while the current one computes (one load unit feeds
-// K row-major and K^T; V row-major), two LDS slots, one barrier per block;
-// the fragment reads of each phase are issued together into their own
-// registers.
-template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
-  constexpr int C = D / 8;
-  constexpr int KS = D / 16;
-  constexpr int MD = D / 32;
-  constexpr int kTile = kKBlock * D * 2;  // 64 rows x D (= D rows x 64 entries)
-  static_assert(D == 64, "D = 128 runs attn_bwd_dq16_kernel");
-  constexpr int kSlot = 3 * kTile;  // K rows, K^T (paired-chunk layout), V rows
-  __shared__ __attribute__((aligned(16))) char lds[2 * kSlot];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 31;
-  const int h = lane >> 5;
-  const int S = a.S;
-  const int nqb = (S + kQBlock - 1) / kQBlock;
-  int qb;
-  int64_t bh;
-  xcd_head_block(nqb, a.BH, qb, bh);
-  qb = nqb - 1 - qb;
-  const int64_t head = bh * (int64_t)S * D;
-  const int q0 = qb * kQBlock + 32 * wave;
-  const int q = q0 + j;
-  const int qc = q < S ? q : S - 1;
-
-  // Q and dO fragments (B operands), and D = rowsum(dO O) of this lane's query
-  u32x4 qf[KS], df[KS];
-  float dpart = 0.f;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int64_t off = head + (int64_t)qc * D + 16 * s + 8 * h;
-    qf[s] = *(const u32x4*)(a.Q + off);
-    df[s] = *(const u32x4*)(a.dO + off);
-    const f32x4 o0 = *(const f32x4*)(a.O + off);
-    const f32x4 o1 = *(const f32x4*)(a.O + off + 4);
-    dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
-             bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
-             bf16_lo(df[s][3]) * o1[2] + bf16_hi(df[s][3]) * o1[3];
-  }
-  const float Dq = dpart + __shfl_xor(dpart, 32);
-  const float lse2 = a.lse[bh * S + qc] * kLog2e;
-  if (h == 0 && q < S) a.delta[bh * S + q] = Dq;
-  const float c = a.scale_log2;
-
-  f32x16 dq[MD];
-#pragma unroll
-  for (int m = 0; m < MD; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dq[m][i] = 0.f;
-
-  const int kend = a.causal ? min(S, (qb + 1) * kQBlock) : S;
-  const int nkb = (kend + kKBlock - 1) / kKBlock;
-  const bf16_t* Kh = a.K + head;
-  const bf16_t* Vh = a.V + head;
-
-  // a key block in registers: units it * 256 + tid, of K below kKU, else of V
-  constexpr int kKU = (D / 8) * (kKBlock / 4);
-  constexpr int kIt = (2 * kKU + kAttnThreads - 1) / kAttnThreads;
-  u32x4 pre[kIt][4];
-  auto prefetch = [&](int kb) {
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int u = it * kAttnThreads + tid;
-      if (u < 2 * kKU)
-        load_unit<D, kKBlock>(pre[it], u < kKU ? Kh : Vh, kb * kKBlock, S, u < kKU ? u : u - kKU);
-    }
-  };
-  auto stage = [&](int kb, int slot) {
-    char* sl = lds + slot * kSlot;
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int u = it * kAttnThreads + tid;
-      if (u < kKU) {
-        store_unit<D, kKBlock>(pre[it], sl, sl + kTile, kb * kKBlock, S, u);
-      } else if (u < 2 * kKU) {
-        store_unit<D, kKBlock, false>(pre[it], sl + 2 * kTile, nullptr, kb * kKBlock, S,
-                                      u - kKU);
-      }
-    }
-  };
-  auto compute = [&](int kb, int slot) {
-    const int k0 = kb * kKBlock;
-    if (a.causal && k0 > q0 + 31) return;  // every key after the wave's queries
-    const char* lk = lds + slot * kSlot;
-    const char* lkt = lk + kTile;
-    const char* lv = lk + 2 * kTile;
-    // S^T = K Q^T and dP^T = V dO^T, one 32-key half (mt) at a time
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      u32x4 fk[KS], fv[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int off = k_offset(32 * mt + j, 2 * s + h, C);
-        fk[s] = *(const u32x4*)(lk + off);
-        fv[s] = *(const u32x4*)(lv + off);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sc[mt][i] = 0.f;
-        dp[mt][i] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        Mma<bf16_t>::run(sc[mt], fk[s], qf[s]);
-        Mma<bf16_t>::run(dp[mt], fv[s], df[s]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // K^T fragments of dQ^T += K^T dS^T: independent of the softmax
-    u32x4 ft[MD][2][2];
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-          ft[m][mt][g] = *(const u32x4*)(lkt + tt_chunk_offset<kKBlock>(
-              32 * m + j, 4 * mt + 2 * g + h));
-    __builtin_amdgcn_sched_barrier(0);
-    // dS^T = P^T (dP^T - D); masks (sequence end, causal diagonal) only on
-    // the blocks that need them
-    const int lim = a.causal ? min(q, S - 1) : S - 1;
-    u32x4 dsf[2][2];
-    // masks (sequence end, causal diagonal) set the scores to -inf in place,
-    // only on the blocks that need them; one softmax code path, so that the
-    // register allocation is the same on every path
-    if (k0 + kKBlock > S || (a.causal && k0 + kKBlock - 1 > q0)) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3) > lim) sc[mt][i] = -INFINITY;
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float ds[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int i = 8 * g + 2 * w + e;
-            const float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
-            ds[e] = p * (dp[mt][i] - Dq);
-          }
-          dsf[mt][g][w] = cvt_pk_bf16(ds[0], ds[1]);
-        }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) Mma<bf16_t>::run(dq[m], ft[m][mt][g], dsf[mt][g]);
-  };
-
-  prefetch(0);
-  stage(0, 0);
-  if (nkb > 1) prefetch(1);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    compute(kb, kb & 1);
-    if (kb + 1 < nkb) {
-      stage(kb + 1, (kb + 1) & 1);  // the slot block kb - 1 used: free since the last barrier
-      if (kb + 2 < nkb) prefetch(kb + 2);
-    }
-    __syncthreads();
-  }
-  if (q >= S) return;
-  float* dQq = a.dQ + head + (int64_t)q * D;
-#pragma unroll
-  for (int m = 0; m < MD; ++m)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 v = {dq[m][4 * r4] * a.scale, dq[m][4 * r4 + 1] * a.scale,
-                 dq[m][4 * r4 + 2] * a.scale, dq[m][4 * r4 + 3] * a.scale};
-      *(f32x4*)(dQq + 32 * m + 8 * r4 + 4 * h) = v;
-    }
-}
-
-// dK / dV pass
-constexpr int kKvKeys = 128;  // keys per workgroup (32 per wave)
-constexpr int kKvQ = 32;      // queries per block
-
-// One wave per SIMD.  Block b of 32 queries runs the S / dP products A(b),
-// then its softmax, and the accumulation C(b) (dV^T += dO^T P^T, dK^T +=
-// Q^T dS^T) is deferred to the next block, where its MFMAs issue under the
-// softmax of b + 1: the wave then keeps the matrix core busy while the VALU
-// works.  Block b lives in LDS slot b % 3 (Q, dO, Q^T, dO^T, lse, D) from its
-// staging two blocks ahead until C(b) has run; the K / V rows are staged
-// through the same LDS once, at the start, into registers.
-template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
-  constexpr int C = D / 8;
-  constexpr int KS = D / 16;
-  constexpr int MD = D / 32;
-  constexpr int kKV = kKvKeys * D * 2;   // K (or V) rows of the workgroup
-  constexpr int kQT = kKvQ * D * 2;      // one 32-query tile (row-major or transposed)
-  static_assert(D == 64, "D = 128 runs attn_bwd_dkv_pair_kernel");
-  constexpr int kTiles = 4;  // Q, dO, and their transposed copies (paired-chunk layout)
-  constexpr int kSlot = kTiles * kQT + 2 * kKvQ * 4;
-  constexpr int kLds = 2 * kKV > 3 * kSlot ? 2 * kKV : 3 * kSlot;
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 31;
-  const int h = lane >> 5;
-  const int S = a.S;
-  int kblk;
-  int64_t bh;
-  xcd_head_block((S + kKvKeys - 1) / kKvKeys, a.BH, kblk, bh);
-  const int64_t head = bh * (int64_t)S * D;
-  const int kbase = kblk * kKvKeys;
-  const int k0w = kbase + 32 * wave;  // first key of this wave
-  const int kk = k0w + j;             // this lane's key
-  const float c = a.scale_log2;
-
-  // this lane's K and V fragments (B operands of S and dP) for the whole pass
-  u32x4 kf[KS], vf[KS];
-  {
-    char* lk = lds;
-    char* lv = lds + kKV;
-    stage_rows2<D, kKvKeys, kAttnThreads>(lk, a.K + head, lv, a.V + head, kbase, S, tid);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int ko = k_offset(32 * wave + j, 2 * s + h, C);
-      kf[s] = *(const u32x4*)(lk + ko);
-      vf[s] = *(const u32x4*)(lv + ko);
-    }
-    __syncthreads();  // the query slots below reuse this LDS
-  }
-
-  f32x16 dk[MD], dv[MD];
-#pragma unroll
-  for (int m = 0; m < MD; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[m][i] = 0.f;
-      dv[m][i] = 0.f;
-    }
-
-  const int nq = (S + kKvQ - 1) / kKvQ;
-  const int qstart = a.causal ? kbase / kKvQ : 0;
-  // a query block in registers: load unit u of Q (u < kUnits) or of dO, and
-  // the lse (threads 0-31) or D (threads 32-63) of one query
-  constexpr int kUnits = (D / 8) * (kKvQ / 4);
-  const bool unit_on = tid < 2 * kUnits;
-  const bool unit_q = tid < kUnits;
-  const int unit = unit_q ? tid : tid - kUnits;
-  const bf16_t* usrc = (unit_q ? a.Q : a.dO) + head;
-  const float* vsrc = (tid < kKvQ ? a.lse : a.delta) + bh * S;
-  u32x4 pre[4];
-  float pre_v = 0.f;
-  auto slot_of = [&](int qbk) { return lds + (qbk % 3) * kSlot; };
-  auto prefetch = [&](int qbk) {
-    const int qb0 = qbk * kKvQ;
-    if (unit_on) load_unit<D, kKvQ>(pre, usrc, qb0, S, unit);
-    if (tid < 2 * kKvQ) pre_v = vsrc[min(qb0 + (tid & (kKvQ - 1)), S - 1)];
-  };
-  auto stage = [&](int qbk) {
-    const int qb0 = qbk * kKvQ;
-    char* sl = slot_of(qbk);
-    if (unit_on)
-      store_unit<D, kKvQ>(pre, sl + (unit_q ? 0 : kQT), sl + (unit_q ? 2 : 3) * kQT, qb0, S, unit);
-    if (tid < 2 * kKvQ) {
-      float* lv4 = (float*)(sl + kTiles * kQT);
-      const bool in = qb0 + (tid & (kKvQ - 1)) < S;
-      lv4[tid] = tid < kKvQ ? (in ? pre_v * kLog2e : INFINITY) : (in ? pre_v : 0.f);
-    }
-  };
-
-  // P and dS of the previous block (B operands of its deferred accumulation);
-  // zero until a block has run, so that the first accumulation adds nothing
-  u32x4 pp[2], ps[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      pp[g][w] = 0u;
-      ps[g][w] = 0u;
-    }
-  int prev_slot = -1;  // slot of the block whose accumulation is pending
-  // C: dV^T += dO^T P^T, dK^T += Q^T dS^T, fragments from slot sl
-  auto accumulate = [&](const char* sl) {
-    const char* lqt = sl + 2 * kQT;   // Q^T
-    const char* ldot = sl + 3 * kQT;  // dO^T
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int off = tt_chunk_offset<kKvQ>(32 * m + j, 2 * g + h);
-        Mma<bf16_t>::run(dv[m], *(const u32x4*)(ldot + off), pp[g]);
-        Mma<bf16_t>::run(dk[m], *(const u32x4*)(lqt + off), ps[g]);
-      }
-  };
-
-  // block qbk: A(qbk), then its softmax with the pending accumulation issued
-  // alongside.  One code path for every block: the first accumulation reads
-  // this block's slot (finite data) against zero P and dS, and the causal
-  // mask sets the diagonal block's scores to -inf in place, so that the
-  // register allocation is the same on every path.
-  auto compute = [&](int qbk) {
-    const int qb0 = qbk * kKvQ;
-    const char* sl = slot_of(qbk);
-    const char* lq = sl;                                    // Q rows
-    const char* ldo = sl + kQT;                             // dO rows
-    const float* llse = (const float*)(sl + kTiles * kQT);  // lse log2(e) (+inf past S)
-    const float* ldel = llse + kKvQ;                   // D
-    u32x4 fq[KS], fdo[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int qo = k_offset(j, 2 * s + h, C);
-      fq[s] = *(const u32x4*)(lq + qo);
-      fdo[s] = *(const u32x4*)(ldo + qo);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 sc, dp;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[i] = 0.f;
-      dp[i] = 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      Mma<bf16_t>::run(sc, fq[s], kf[s]);
-      Mma<bf16_t>::run(dp, fdo[s], vf[s]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      l4[r4] = *(const f32x4*)(llse + 8 * r4 + 4 * h);
-      d4[r4] = *(const f32x4*)(ldel + 8 * r4 + 4 * h);
-    }
-    accumulate(slot_of(prev_slot < 0 ? qbk : prev_slot));
-    if (a.causal && qb0 < k0w + 32) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (qb0 + 8 * (i >> 2) + 4 * h + (i & 3) < kk) sc[i] = -INFINITY;
-    }
-    u32x4 np[2], ns[2];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * r4 + e;
-        const float pv = fast_exp2(fmaf(sc[i], c, -l4[r4][e]));  // 0 past S (lse = +inf)
-        p[e] = pv;
-        ds[e] = pv * (dp[i] - d4[r4][e]);
-      }
-      const int g = r4 >> 1, w0 = (r4 & 1) * 2;
-      np[g][w0] = cvt_pk_bf16(p[0], p[1]);
-      np[g][w0 + 1] = cvt_pk_bf16(p[2], p[3]);
-      ns[g][w0] = cvt_pk_bf16(ds[0], ds[1]);
-      ns[g][w0 + 1] = cvt_pk_bf16(ds[2], ds[3]);
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      pp[g] = np[g];
-      ps[g] = ns[g];
-    }
-    prev_slot = qbk;
-  };
-
-  // Prologue: blocks qstart and qstart + 1 staged, qstart + 2 in registers.
-  prefetch(qstart);
-  stage(qstart);
-  if (qstart + 1 < nq) {
-    prefetch(qstart + 1);
-    stage(qstart + 1);
-  }
-  if (qstart + 2 < nq) prefetch(qstart + 2);
-  __syncthreads();
-  for (int qbk = qstart; qbk < nq; ++qbk) {
-    // every query before the wave's keys: nothing to do (only blocks before
-    // the wave's first active one are skipped, so nothing is pending then)
-    if (!(a.causal && qbk * kKvQ + kKvQ - 1 < k0w)) compute(qbk);
-    __syncthreads();  // slot (qbk + 2) % 3 = slot of qbk - 1: its C has run
-    if (qbk + 2 < nq) {
-      stage(qbk + 2);
-      if (qbk + 3 < nq) prefetch(qbk + 3);
-    }
-  }
-  if (prev_slot >= 0) accumulate(slot_of(prev_slot));
-
-  if (kk >= S) return;
-  float* dKk = a.dK + head + (int64_t)kk * D;
-  float* dVk = a.dV + head + (int64_t)kk * D;
-#pragma unroll
-  for (int m = 0; m < MD; ++m)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * m + 8 * r4 + 4 * h;
-      f32x4 vk = {dk[m][4 * r4] * a.scale, dk[m][4 * r4 + 1] * a.scale,
-                  dk[m][4 * r4 + 2] * a.scale, dk[m][4 * r4 + 3] * a.scale};
-      f32x4 vv = {dv[m][4 * r4], dv[m][4 * r4 + 1], dv[m][4 * r4 + 2], dv[m][4 * r4 + 3]};
-      *(f32x4*)(dKk + d0) = vk;
-      *(f32x4*)(dVk + d0) = vv;
-    }
-}
-
-// Shared by the D = 128 backward passes: 8 waves (two per SIMD) on
-// v_mfma_f32_16x16x32_bf16.  Operand layouts of the 16 x 16 x 32 product: A
+// Shared by the backward passes: 8 waves on v_mfma_f32_16x16x32_bf16.  Operand layouts of the 16 x 16 x 32 product: A
 // lane l holds row l % 16 with K entries 8 (l / 16) .. + 7, B lane l column
 // l % 16 with the same K entries, the result lane l column l % 16 with rows
 // 4 (l / 16) .. + 3.
@@ -919,17 +438,25 @@ __device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b) 
                                               __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Row-major Q / dO tiles of this pass (256-byte rows of 16 sixteen-byte
-// chunks): chunk c of row r sits at position c ^ swz16(r), swz16(r) =
-// 2 (r % 8).  The S / dP fragment reads (16 lanes: one chunk of 16
+// Row-major tiles of the 16 x 16 x 32 passes (rows of D bf16 entries, D / 8
+// sixteen-byte chunks): chunk c of row r sits at position c ^ swz(r), with
+// swz(r) = 2 (r % 8) for 256-byte rows (D = 128) and r & 6 for 128-byte rows
+// (D = 64).  The S / dP fragment reads (16 lanes: one chunk of 16
 // consecutive rows; lane groups 16 g read chunk 4 s + g) and the transposing
-// reads (32 lanes: chunks 2 m, 2 m + 1 of 8 consecutive rows) run at the LDS
-// rate of conflict-free reads on gfx950 (16-byte reads 4 clocks per wave,
-// measured).  Adding (r / 8) % 2 to the swizzle, which separates rows r and
-// r + 8 but pairs the chunk of lane group g with that of group g ^ 1 in rows
-// r ^ 8, halves the rate of the 16-byte reads.
-__device__ __forceinline__ int swz16_offset(int row, int chunk) {
-  return row * 256 + ((chunk ^ ((row & 7) << 1)) << 4);
+// reads (32 lanes: chunks 2 m, 2 m + 1 of 8 consecutive rows) then run at
+// the LDS rate of conflict-free reads on gfx950 (16-byte reads 4 clocks per
+// wave, transposing reads 175-181 bytes per clock per CU, measured).  Any
+// term that flips bit 0 of the position (e.g. adding (r / 8) % 2 for
+// D = 128, which separates rows r and r + 8 but pairs the chunk of lane
+// group g with that of group g ^ 1 in rows r ^ 8) halves the rate of the
+// 16-byte reads.
+template <int D>
+__device__ __forceinline__ int swz_offset(int row, int chunk) {
+  static_assert(D == 64 || D == 128, "D = 64 or 128");
+  if constexpr (D == 128)
+    return row * 256 + ((chunk ^ ((row & 7) << 1)) << 4);
+  else
+    return row * 128 + ((chunk ^ (row & 6)) << 4);
 }
 
 // A fragment of the transposed tile for the 16 x 16 x 32 product: operand row
@@ -938,11 +465,13 @@ __device__ __forceinline__ int swz16_offset(int row, int chunk) {
 // off + 16 rows).  Within a group of 16 lanes, lane i receives as element e
 // the element i % 4 of the 8 bytes that lane 4 e + i / 4 addressed; so lane L
 // of group G addresses row 4 G + L / 4, columns 16 m + 4 (L % 4) .. + 3.
+template <int D>
 __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
   typedef short i16x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p + 4096));
+  const i16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)LCE_LDS_PTR(p + 16 * 2 * D));
   const u32x2 x = __builtin_bit_cast(u32x2, lo);
   const u32x2 y = __builtin_bit_cast(u32x2, hi);
   u32x4 r = {x[0], x[1], y[0], y[1]};
@@ -950,9 +479,9 @@ __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
 }
 }  // namespace
 
-// dK / dV pass for D = 128, split by gradient: a workgroup of 8 waves takes
+// dK / dV pass (D = 64 or 128), split by gradient: a workgroup of 8 waves takes
 // 128 keys as 4 pairs of 32 and streams the queries in blocks of 64 through
-// two LDS slots (Q rows, dO rows in the swizzle of swz16_offset, lse, D).
+// two LDS slots (Q rows, dO rows in the swizzle of swz_offset, lse, D).
 // Of the two waves of a pair, which share a SIMD (waves w and w + 4), the P
 // wave computes S = Q K^T, the softmax P and dV^T += dO^T P^T, the dS wave
 // dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS^T.  Against one wave per
@@ -987,10 +516,15 @@ __device__ __forceinline__ u32x4 tr_frag16(const char* p) {
 //  * NP pairs per workgroup (32 NP keys).  NP = 4 is launched: NP = 2 (two
 //    workgroups per CU, each staging every query block for its 64 keys) ran
 //    15% slower.
-template <int NP>
-__global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(AttnBwdArgs a) {
-  constexpr int D = 128;
+// Launch bounds: D = 128 needs up to 256 VGPRs (two waves per SIMD, one
+// workgroup per CU); D = 64 is held to 128 (four waves per SIMD: two
+// workgroups per CU, 8% faster than one despite a few spilled registers).
+template <int NP, int D>
+__global__ __launch_bounds__(128 * NP, D == 64 ? 4 : 4 / NP) void attn_bwd_dkv_pair_kernel(AttnBwdArgs a) {
   constexpr int QB = 64;                  // queries per block
+  constexpr int C = D / 8;                // 16-byte chunks per row
+  constexpr int RB = 2 * D;               // bytes per row
+  constexpr int KS = D / 32;              // K steps of the S / dP products
   constexpr int NT = 128 * NP;            // threads
   constexpr int KK = 32 * NP;             // keys of the workgroup
   constexpr int kKV = KK * D * 2;         // K (or V) rows of the workgroup
@@ -998,7 +532,7 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
   constexpr int kSlot = 2 * kQT + 512;    // Q, dO, lse[64], D[64]
   constexpr int kXch = NP * 4 * 64 * 16;  // P of the pairs: 4 fragments x 64 lanes x 16 B
   constexpr int kLds = 2 * kKV > 2 * kSlot + kXch ? 2 * kKV : 2 * kSlot + kXch;
-  constexpr int kRows = NT / 16;          // tile rows staged per pass
+  constexpr int kRows = NT / C;           // tile rows staged per pass
   constexpr int kPre = QB / kRows;        // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x;
@@ -1019,9 +553,9 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
 
   const int nq = (S + QB - 1) / QB;
   const int qstart = a.causal ? kbase / QB : 0;
-  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 +
-  // kRows i of the Q and the dO tile, stored at position t % 16 of its
-  // row, i.e. chunk (t % 16) ^ swz16(row) of the source row; even waves
+  // register-staged loads: thread t carries chunk t % C of rows t / C +
+  // kRows i of the Q and the dO tile, stored at position t % C of its row,
+  // i.e. chunk (t % C) ^ swz(row) of the source row; even waves
   // carry the block's lse values (times log2 e), odd waves its D values (the
   // waves of a parity write identical values)
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)(a.Q + head), (int64_t)S * D * 2);
@@ -1029,21 +563,21 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
   const __amdgpu_buffer_rsrc_t rv = (wave & 1)
       ? make_rsrc((const char*)(a.delta + bh * S), (int64_t)S * 4)
       : make_rsrc((const char*)(a.lse + bh * S), (int64_t)S * 4);
-  const int srow = tid >> 4;
-  const uint32_t gvoff = (uint32_t)swz16_offset(srow, tid & 15);
-  const int lvoff = srow * 256 + ((tid & 15) << 4);
+  const int srow = tid / C;
+  const uint32_t gvoff = (uint32_t)swz_offset<D>(srow, tid % C);
+  const int lvoff = srow * RB + ((tid % C) << 4);
   typedef u32x4 BlockRegs16[2 * kPre];
   BlockRegs16 pre;
   float pre_v;
   auto slot_of = [&](int qbk) { return lds + ((qbk - qstart) & 1) * kSlot; };
   auto load_into = [&](BlockRegs16& r, float& rv_, int qbk) {
-    const uint32_t soff = (uint32_t)(qbk * QB) * 256u;
+    const uint32_t soff = (uint32_t)(qbk * QB) * (uint32_t)RB;
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       r[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + 256 * kRows * i, soff, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, gvoff + RB * kRows * i, soff, 0));
       r[kPre + i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + 256 * kRows * i, soff, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, gvoff + RB * kRows * i, soff, 0));
     }
     rv_ = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        rv, lane * 4, (uint32_t)(qbk * QB) * 4u, 0));
@@ -1052,8 +586,8 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
     char* sl = slot_of(qbk);
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      *(u32x4*)(sl + lvoff + 256 * kRows * i) = r[i];
-      *(u32x4*)(sl + kQT + lvoff + 256 * kRows * i) = r[kPre + i];
+      *(u32x4*)(sl + lvoff + RB * kRows * i) = r[i];
+      *(u32x4*)(sl + kQT + lvoff + RB * kRows * i) = r[kPre + i];
     }
     // lse in log2 units (one multiply here instead of one per score)
     *(float*)(sl + 2 * kQT + (wave & 1) * 256 + lane * 4) = (wave & 1) ? rv_ : rv_ * kLog2e;
@@ -1063,14 +597,14 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
 
   // per-lane LDS offsets: S / dP fragments (row i16 of a 16-query quarter,
   // chunk 4 s + g) and the transposing reads of the accumulation
-  int aoff[4], toff[8];
+  int aoff[KS], toff[D / 16];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = swz16_offset(i16, 4 * s + g);
+  for (int s = 0; s < KS; ++s) aoff[s] = swz_offset<D>(i16, 4 * s + g);
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < D / 16; ++m) {
     const int row = 4 * g + (i16 >> 2);
     const int dim = 16 * m + 4 * (lane & 3);
-    toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
+    toff[m] = swz_offset<D>(row, dim >> 3) + (dim & 7) * 2;
   }
 
   // The two roles take separate code paths, each with its own registers.
@@ -1078,12 +612,12 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
     constexpr bool kP = decltype(role)::value;
     // K (P wave) or V (dS wave) fragments of the pair's two 16-key tiles:
     // B operands of S and dP for the whole pass
-    u32x4 bf[2][4];
-    f32x4 acc[2][8];  // dV^T (P wave) or dK^T (dS wave) per key tile
+    u32x4 bf[2][KS];
+    f32x4 acc[2][D / 16];  // dV^T (P wave) or dK^T (dS wave) per key tile
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < D / 16; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t][m][e] = 0.f;
 
@@ -1105,7 +639,7 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
           bf[t][s] = *(const u32x4*)(lb + k_offset(32 * pair + 16 * t + i16, 4 * s + g, D / 8));
       __syncthreads();
       store_from(pre0, pre0_v, qstart);
@@ -1126,23 +660,24 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
             for (int e = 0; e < 4; ++e) sc[t][h][e] = 0.f;
         const char* op = sl + (kP ? 0 : kQT);  // Q or dO tile
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
-            const u32x4 af = *(const u32x4*)(op + aoff[s] + 4096 * h);
+            const u32x4 af = *(const u32x4*)(op + aoff[s] + 16 * RB * h);
             mma16(sc[0][h], af, bf[0][s]);
             mma16(sc[1][h], af, bf[1][s]);
           }
-        // the first 6 fragment reads go out together, then one read after
-        // every two MFMAs (the compiler's order waits on each read right in
-        // front of its MFMAs)
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        // the first fragment reads (6 of 16, 4 of 8) go out together, then
+        // one read after every two MFMAs (the compiler's order waits on each
+        // read right in front of its MFMAs)
+        constexpr int kAhead = KS == 4 ? 6 : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-        for (int q = 0; q < 10; ++q) {
+        for (int q = 0; q < 4 * KS - kAhead; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (kP) {
           const float* lv = (const float*)(sl + 2 * kQT);
@@ -1212,8 +747,8 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const u32x4 tf = tr_frag16(tp + 8192 * n + toff[m]);
+          for (int m = 0; m < D / 16; ++m) {
+            const u32x4 tf = tr_frag16<D>(tp + 32 * RB * n + toff[m]);
             mma16(acc[0][m], tf, pp[0][n]);
             mma16(acc[1][m], tf, pp[1][n]);
           }
@@ -1250,7 +785,7 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
       if (kk < S) {
         float* row = out + head + (int64_t)kk * D;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < D / 16; ++m) {
           f32x4 v = {acc[t][m][0] * sc_out, acc[t][m][1] * sc_out, acc[t][m][2] * sc_out,
                      acc[t][m][3] * sc_out};
           *(f32x4*)(row + 16 * m + 4 * g) = v;
@@ -1264,10 +799,10 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
     run(std::integral_constant<bool, false>{});
 }
 
-// dQ pass for D = 128 on the 16 x 16 x 32 product, two waves per SIMD: a
-// workgroup of 8 waves takes 128 queries, 16 per wave, and streams the keys
-// in blocks of 64 through two LDS slots (K rows, V rows, in the swizzle of
-// swz16_offset).
+// dQ pass (D = 64 or 128) on the 16 x 16 x 32 product, two waves per SIMD
+// (four for D = 64): a workgroup of 8 waves takes 128 queries, 16 per wave,
+// and streams the keys in blocks of 64 through two LDS slots (K rows, V
+// rows, in the swizzle of swz_offset).
 //  * S^T = K Q^T and dP^T = V dO^T per 16-key quarter of the block: lane l
 //    (g = l / 16) holds query l % 16 and keys 16 kq + 4 g + e; the wave's Q
 //    and dO rows stay in registers (the B operands), so lse and D are one
@@ -1283,9 +818,14 @@ __global__ __launch_bounds__(128 * NP, 4 / NP) void attn_bwd_dkv_pair_kernel(Att
 //    two blocks (the causal diagonal, the sequence tail) take the masked
 //    path.
 //  * It also writes D = rowsum(dO O) for the dK / dV pass.
+template <int D>
 __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArgs a) {
-  constexpr int D = 128;
   constexpr int KB = 64;               // keys per block
+  constexpr int C = D / 8;             // 16-byte chunks per row
+  constexpr int RB = 2 * D;            // bytes per row
+  constexpr int KS = D / 32;           // K steps of the S / dP products
+  constexpr int kRows = k16Threads / C;  // tile rows staged per pass
+  constexpr int kPre = KB / kRows;       // 16-byte chunks per thread per tile
   constexpr int kT = KB * D * 2;       // one block's K (or V) tile
   constexpr int kSlot = 2 * kT;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kSlot];
@@ -1306,40 +846,44 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
   const int qc = q < S ? q : S - 1;
   const float c = a.scale_log2;
 
-  f32x4 dq[8];
+  f32x4 dq[D / 16];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < D / 16; ++m)
 #pragma unroll
     for (int e = 0; e < 4; ++e) dq[m][e] = 0.f;
 
   const int kend = a.causal ? min(S, qb * kQBlock + kQBlock) : S;
   const int nkb = (kend + KB - 1) / KB;
-  // register-staged loads: thread t carries chunk t % 16 of rows t / 16 and
-  // t / 16 + 32 of the K and the V tile (position t % 16 of the row in LDS);
-  // two register sets by block parity, compile-time at every use
+  // register-staged loads: thread t carries chunk t % C of rows t / C +
+  // kRows i of the K and the V tile (position t % C of the row in LDS); two
+  // register sets by block parity, compile-time at every use
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)(a.K + head), (int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)(a.V + head), (int64_t)S * D * 2);
-  const int srow = tid >> 4;
-  const uint32_t gvoff = (uint32_t)swz16_offset(srow, tid & 15);
-  const int lvoff = srow * 256 + ((tid & 15) << 4);
-  u32x4 pre[2][4];
+  const int srow = tid / C;
+  const uint32_t gvoff = (uint32_t)swz_offset<D>(srow, tid % C);
+  const int lvoff = srow * RB + ((tid % C) << 4);
+  u32x4 pre[2][2 * kPre];
   auto slot_of = [&](int kb) { return lds + (kb & 1) * kSlot; };
   auto load_regs = [&](int kb, auto par) {
     constexpr int r = decltype(par)::value;
-    const uint32_t soff = (uint32_t)(kb * KB) * 256u;
-    pre[r][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, gvoff, soff, 0));
-    pre[r][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, gvoff + 8192, soff, 0));
-    pre[r][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvoff, soff, 0));
-    pre[r][3] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvoff + 8192, soff, 0));
+    const uint32_t soff = (uint32_t)(kb * KB) * (uint32_t)RB;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      pre[r][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, gvoff + RB * kRows * i, soff, 0));
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      pre[r][kPre + i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvoff + RB * kRows * i, soff, 0));
     __builtin_amdgcn_sched_barrier(0);  // issued first
   };
   auto store_regs = [&](int kb, auto par) {
     constexpr int r = decltype(par)::value;
     char* sl = slot_of(kb);
-    *(u32x4*)(sl + lvoff) = pre[r][0];
-    *(u32x4*)(sl + lvoff + 8192) = pre[r][1];
-    *(u32x4*)(sl + kT + lvoff) = pre[r][2];
-    *(u32x4*)(sl + kT + lvoff + 8192) = pre[r][3];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) *(u32x4*)(sl + lvoff + RB * kRows * i) = pre[r][i];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) *(u32x4*)(sl + kT + lvoff + RB * kRows * i) = pre[r][kPre + i];
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -1353,14 +897,14 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
   // the Q and dO fragments (B operands: query i16, dims 32 s + 8 g .. + 7), and
   // D = rowsum(dO O) of the lane's query (the four lanes of a query each sum
   // a quarter of the dims)
-  u32x4 qf[4], df[4];
-  f32x4 of[8];
+  u32x4 qf[KS], df[KS];
+  f32x4 of[2 * KS];
   // lse of the lane's query (0 past S: buffer bounds)
   const float lse_q = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(
                  make_rsrc((const char*)(a.lse + bh * S), (int64_t)S * 4), (uint32_t)q * 4u, 0, 0));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < KS; ++s) {
     const int64_t off = head + (int64_t)qc * D + 32 * s + 8 * g;
     qf[s] = *(const u32x4*)(a.Q + off);
     df[s] = *(const u32x4*)(a.dO + off);
@@ -1370,7 +914,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
   __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
   float dpart = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < KS; ++s) {
     const f32x4 o0 = of[2 * s], o1 = of[2 * s + 1];
     dpart += bf16_lo(df[s][0]) * o0[0] + bf16_hi(df[s][0]) * o0[1] + bf16_lo(df[s][1]) * o0[2] +
              bf16_hi(df[s][1]) * o0[3] + bf16_lo(df[s][2]) * o1[0] + bf16_hi(df[s][2]) * o1[1] +
@@ -1381,14 +925,14 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
   if (g == 0 && q < S) a.delta[bh * S + q] = Dq;
   const float lse2 = lse_q * kLog2e;
 
-  int aoff[4], toff[8];
+  int aoff[KS], toff[D / 16];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = swz16_offset(i16, 4 * s + g);
+  for (int s = 0; s < KS; ++s) aoff[s] = swz_offset<D>(i16, 4 * s + g);
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < D / 16; ++m) {
     const int row = 4 * g + (i16 >> 2);
     const int dim = 16 * m + 4 * (lane & 3);
-    toff[m] = swz16_offset(row, dim >> 3) + (dim & 7) * 2;
+    toff[m] = swz_offset<D>(row, dim >> 3) + (dim & 7) * 2;
   }
   const int lim = a.causal ? min(q, S - 1) : S - 1;  // last key this lane may see
 
@@ -1403,18 +947,18 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
         dp[kq][e] = 0.f;
       }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
-        mma16(sc[kq], *(const u32x4*)(sl + aoff[s] + 4096 * kq), qf[s]);
-        mma16(dp[kq], *(const u32x4*)(sl + kT + aoff[s] + 4096 * kq), df[s]);
+        mma16(sc[kq], *(const u32x4*)(sl + aoff[s] + 16 * RB * kq), qf[s]);
+        mma16(dp[kq], *(const u32x4*)(sl + kT + aoff[s] + 16 * RB * kq), df[s]);
       }
     // the first 4 fragment reads go out together, then one read after each
     // MFMA (the compiler's order waits on each read right in front of its
     // MFMA; 5 or more reads ahead measured 6% slower)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int q = 0; q < 28; ++q) {
+    for (int q = 0; q < 8 * KS - 4; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -1447,7 +991,8 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) mma16(dq[m], dsf[j], tr_frag16(sl + 8192 * j + toff[m]));
+      for (int m = 0; m < D / 16; ++m)
+        mma16(dq[m], dsf[j], tr_frag16<D>(sl + 32 * RB * j + toff[m]));
   };
 
   store_regs(0, P0{});
@@ -1497,7 +1042,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
     if (qq < S) {
       float* dQq = a.dQ + head + (int64_t)qq * D + i16;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) dQq[16 * m] = dq[m][e] * a.scale;
+      for (int m = 0; m < D / 16; ++m) dQq[16 * m] = dq[m][e] * a.scale;
     }
   }
 }
@@ -1507,24 +1052,21 @@ hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, int D, hipStream_t s) {
   const int64_t nqb = (a.S + kQBlock - 1) / kQBlock;
   const dim3 grid((unsigned)(nqb * a.BH));
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dq16_kernel, grid, dim3(k16Threads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq16_kernel<128>, grid, dim3(k16Threads), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kAttnThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq16_kernel<64>, grid, dim3(k16Threads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkv(const AttnBwdArgs& a, int D, hipStream_t s) {
   if (a.S <= 0 || a.BH <= 0) return hipSuccess;
-  if (D == 128) {
-    constexpr int NP = 4;
-    const int64_t nkb = (a.S + 32 * NP - 1) / (32 * NP);
-    hipLaunchKernelGGL(attn_bwd_dkv_pair_kernel<NP>, dim3((unsigned)(nkb * a.BH)),
-                       dim3(128 * NP), 0, s, a);
-    return hipGetLastError();
-  }
-  const int64_t nkb = (a.S + kKvKeys - 1) / kKvKeys;
-  hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3((unsigned)(nkb * a.BH)), dim3(kAttnThreads), 0,
-                     s, a);
+  constexpr int NP = 4;
+  const int64_t nkb = (a.S + 32 * NP - 1) / (32 * NP);
+  const dim3 grid((unsigned)(nkb * a.BH));
+  if (D == 128)
+    hipLaunchKernelGGL((attn_bwd_dkv_pair_kernel<NP, 128>), grid, dim3(128 * NP), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkv_pair_kernel<NP, 64>), grid, dim3(128 * NP), 0, s, a);
   return hipGetLastError();
 }
 
