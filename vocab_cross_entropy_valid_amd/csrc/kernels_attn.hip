@@ -118,31 +118,35 @@ struct BlockRegs {
   u32x4 v[kVIters][4];
 };
 
-// Global -> registers for key block kb (rows past S read as zeros).
+// Global -> registers for key block kb: buffer loads over the head's K and V
+// rows (rk, rv: S rows), so rows past S read as zeros and no load waits on a
+// branch.
 template <int D>
-__device__ __forceinline__ void load_block(BlockRegs<D>& r, const bf16_t* Kh, const bf16_t* Vh, int S,
-                                           int kb, int tid) {
+__device__ __forceinline__ void load_block(BlockRegs<D>& r, const __amdgpu_buffer_rsrc_t& rk,
+                                           const __amdgpu_buffer_rsrc_t& rv, int kb, int tid) {
   constexpr int C = AttnLds<D>::kChunks;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  const uint32_t soff = (uint32_t)(kb * kKBlock) * (uint32_t)(D * 2);
 #pragma unroll
   for (int j = 0; j < BlockRegs<D>::kKLoads; ++j) {
     const int idx = j * kAttnThreads + tid;
-    const int row = idx / C;
-    const int c = idx % C;
-    const int key = kb * kKBlock + row;
-    r.k[j] = key < S ? *(const u32x4*)(Kh + (int64_t)key * D + 8 * c) : z;
+    const uint32_t off = (uint32_t)((idx / C) * D + 8 * (idx % C)) * 2u;
+    r.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, soff, 0));
   }
 #pragma unroll
   for (int it = 0; it < BlockRegs<D>::kVIters; ++it) {
     const int unit = it * kAttnThreads + tid;
     const int kg = unit & 15;  // keys 4 kg .. 4 kg + 3
     const int dg = unit >> 4;  // dims 8 dg .. 8 dg + 7
+    if (unit < BlockRegs<D>::kVUnits) {  // wave-uniform
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int key = kb * kKBlock + 4 * kg + q;
-      r.v[it][q] = (unit < BlockRegs<D>::kVUnits && key < S)
-                       ? *(const u32x4*)(Vh + (int64_t)key * D + 8 * dg)
-                       : z;
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t off = (uint32_t)((4 * kg + q) * D + 8 * dg) * 2u;
+        r.v[it][q] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, soff, 0));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r.v[it][q] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
@@ -224,11 +228,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   float lrun = 0.f;        // this lane's part of the running sum
   const float c = a.scale_log2;
 
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)Kh, (int64_t)S * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)Vh, (int64_t)S * D * 2);
   BlockRegs<D> r;
-  load_block<D>(r, Kh, Vh, S, 0, tid);
+  load_block<D>(r, rk, rv, 0, tid);
   store_block<D>(r, lds, tid);
   __syncthreads();
-  if (nkb > 1) load_block<D>(r, Kh, Vh, S, 1, tid);
+  if (nkb > 1) load_block<D>(r, rk, rv, 1, tid);
   for (int kb = 0; kb < nkb; ++kb) {
     const char* buf = lds + (kb & 1) * AttnLds<D>::kBuf;
     const int k0 = kb * kKBlock;
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     // every wave finished before the previous barrier)
     if (kb + 1 < nkb) store_block<D>(r, lds + ((kb + 1) & 1) * AttnLds<D>::kBuf, tid);
     __syncthreads();
-    if (kb + 2 < nkb) load_block<D>(r, Kh, Vh, S, kb + 2, tid);
+    if (kb + 2 < nkb) load_block<D>(r, rk, rv, kb + 2, tid);
   }
 
   const float ltot = lrun + __shfl_xor(lrun, 32);
