@@ -550,7 +550,21 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
     // formulas: SGD p -= lr (g + wd p); AdamW p *= 1 - lr wd, m = b1 m +
     // (1 - b1) g, v = b2 v + (1 - b2) g^2, p -= (lr / bc1) m / (sqrt(v) / bc2s
     // + eps).  Batches of 16 values per lane keep the loads in flight together.
-    const int64_t row0 = a.v0;
+    // State and weights through buffer resources over the block's rows
+    // [v0, v0 + nv): loads past them read 0 and stores past them are dropped,
+    // so no element needs a branch.  (With a branch per element the compiler
+    // waited for all outstanding memory operations, stores included, in front
+    // of each update.)  Columns past d (d not a multiple of the tile) stay
+    // behind one per-lane condition.
+    const char* mbase = (const char*)(a.master + a.v0 * a.d);
+    const int64_t nbytes = nv * a.d * 4;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(mbase, nbytes);
+    const __amdgpu_buffer_rsrc_t rm1 =
+        make_rsrc((const char*)(kStep == 2 ? a.exp_avg + a.v0 * a.d : nullptr), kStep == 2 ? nbytes : 0);
+    const __amdgpu_buffer_rsrc_t rm2 = make_rsrc(
+        (const char*)(kStep == 2 ? a.exp_avg_sq + a.v0 * a.d : nullptr), kStep == 2 ? nbytes : 0);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc((const char*)(a.w16 ? a.w16 + a.v0 * a.d : nullptr), a.w16 ? nv * a.d * 2 : 0);
     // values per lane in flight (AdamW holds three arrays; 16 fp32 values
     // for SGD spilled)
     constexpr int kB = (kStep == 2 || sizeof(T) == 4) ? 8 : 16;
@@ -562,38 +576,37 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
         for (int i0 = 0; i0 < 16; i0 += kB) {
           const int n = n_base + 32 * nt;
           float p[kB], m[kB], v[kB];
+          uint32_t off[kB];  // element offset from the block's first row
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
             const int i = i0 + b;
             const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-            const bool in = ml < nv && n < a.d;
-            const int64_t o = (row0 + ml) * a.d + n;
-            p[b] = in ? a.master[o] : 0.f;
+            off[b] = (uint32_t)((int64_t)ml * a.d + n);
+            p[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off[b] * 4u, 0, 0));
             if constexpr (kStep == 2) {
-              m[b] = in ? a.exp_avg[o] : 0.f;
-              v[b] = in ? a.exp_avg_sq[o] : 0.f;
+              m[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm1, off[b] * 4u, 0, 0));
+              v[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm2, off[b] * 4u, 0, 0));
             }
           }
+          if (n < a.d) {
 #pragma unroll
-          for (int b = 0; b < kB; ++b) {
-            const int i = i0 + b;
-            const int ml = m_base + 32 * mt + 8 * (i >> 2) + (i & 3);
-            if (ml >= nv || n >= a.d) continue;
-            const int64_t o = (row0 + ml) * a.d + n;
-            const float g = acc[mt][nt][i];
-            float q;
-            if constexpr (kStep == 1) {
-              q = p[b] - a.lr * (g + a.wd * p[b]);
-            } else {
-              const float pd = p[b] * (1.f - a.lr * a.wd);
-              const float m1 = a.beta1 * m[b] + (1.f - a.beta1) * g;
-              const float v1 = a.beta2 * v[b] + (1.f - a.beta2) * g * g;
-              q = pd - (a.lr / a.bc1) * m1 / (__builtin_sqrtf(v1) / a.bc2s + a.eps);
-              a.exp_avg[o] = m1;
-              a.exp_avg_sq[o] = v1;
+            for (int b = 0; b < kB; ++b) {
+              const float g = acc[mt][nt][i0 + b];
+              float q;
+              if constexpr (kStep == 1) {
+                q = p[b] - a.lr * (g + a.wd * p[b]);
+              } else {
+                const float pd = p[b] * (1.f - a.lr * a.wd);
+                const float m1 = a.beta1 * m[b] + (1.f - a.beta1) * g;
+                const float v1 = a.beta2 * v[b] + (1.f - a.beta2) * g * g;
+                q = pd - (a.lr / a.bc1) * m1 / (__builtin_sqrtf(v1) / a.bc2s + a.eps);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, m1), rm1, off[b] * 4u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), rm2, off[b] * 4u, 0, 0);
+              }
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, q), rp, off[b] * 4u, 0, 0);
+              if (a.w16)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits(q), rw, off[b] * 2u, 0, 0);
             }
-            a.master[o] = q;
-            if (a.w16) a.w16[o] = (uint16_t)bf16_bits(q);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
