@@ -35,8 +35,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every kernel is
  *     launched on it and the calls return without synchronising (except
  *     lce_check_error and lce_timing_query).
- *   - Requirements: N >= 0, d > 0 with d % 64 == 0, V > 0, N, V and d below
- *     2^31.  Outputs must not alias inputs.
+ *   - Requirements: N >= 0, d > 0 with d % 64 == 0 and d below 2^22, V > 0,
+ *     N and V below 2^31, N * d * (element size) below 4 GiB.  Outputs must
+ *     not alias inputs.
  *   - No state is kept between calls (besides the optional timing registry);
  *     calls on different streams may run concurrently if they use different
  *     workspaces and outputs.

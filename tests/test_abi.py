@@ -70,6 +70,8 @@ def test_workspace_bounded_independent_of_n_times_v():
     (10, 64, 10, 7, _lib.LCE_ERR_INVALID_ARG),
     (10, 100, 10, 1, _lib.LCE_ERR_UNSUPPORTED),
     (10, 64, 1 << 31, 1, _lib.LCE_ERR_UNSUPPORTED),
+    (1, 1 << 22, 10, 1, _lib.LCE_ERR_UNSUPPORTED),     # fp32 block rows need 32-bit offsets
+    (1 << 20, 4096, 10, 1, _lib.LCE_ERR_UNSUPPORTED),  # N * d * 2 bytes reach 4 GiB
 ])
 def test_forward_rejects_bad_sizes_before_launch(N, d, V, dt, status):
     lib = _lib.load()

@@ -97,6 +97,9 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int dtype, bool step = false) {
   p.fwd_bytes = o;
   p.C = std::min<int64_t>(kChunkMax, round_up(std::max<int64_t>(N, 1), 256));
   p.Vs = std::min<int64_t>(kVocabBlockMax, round_up(V, 256));
+  // fp32 rows of a vocabulary block (dW, optimizer state) are addressed by
+  // 32-bit byte offsets: Vs * d * 4 stays below 4 GiB
+  p.Vs = std::min<int64_t>(p.Vs, (((int64_t)1 << 32) - 1) / (d * 4) / 256 * 256);
   // Row strides of the K-contiguous backward buffers are padded by 64
   // elements: with power-of-two strides the 256 rows of a tile all start on
   // the same memory channel at every K step.
@@ -133,6 +136,8 @@ lce_status check_sizes(int64_t N, int64_t d, int64_t V, int dtype) {
   if (N >= lim || d >= lim || V >= lim)
     return fail(LCE_ERR_UNSUPPORTED, "N, d and V must be below 2^31");
   if (d % 64 != 0) return fail(LCE_ERR_UNSUPPORTED, "d must be a multiple of 64");
+  if (d * 4 * 256 >= ((int64_t)1 << 32))
+    return fail(LCE_ERR_UNSUPPORTED, "d must be below 2^22");
   // gathered token rows are addressed by 32-bit byte offsets from H
   const int64_t esz = dtype == LCE_BF16 ? 2 : 4;
   if (N * d * esz >= ((int64_t)1 << 32))
@@ -524,6 +529,7 @@ lce_status backward_impl(const void* H, const void* W, const int64_t* labels, in
     ha.v0 = v0;
     ha.V = V;
     ha.dH = dH;
+    ha.N = p.N;
     ha.beta = (v0 > 0 || accumulate_dH) ? 1 : 0;
     lce::DwArgs wa{};
     wa.GT = GT;

@@ -51,7 +51,8 @@ struct DhArgs {
   const int32_t* valid_idx;
   const int32_t* valid_count;
   int64_t c0, v0, V;
-  float* dH;
+  float* dH;  // [N][d]
+  int64_t N;
   int beta;
 };
 

@@ -429,7 +429,42 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int slot, char* lds, in
   const int n_base = tn * kTile + wb * kWaveN + (lane & 31);
   // Read-modify-write in four batches (one per mt): all 32 loads of a batch
   // are in flight together, so the epilogue pays four memory latencies, not
-  // one per element.
+  // one per element.  Through a buffer resource over dH, an element without a
+  // destination (no valid row, or a column past d) takes an offset past the
+  // end, where the load reads 0 and the store is dropped: no element needs a
+  // branch.  (With a branch per element the compiler waited for every
+  // outstanding memory operation, stores included, in front of each store.)
+  const int64_t hbytes = a.N * a.d * 4;
+  if (hbytes < 0xFFFFFFFFll) {
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc((const char*)a.dH, hbytes);
+    const uint32_t oob = (uint32_t)hbytes;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float old[16][kNT];
+      uint32_t off[16][kNT];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rows[wa * kHalf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const int n = n_base + 32 * nt;
+          off[i][nt] = (r >= 0 && n < a.d) ? (uint32_t)(((int64_t)r * a.d + n) * 4) : oob;
+          old[i][nt] = a.beta ? __builtin_bit_cast(
+                                    float, __builtin_amdgcn_raw_buffer_load_b32(rh, off[i][nt], 0, 0))
+                              : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, old[i][nt] + acc[mt][nt][i]), rh, off[i][nt], 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
+  // dH of 4 GB or more: 64-bit addresses
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     float old[16][kNT];
@@ -509,7 +544,12 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
                        nstages, tid);
     }
     // acc[mt][nt][4 g + e] is dW[v_base + 32 nt][k_base + 32 mt + 8 g + e]
-    float* out0 = a.dW + a.v0 * a.d;
+    // Through a buffer resource over the block's rows [v0, v0 + nv): rows
+    // past nv fall outside it (loads read 0, stores are dropped), columns
+    // past d take the offset past its end; no element needs a branch.
+    const int64_t wbytes = nv * a.d * 4;
+    const __amdgpu_buffer_rsrc_t rdw = make_rsrc((const char*)(a.dW + a.v0 * a.d), wbytes);
+    const uint32_t oob = (uint32_t)wbytes;
     const int v_base = tm * kTile + wb * kWaveN + (lane & 31);
     const int k_base = tn * kTile + wa * kHalf + 4 * h;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -518,25 +558,25 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int slot, char* lds) {
     for (int nt = 0; nt < kNT; ++nt) {
       const int v = v_base + 32 * nt;
       f32x4 old[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int k = k_base + 32 * mt + 8 * g;
-          old[mt][g] = (a.accumulate && v < nv && k < a.d)
-                           ? *(const f32x4*)(out0 + (int64_t)v * a.d + k) : zero;
-        }
+      uint32_t off[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int k = k_base + 32 * mt + 8 * g;  // d is a multiple of 64: all four in range
-          if (v < nv && k < a.d) {
-            f32x4 r;
+          off[mt][g] = k < a.d ? (uint32_t)(((int64_t)v * a.d + k) * 4) : oob;
+          old[mt][g] = a.accumulate ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    rdw, off[mt][g], 0, 0))
+                                    : zero;
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = old[mt][g][e] + acc[mt][nt][4 * g + e];
-            *(f32x4*)(out0 + (int64_t)v * a.d + k) = r;
-          }
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = old[mt][g][e] + acc[mt][nt][4 * g + e];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), rdw, off[mt][g], 0, 0);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
