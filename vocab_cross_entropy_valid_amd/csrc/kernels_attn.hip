@@ -77,16 +77,27 @@ __device__ __forceinline__ int k_offset(int row, int chunk, int chunks) {
 }
 
 // Workgroup -> (block b of the sequence, head bh) for a grid of nblk x BH
-// workgroups.  Workgroups go to the 8 XCDs round-robin (blockIdx % 8), so
-// here the nblk blocks of one head run back to back on one XCD and the rows
-// they all read (K / V, or Q / dO) are fetched into that XCD's L2 once
-// (A/B on one box: the attention step 1.69 -> 1.62 ms against head-minor
-// order).  Head-minor order when BH is not a multiple of 8.
+// workgroups, b = 0 the heaviest block of a head.  Workgroups go to the 8
+// XCDs round-robin (blockIdx % 8), so here the blocks of G heads run back to
+// back on one XCD, heaviest first across the G heads (all G heads' block 0,
+// then their block 1, ...): the rows those workgroups all read (K / V, or
+// Q / dO) are fetched into that XCD's L2 once (A/B on one box: the attention
+// step 1.69 -> 1.62 ms against head-minor order, with G = 1), and the mix of
+// block lengths in flight evens out the end of the launch (G = 4 against
+// G = 1: forward 393 -> 375 us, dQ 524 -> 505, dK / dV 690 -> 649; G = 16 or
+// 32 lose the L2 sharing: dK / dV 680, 716; the forward takes G = 8: 375 ->
+// 370 us).  G shrinks to the largest power
+// of two dividing BH / 8; head-minor order when BH is not a multiple of 8.
+template <int G>
 __device__ __forceinline__ void xcd_head_block(int nblk, int64_t BH, int& b, int64_t& bh) {
   if (BH % 8 == 0) {
+    int g = G;
+    while ((BH / 8) % g != 0) g >>= 1;
     const int64_t slot = blockIdx.x >> 3;
-    b = (int)(slot % nblk);
-    bh = (slot / nblk) * 8 + (blockIdx.x & 7);
+    const int64_t grp = slot / (g * nblk);
+    const int r = (int)(slot % (g * nblk));
+    b = r / g;
+    bh = (grp * g + r % g) * 8 + (blockIdx.x & 7);
   } else {
     b = (int)(blockIdx.x / BH);
     bh = blockIdx.x % BH;
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   // heaviest (last) query blocks of every head first
   int qb;
   int64_t bh;
-  xcd_head_block(nqb, a.BH, qb, bh);
+  xcd_head_block<8>(nqb, a.BH, qb, bh);
   qb = nqb - 1 - qb;
   const int64_t head = bh * (int64_t)S * D;
   const bf16_t* Qh = a.Q + head;
@@ -550,7 +561,7 @@ __global__ __launch_bounds__(128 * NP, D == 64 ? 4 : 4 / NP) void attn_bwd_dkv_p
   const int S = a.S;
   int kblk;
   int64_t bh;
-  xcd_head_block((S + KK - 1) / KK, a.BH, kblk, bh);
+  xcd_head_block<4>((S + KK - 1) / KK, a.BH, kblk, bh);
   const int64_t head = bh * (int64_t)S * D;
   const int kbase = kblk * KK;
   const int k0p = kbase + 32 * pair;  // first key of this pair
@@ -844,7 +855,7 @@ __global__ __launch_bounds__(k16Threads, 1) void attn_bwd_dq16_kernel(AttnBwdArg
   const int nqb = (S + kQBlock - 1) / kQBlock;
   int qb;
   int64_t bh;
-  xcd_head_block(nqb, a.BH, qb, bh);
+  xcd_head_block<4>(nqb, a.BH, qb, bh);
   qb = nqb - 1 - qb;  // heaviest first
   const int64_t head = bh * (int64_t)S * D;
   const int q0w = qb * kQBlock + 16 * wave;  // first query of this wave
