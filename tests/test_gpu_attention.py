@@ -49,9 +49,13 @@ CASES = [
     (1, 1, 300, 128, False, 605),
     (2, 2, 130, 128, True, 606),     # second query block holds 2 queries
     (1, 4, 512, 128, True, 607),     # several query blocks, diagonal skips
-    # B * H a multiple of 8: the blocks of a head run back to back on one XCD
+    # B * H a multiple of 8: the blocks of a group of heads run interleaved,
+    # heaviest first, on one XCD (group of 8 heads per XCD for the forward,
+    # shrunk to the largest power of two dividing B * H / 8)
     (2, 4, 300, 128, True, 608),
     (1, 8, 130, 64, False, 609),
+    (2, 32, 260, 128, True, 610),    # groups of 8
+    (3, 16, 200, 64, True, 611),     # B * H / 8 = 6: groups of 2
 ]
 
 
@@ -164,10 +168,13 @@ BWD_CASES = [
     (2, 1, 96, 128, True, 629),      # three query blocks (every LDS slot used once)
     (1, 2, 700, 128, True, 630),     # 11 blocks of 64 queries: odd count, ragged tail
     (1, 1, 384, 128, False, 631),    # non-causal, 6 blocks of 64 (no masked path)
-    # B * H a multiple of 8: the blocks of a head run back to back on one XCD
+    # B * H a multiple of 8: the blocks of a group of heads (4 per XCD,
+    # shrunk as in the forward) run interleaved, heaviest first, on one XCD
     (2, 4, 300, 128, True, 632),
     (1, 8, 200, 64, True, 633),
     (1, 16, 257, 128, False, 634),
+    (2, 16, 260, 128, True, 635),    # groups of 4
+    (1, 40, 130, 64, True, 636),     # B * H / 8 = 5: one head per group
 ]
 
 
